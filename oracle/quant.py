@@ -1,0 +1,322 @@
+"""Round-to-nearest quantizers producing the canonical byte layouts (oracle).
+
+Test infrastructure only: tests, the smoke check and bench's cpu_baseline leg
+may call this module; the GPU library never does.
+
+All arithmetic that decides a code or a scale is a fixed sequence of IEEE fp64
+operations followed by a single rounding to the target grid, exactly as
+written below.  "RNE" is round-half-to-even (``numpy.rint``).
+
+Formats (a weight matrix is W[N][K]: N output rows, K contiguous inputs, and the
+product is ``y[m][n] = sum_k x[m][k] * W[n][k]``):
+
+W8_SYM / W4_SYM, group G in {16, 32, 64} along K
+    Symmetric round-to-nearest with one fp16 scale per (row, group).  Pages:
+    "RWKV-7 G1 1.5B -- int4 GPTQ for rwkv-sglang" (summary; "Format & loading":
+    group-wise GROUP=64 symmetric int4, ``.qweight`` + ``.scale``, and the int8
+    w8g64 tier in the accuracy warning) and the rwkv-quant news article
+    ("Dois presets e seis tamanhos": 8-bit symmetric projections, group 16).
+    For b bits the code range is symmetric about zero, Q = 2**(b-1) - 1
+    (127 for int8, 7 for int4) and ``s = fp16(absmax / Q)``.  The int4 reading
+    (codes -7..7, -8 unused) extends the int8 rule; the pages do not print it
+    ("parity unpinned by the pages": pinned by the exact round-trip tests).
+    int8 codes: two's complement int8 [N][K].
+    int4 codes: offset binary u = q + 8 in 1..15, two per byte, the even k in
+    the low nibble: uint8 [N][K/2].  Scales: fp16 [N][K/G].
+
+W4_ASYM_SB256
+    Asymmetric 4-bit codes in superblocks of 256 = 8 groups of 32 (news
+    article, "Dois presets e seis tamanhos": 4-bit asymmetric superblock layout,
+    group 32).  Per group j: lo_j = min(0, min w), hi_j = max w,
+    s_j = (hi_j - lo_j) / 15.  Per superblock: d = fp16(max_j s_j / 63),
+    dmin = fp16(max_j(-lo_j) / 63); 6-bit sub-codes
+    sc_j = clamp(RNE(s_j / d), 0, 63), mc_j = clamp(RNE(-lo_j / dmin), 0, 63);
+    effective S_j = d * sc_j, M_j = dmin * mc_j; codes
+    q = clamp(RNE((w + M_j) / S_j), 0, 15); w_hat = S_j * q - M_j.
+    The article chooses scale and offset by an activation-weighted search; this
+    format uses plain RTN for them ("parity unpinned by the pages").
+    Storage: qs uint8 [N][K/2] (nibbles, even k low), d fp16 [N][K/256],
+    dmin fp16 [N][K/256], sub uint8 [N][K/256][12] = a little-endian 96-bit
+    stream with sc_j at bit 6j and mc_j at bit 48 + 6j.
+
+FP8_E4M3_CH / I8_CH
+    Per-output-channel scale in fp32, FP8 e4m3fn or int8 codes ("RWKV-7
+    Quantization Toolkit", Key Design: FP8 weights on FP8 tensor cores, INT8
+    weights through int8 x int8 dot products).  s_n = fp32(absmax_n / 448)
+    (fp8) or fp32(absmax_n / 127) (int8); codes e4m3fn_rne_sat(w / s_n) or
+    clamp(RNE(w / s_n), -127, 127).
+
+Per-token activation quantization uses the same per-row rule on x[M][K]
+(both operands of the int8 x int8 and fp8 x fp8 products are quantized).
+
+Zero scales (all-zero group, or a scale that rounds to zero) give all-zero
+codes (0x00 for fp8).  Non-finite inputs raise ValueError; a scale that
+overflows its storage type raises OverflowError.
+"""
+
+import numpy as np
+
+from . import codecs
+
+W8_SYM = 1
+W4_SYM = 2
+W4_ASYM_SB256 = 3
+FP8_E4M3_CH = 4
+I8_CH = 5
+F16 = 6
+
+SB = 256          # superblock length
+SB_GROUP = 32     # group length inside a superblock
+SB_NGROUPS = SB // SB_GROUP
+
+
+def _check_finite(a):
+    if not np.all(np.isfinite(a)):
+        raise ValueError("non-finite input")
+
+
+def _rne(v):
+    return np.rint(v)
+
+
+def _group_low(wd):
+    """Lower end of each 32-group's range: min(0, min w) (zero stays reachable)."""
+    return np.minimum(0.0, np.min(wd, axis=3))
+
+
+def _qmax(bits):
+    """Largest code magnitude of a b-bit symmetric code: 2**(b-1) - 1."""
+    return (1 << (bits - 1)) - 1
+
+
+# --------------------------------------------------------------------------
+# symmetric group RTN
+# --------------------------------------------------------------------------
+
+
+def quantize_sym(w, bits, group):
+    """Symmetric group RTN of fp32 W[N][K]; returns dict(codes, scales, q).
+
+    ``q`` is the unpacked int code array [N][K] (int8), ``codes`` the stored
+    layout, ``scales`` fp16 [N][K/group].
+    """
+    w = np.asarray(w, dtype=np.float32)
+    _check_finite(w)
+    n, k = w.shape
+    if bits not in (4, 8) or group not in (16, 32, 64) or k % group:
+        raise ValueError("unsupported bits/group/shape")
+    qmax = _qmax(bits)
+    wd = w.astype(np.float64).reshape(n, k // group, group)
+    absmax = np.max(np.abs(wd), axis=2)
+    s16 = codecs.f16_encode(absmax / float(qmax))
+    if not np.all(np.isfinite(s16)):
+        raise OverflowError("fp16 scale overflow")
+    s = s16.astype(np.float64)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.clip(_rne(wd / s), -qmax, qmax)
+    q = np.where(s == 0.0, 0.0, q).astype(np.int8).reshape(n, k)
+    return {"codes": pack_sym(q, bits), "scales": s16, "q": q}
+
+
+def pack_sym(q, bits):
+    """Unpacked int codes [N][K] -> stored layout (int8, or int4 offset nibbles)."""
+    q = np.asarray(q)
+    if bits == 8:
+        return q.astype(np.int8)
+    u = (q.astype(np.int16) + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_sym(codes, bits):
+    """Stored layout -> unpacked int codes [N][K] (int8)."""
+    if bits == 8:
+        return np.asarray(codes).view(np.int8)
+    c = np.asarray(codes, dtype=np.uint8)
+    n, kh = c.shape
+    u = np.empty((n, 2 * kh), dtype=np.int16)
+    u[:, 0::2] = c & 0xF
+    u[:, 1::2] = c >> 4
+    return (u - 8).astype(np.int8)
+
+
+def dequant_sym(codes, scales, bits, group):
+    q = unpack_sym(codes, bits).astype(np.float64)
+    n, k = q.shape
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    return (q.reshape(n, k // group, group) * s[:, :, None]).reshape(n, k)
+
+
+# --------------------------------------------------------------------------
+# asymmetric 4-bit superblocks
+# --------------------------------------------------------------------------
+
+
+def quantize_sb256(w):
+    """Asymmetric superblock RTN of fp32 W[N][K] (K % 256 == 0).
+
+    Returns dict(qs, d, dmin, sub, q, sc, mc).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    _check_finite(w)
+    n, k = w.shape
+    if k % SB:
+        raise ValueError("K must be a multiple of 256")
+    nsb = k // SB
+    wd = w.astype(np.float64).reshape(n, nsb, SB_NGROUPS, SB_GROUP)
+    hi = np.max(wd, axis=3)
+    lo = _group_low(wd)
+    s = (hi - lo) / 15.0                       # fp64 group scale
+    neglo = -lo                                # fp64 group offset (>= 0)
+    d16 = codecs.f16_encode(np.max(s, axis=2) / 63.0)
+    m16 = codecs.f16_encode(np.max(neglo, axis=2) / 63.0)
+    if not (np.all(np.isfinite(d16)) and np.all(np.isfinite(m16))):
+        raise OverflowError("fp16 superblock scale overflow")
+    d = d16.astype(np.float64)[:, :, None]
+    dm = m16.astype(np.float64)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.clip(_rne(s / d), 0, 63)
+        mc = np.clip(_rne(neglo / dm), 0, 63)
+    sc = np.where(d == 0.0, 0.0, sc)
+    mc = np.where(dm == 0.0, 0.0, mc)
+    S = d * sc                                 # exact: 11-bit x 6-bit
+    M = dm * mc
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.clip(_rne((wd + M[..., None]) / S[..., None]), 0, 15)
+    q = np.where(S[..., None] == 0.0, 0.0, q)
+    q = q.astype(np.uint8).reshape(n, k)
+    sc = sc.astype(np.uint8)
+    mc = mc.astype(np.uint8)
+    qs = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    return {"qs": qs, "d": d16, "dmin": m16, "sub": pack_sub(sc, mc),
+            "q": q, "sc": sc, "mc": mc}
+
+
+def pack_sub(sc, mc):
+    """6-bit codes sc, mc [N][nsb][8] -> uint8 [N][nsb][12] bit stream.
+
+    Bit i of the 96-bit little-endian stream is bit (i % 8) of byte i // 8;
+    sc_j occupies bits 6j .. 6j+5 and mc_j bits 48+6j .. 48+6j+5.
+    """
+    sc = np.asarray(sc, dtype=np.uint64)
+    mc = np.asarray(mc, dtype=np.uint64)
+    lo48 = np.zeros(sc.shape[:-1], dtype=np.uint64)
+    hi48 = np.zeros(sc.shape[:-1], dtype=np.uint64)
+    for j in range(SB_NGROUPS):
+        lo48 |= sc[..., j] << np.uint64(6 * j)
+        hi48 |= mc[..., j] << np.uint64(6 * j)
+    out = np.empty(sc.shape[:-1] + (12,), dtype=np.uint8)
+    for b in range(6):
+        out[..., b] = (lo48 >> np.uint64(8 * b)) & np.uint64(0xFF)
+        out[..., 6 + b] = (hi48 >> np.uint64(8 * b)) & np.uint64(0xFF)
+    return out
+
+
+def unpack_sub(sub):
+    """uint8 [N][nsb][12] -> (sc, mc) uint8 [N][nsb][8]."""
+    sub = np.asarray(sub, dtype=np.uint8).astype(np.uint64)
+    lo48 = np.zeros(sub.shape[:-1], dtype=np.uint64)
+    hi48 = np.zeros(sub.shape[:-1], dtype=np.uint64)
+    for b in range(6):
+        lo48 |= sub[..., b] << np.uint64(8 * b)
+        hi48 |= sub[..., 6 + b] << np.uint64(8 * b)
+    sc = np.stack([(lo48 >> np.uint64(6 * j)) & np.uint64(63) for j in range(8)], -1)
+    mc = np.stack([(hi48 >> np.uint64(6 * j)) & np.uint64(63) for j in range(8)], -1)
+    return sc.astype(np.uint8), mc.astype(np.uint8)
+
+
+def dequant_sb256(qs, d, dmin, sub):
+    qs = np.asarray(qs, dtype=np.uint8)
+    n, kh = qs.shape
+    k = 2 * kh
+    q = np.empty((n, k), dtype=np.float64)
+    q[:, 0::2] = qs & 0xF
+    q[:, 1::2] = qs >> 4
+    sc, mc = unpack_sub(sub)
+    dd = np.asarray(d, dtype=np.float16).astype(np.float64)[:, :, None]
+    dm = np.asarray(dmin, dtype=np.float16).astype(np.float64)[:, :, None]
+    S = dd * sc.astype(np.float64)
+    M = dm * mc.astype(np.float64)
+    q = q.reshape(n, k // SB, SB_NGROUPS, SB_GROUP)
+    return (S[..., None] * q - M[..., None]).reshape(n, k)
+
+
+# --------------------------------------------------------------------------
+# per-row (per-output-channel weights / per-token activations) fp8 and int8
+# --------------------------------------------------------------------------
+
+
+def quantize_rows(a, kind):
+    """Per-row scale quantization of a[R][K] (fp32 weights or fp16 activations).
+
+    kind 'fp8': s = fp32(absmax/448), codes e4m3fn (uint8).
+    kind 'int8': s = fp32(absmax/127), codes int8 in -127..127.
+    Returns dict(codes, scales) with fp32 scales [R].
+    """
+    a = np.asarray(a)
+    _check_finite(a)
+    ad = a.astype(np.float64)
+    absmax = np.max(np.abs(ad), axis=1)
+    if kind == "fp8":
+        s32 = (absmax / codecs.E4M3_MAX).astype(np.float32)
+    elif kind == "int8":
+        s32 = (absmax / 127.0).astype(np.float32)
+    else:
+        raise ValueError(kind)
+    if not np.all(np.isfinite(s32)):
+        raise OverflowError("fp32 scale overflow")
+    s = s32.astype(np.float64)[:, None]
+    zero = s == 0.0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quo = np.where(zero, 0.0, ad / np.where(zero, 1.0, s))
+    if kind == "fp8":
+        codes = codecs.e4m3_encode(quo)
+        codes = np.where(zero, np.uint8(0), codes).astype(np.uint8)
+    else:
+        codes = np.clip(_rne(quo), -127, 127).astype(np.int8)
+    return {"codes": codes, "scales": s32}
+
+
+def dequant_rows(codes, scales, kind):
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)[:, None]
+    if kind == "fp8":
+        return codecs.e4m3_decode(codes) * s
+    return np.asarray(codes).view(np.int8).astype(np.float64) * s
+
+
+# --------------------------------------------------------------------------
+# uniform front door
+# --------------------------------------------------------------------------
+
+
+def quantize(w, fmt, group=0):
+    """Quantize fp32 W[N][K] into format ``fmt``; returns a dict of buffers."""
+    if fmt == W8_SYM:
+        return quantize_sym(w, 8, group)
+    if fmt == W4_SYM:
+        return quantize_sym(w, 4, group)
+    if fmt == W4_ASYM_SB256:
+        return quantize_sb256(w)
+    if fmt == FP8_E4M3_CH:
+        return quantize_rows(np.asarray(w, dtype=np.float32), "fp8")
+    if fmt == I8_CH:
+        return quantize_rows(np.asarray(w, dtype=np.float32), "int8")
+    if fmt == F16:
+        return {"codes": np.asarray(w, dtype=np.float16)}
+    raise ValueError("unknown format")
+
+
+def dequant(fmt, parts, group=0):
+    """Dequantize a dict of buffers (as returned by ``quantize``) to fp64 W_hat."""
+    if fmt == W8_SYM:
+        return dequant_sym(parts["codes"], parts["scales"], 8, group)
+    if fmt == W4_SYM:
+        return dequant_sym(parts["codes"], parts["scales"], 4, group)
+    if fmt == W4_ASYM_SB256:
+        return dequant_sb256(parts["qs"], parts["d"], parts["dmin"], parts["sub"])
+    if fmt == FP8_E4M3_CH:
+        return dequant_rows(parts["codes"], parts["scales"], "fp8")
+    if fmt == I8_CH:
+        return dequant_rows(parts["codes"], parts["scales"], "int8")
+    if fmt == F16:
+        return np.asarray(parts["codes"], dtype=np.float16).astype(np.float64)
+    raise ValueError("unknown format")
