@@ -1,0 +1,50 @@
+// Internal kernel launchers of librq (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rq {
+
+// ---- quantizers (quant.hip) ------------------------------------------------
+hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int group, void* codes,
+                            uint16_t* scales, int* flags, hipStream_t st);
+hipError_t launch_quant_sb256(const float* w, int64_t n, int64_t k, void* qs, void* d, void* dmin,
+                              void* sub, int* flags, hipStream_t st);
+hipError_t launch_quant_rows_f32(const float* w, int64_t n, int64_t k, bool fp8, void* codes,
+                                 float* scales, int* flags, hipStream_t st);
+hipError_t launch_quant_rows_f16(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, bool fp8,
+                                 void* codes, float* scales, int* flags, hipStream_t st);
+hipError_t launch_to_f16(const float* w, int64_t count, uint16_t* out, int* flags, hipStream_t st);
+
+// ---- weight-streaming products, 1 <= m <= 32 (gemv.hip) ----------------------
+enum GemvFormat { GF_W4 = 0, GF_W8 = 1, GF_SB = 2, GF_F16 = 3 };
+
+struct GemvMatrix {
+  const void* codes;
+  const uint16_t* scales;  // W4/W8: fp16 [n][k/g]; SB: d [n][k/256]
+  const uint16_t* mins;    // SB: dmin [n][k/256]
+  const uint32_t* sub;     // SB: [n][k/256][3] words
+  const uint16_t* x;       // fp16 [m][ldx]
+  uint16_t* y;             // fp16 [m][ldy]
+  int n;
+  int tiles;               // ceil(n / 16)
+};
+
+struct GemvBatch {
+  GemvMatrix mat[3];
+  int nmat;
+  int k;
+  int m;
+  int ldx;
+  int ldy;
+};
+
+hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
+
+// ---- MFMA GEMMs on per-row quantized operands (gemm_mfma.hip) ---------------
+hipError_t launch_gemm_w8a8(const void* xq, const float* sx, int m, const void* wq, const float* sw,
+                            int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out,
+                            hipStream_t st);
+
+}  // namespace rq

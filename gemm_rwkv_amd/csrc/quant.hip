@@ -1,0 +1,281 @@
+// Round-to-nearest quantizers: weights (fp32) into the librq formats and
+// per-token activations (fp16) into fp8 / int8 codes.
+//
+// Every scale and code is decided by IEEE fp64 operations followed by one
+// round-to-nearest-even step (device_common.h), so the results are exactly
+// those of the format definitions:
+//   symmetric groups  s = fp16(absmax / Q), q = clamp(RNE(w / s), -Q, Q)
+//     (model card "RWKV-7 G1 1.5B -- int4 GPTQ for rwkv-sglang", Format &
+//     loading: group-wise symmetric int4; Q = 127 for int8, 7 for int4)
+//   asymmetric superblocks of 256 = 8 x 32 with 6-bit sub-codes
+//     (rwkv-quant news article, "Dois presets e seis tamanhos")
+//   per-row fp8 e4m3fn / int8 with an fp32 scale
+//     (RWKV-7 Quantization Toolkit, Key Design: FP8 and INT8 GEMMs)
+// No fused multiply-add may merge these steps, so contraction is off here.
+#include "device_common.h"
+#include "kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace rq {
+
+// flags[0] <- 1 on a non-finite input, flags[1] <- 1 on a scale overflow
+// (flags may be null: per-token activation quantization reports nothing).
+__device__ __forceinline__ void raise_flag(int* flags, int which) {
+  if (flags) flags[which] = 1;
+}
+
+// ---------------------------------------------------------------------------
+// symmetric group RTN: one lane per 4 consecutive weights, G/4 lanes a group
+// ---------------------------------------------------------------------------
+template <int BITS, int G>
+__global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict__ w, int64_t total4,
+                                                        void* __restrict__ codes,
+                                                        uint16_t* __restrict__ scales,
+                                                        int* __restrict__ flags) {
+  constexpr int LPG = G / 4;
+  constexpr int Q = (1 << (BITS - 1)) - 1;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool active = t < total4;
+  float4 v = active ? w[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool fin = finite_f32(v.x) && finite_f32(v.y) && finite_f32(v.z) && finite_f32(v.w);
+  if (!fin) raise_flag(flags, 0);
+  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  a = group_max<LPG>(a);
+  const uint16_t sbits = f64_to_f16_bits((double)a / (double)Q);
+  if (sbits == 0x7c00u) raise_flag(flags, 1);
+  if (!active) return;
+  const double s = f16_bits_to_f64(sbits);
+  int q[4];
+  const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double r = s == 0.0 ? 0.0 : __builtin_rint((double)e[i] / s);
+    r = r > (double)Q ? (double)Q : (r < -(double)Q ? -(double)Q : r);
+    q[i] = (int)r;
+  }
+  if (BITS == 8) {
+    uint32_t packed = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                      ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+    ((uint32_t*)codes)[t] = packed;
+  } else {
+    uint32_t u0 = q[0] + 8, u1 = q[1] + 8, u2 = q[2] + 8, u3 = q[3] + 8;
+    ((uint16_t*)codes)[t] = (uint16_t)(u0 | (u1 << 4) | (u2 << 8) | (u3 << 12));
+  }
+  if ((t % LPG) == 0) scales[t / LPG] = sbits;
+}
+
+// ---------------------------------------------------------------------------
+// asymmetric 4-bit superblocks: one wave per 256 weights, 8 lanes per group
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) quant_sb256_kernel(const float4* __restrict__ w, int64_t nsb,
+                                                          uint16_t* __restrict__ qs,
+                                                          uint16_t* __restrict__ dout,
+                                                          uint16_t* __restrict__ mout,
+                                                          uint32_t* __restrict__ sub,
+                                                          int* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int64_t sbi = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  if (sbi >= nsb) return;  // uniform per wave
+  const float4 v = w[sbi * 64 + lane];
+  const bool fin = finite_f32(v.x) && finite_f32(v.y) && finite_f32(v.z) && finite_f32(v.w);
+  if (!fin) raise_flag(flags, 0);
+  float hi = group_max<8>(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  float lo = fminf(0.f, group_min<8>(fminf(fminf(v.x, v.y), fminf(v.z, v.w))));
+  double s = ((double)hi - (double)lo) / 15.0;
+  if (s == 0.0) s = 0.0;  // a zero range is +0
+  const double nl = 0.0 - (double)lo;
+  const double smax = group_max_d<64>(s);
+  const double nlmax = group_max_d<64>(nl);
+  const uint16_t db = f64_to_f16_bits(smax / 63.0);
+  const uint16_t mb = f64_to_f16_bits(nlmax / 63.0);
+  if (db == 0x7c00u || mb == 0x7c00u) raise_flag(flags, 1);
+  const double dd = f16_bits_to_f64(db);
+  const double dm = f16_bits_to_f64(mb);
+  double sc = dd == 0.0 ? 0.0 : __builtin_rint(s / dd);
+  double mc = dm == 0.0 ? 0.0 : __builtin_rint(nl / dm);
+  sc = sc < 0.0 ? 0.0 : (sc > 63.0 ? 63.0 : sc);
+  mc = mc < 0.0 ? 0.0 : (mc > 63.0 ? 63.0 : mc);
+  const double S = dd * sc;
+  const double M = dm * mc;
+  const float e[4] = {v.x, v.y, v.z, v.w};
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double r = S == 0.0 ? 0.0 : __builtin_rint(((double)e[i] + M) / S);
+    r = r < 0.0 ? 0.0 : (r > 15.0 ? 15.0 : r);
+    packed |= (uint32_t)r << (4 * i);
+  }
+  qs[sbi * 64 + lane] = (uint16_t)packed;
+  // gather the eight 6-bit pairs into lane 0
+  const uint32_t isc = (uint32_t)sc, imc = (uint32_t)mc;
+  uint64_t lo48 = 0, hi48 = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    lo48 |= (uint64_t)__shfl(isc, 8 * j) << (6 * j);
+    hi48 |= (uint64_t)__shfl(imc, 8 * j) << (6 * j);
+  }
+  if (lane == 0) {
+    dout[sbi] = db;
+    mout[sbi] = mb;
+    uint32_t* o = sub + sbi * 3;
+    o[0] = (uint32_t)lo48;
+    o[1] = (uint32_t)(lo48 >> 32) | ((uint32_t)hi48 << 16);
+    o[2] = (uint32_t)(hi48 >> 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-row fp8 / int8: one workgroup per row, scale from the row's absmax
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float (&o)[4]);
+
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float (&o)[4]) {
+  float4 v = *(const float4*)p;
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float (&o)[4]) {
+  uint2 v = *(const uint2*)p;
+  o[0] = f16_bits_to_f32((uint16_t)(v.x & 0xffff));
+  o[1] = f16_bits_to_f32((uint16_t)(v.x >> 16));
+  o[2] = f16_bits_to_f32((uint16_t)(v.y & 0xffff));
+  o[3] = f16_bits_to_f32((uint16_t)(v.y >> 16));
+}
+
+template <typename T, bool FP8>
+__global__ void __launch_bounds__(256) quant_rows_kernel(const T* __restrict__ in, int64_t k, int64_t ld,
+                                                         uint32_t* __restrict__ codes,
+                                                         float* __restrict__ scales,
+                                                         int* __restrict__ flags) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const T* r = in + row * ld;
+  const int64_t k4 = k >> 2;
+  float a = 0.f;
+  bool fin = true;
+  for (int64_t i = threadIdx.x; i < k4; i += 256) {
+    float e[4];
+    load4<T>(r + 4 * i, e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fin = fin && finite_f32(e[j]);
+      a = fmaxf(a, fabsf(e[j]));
+    }
+  }
+  if (!fin) raise_flag(flags, 0);
+  a = group_max<64>(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const uint32_t sb = f64_to_f32_bits((double)a / (FP8 ? 448.0 : 127.0));
+  if (sb == 0x7f800000u) raise_flag(flags, 1);
+  const double s = (double)__builtin_bit_cast(float, sb);
+  uint32_t* out = codes + row * k4;
+  for (int64_t i = threadIdx.x; i < k4; i += 256) {
+    float e[4];
+    load4<T>(r + 4 * i, e);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t c;
+      if (s == 0.0) {
+        c = 0;
+      } else if (FP8) {
+        c = f64_to_e4m3((double)e[j] / s);
+      } else {
+        double q = __builtin_rint((double)e[j] / s);
+        q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
+        c = (uint32_t)((int)q & 0xff);
+      }
+      packed |= c << (8 * j);
+    }
+    out[i] = packed;
+  }
+  if (threadIdx.x == 0) scales[row] = __builtin_bit_cast(float, sb);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> fp16 (RNE) for unquantized head weights
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) to_f16_kernel(const float* __restrict__ w, int64_t count,
+                                                     uint16_t* __restrict__ out, int* __restrict__ flags) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const float v = w[i];
+  if (!finite_f32(v)) raise_flag(flags, 0);
+  const uint16_t h = f64_to_f16_bits((double)v);
+  if ((h & 0x7fffu) == 0x7c00u) raise_flag(flags, 1);
+  out[i] = h;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+
+hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int group, void* codes,
+                            uint16_t* scales, int* flags, hipStream_t st) {
+  const int64_t total4 = n * k / 4;
+  if (total4 == 0) return hipSuccess;
+  const dim3 grid(grid_for(total4)), block(256);
+  const float4* w4 = (const float4*)w;
+#define RQ_SYM_CASE(B, G)                                                                   \
+  if (bits == B && group == G) {                                                            \
+    hipLaunchKernelGGL((quant_sym_kernel<B, G>), grid, block, 0, st, w4, total4, codes, scales, \
+                       flags);                                                              \
+    return hipGetLastError();                                                               \
+  }
+  RQ_SYM_CASE(8, 16)
+  RQ_SYM_CASE(8, 32)
+  RQ_SYM_CASE(8, 64)
+  RQ_SYM_CASE(4, 16)
+  RQ_SYM_CASE(4, 32)
+  RQ_SYM_CASE(4, 64)
+#undef RQ_SYM_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_sb256(const float* w, int64_t n, int64_t k, void* qs, void* d, void* dmin,
+                              void* sub, int* flags, hipStream_t st) {
+  const int64_t nsb = n * k / 256;
+  if (nsb == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_sb256_kernel, dim3(grid_for(nsb * 64)), dim3(256), 0, st, (const float4*)w,
+                     nsb, (uint16_t*)qs, (uint16_t*)d, (uint16_t*)dmin, (uint32_t*)sub, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_f32(const float* w, int64_t n, int64_t k, bool fp8, void* codes,
+                                 float* scales, int* flags, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (fp8)
+    hipLaunchKernelGGL((quant_rows_kernel<float, true>), dim3((unsigned)n), dim3(256), 0, st, w, k, k,
+                       (uint32_t*)codes, scales, flags);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<float, false>), dim3((unsigned)n), dim3(256), 0, st, w, k, k,
+                       (uint32_t*)codes, scales, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_f16(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, bool fp8,
+                                 void* codes, float* scales, int* flags, hipStream_t st) {
+  if (m == 0) return hipSuccess;
+  if (fp8)
+    hipLaunchKernelGGL((quant_rows_kernel<uint16_t, true>), dim3((unsigned)m), dim3(256), 0, st, x, k,
+                       ldx, (uint32_t*)codes, scales, flags);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<uint16_t, false>), dim3((unsigned)m), dim3(256), 0, st, x, k,
+                       ldx, (uint32_t*)codes, scales, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f16(const float* w, int64_t count, uint16_t* out, int* flags, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(to_f16_kernel, dim3(grid_for(count)), dim3(256), 0, st, w, count, out, flags);
+  return hipGetLastError();
+}
+
+}  // namespace rq

@@ -1,0 +1,214 @@
+/*
+ * rq.h -- C ABI of librq: matrix products that read group-wise quantized
+ * RWKV-7 projection weights directly, on AMD MI355X (gfx950).
+ *
+ * What is computed.  A weight matrix W[N][K] (N outputs, K inputs) is stored
+ * quantized; a product computes y[m][n] = sum_k x[m][k] * W_hat[n][k] where
+ * W_hat is the dequantized weight, without ever writing W_hat out.  This is
+ * the "no dequantization" inference of the RWKV-7 Quantization Toolkit page
+ * (Key Design) and the int4 GEMV / small-M GEMM family of the
+ * "RWKV-7 G1 1.5B -- int4 GPTQ for rwkv-sglang" model card (summary:
+ * decode at batch <= 32; "Format & loading": group-wise symmetric int4 with a
+ * .qweight code tensor and a .scale tensor, fp16 activations).
+ *
+ * Conventions shared by every entry point
+ *   - Every buffer pointer is a DEVICE pointer on the current HIP device,
+ *     except the rq_qweight descriptor itself and the size_t outputs of
+ *     rq_qweight_bytes, which live in host memory.  The caller allocates and
+ *     frees every buffer; the library keeps no pointer after returning.
+ *   - fp16 values are IEEE binary16 bit patterns (uint16_t).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; product calls return without synchronizing.
+ *   - Return value: RQ_OK (0) or a negative rq_status.  On a validation error
+ *     nothing is launched and no output is touched.  A failed launch returns
+ *     RQ_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronization.  No C++ exception crosses the ABI.
+ *   - Alignment: every device pointer must be 16-byte aligned (RQ_ERR_ALIGN);
+ *     leading dimensions of fp16 activation arrays (ldx) are multiples of 8
+ *     elements.  Outputs may not overlap any input (RQ_ERR_ALIAS).
+ *   - Shapes: n >= 0 and m >= 0 (zero = nothing to do, RQ_OK, but pointers must
+ *     still be valid), k >= 1, n and k below 2^31, and the per-format rules of
+ *     rq_qweight.
+ *   - Determinism: the same inputs on the same device give bit-identical
+ *     outputs (fixed reduction order, no floating-point atomics).
+ *   - Thread safety: the library is stateless; calls on different streams
+ *     may run concurrently.
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RQ_ABI_VERSION 1
+
+enum rq_status {
+  RQ_OK = 0,
+  RQ_ERR_NULL = -1,      /* a required pointer is NULL                         */
+  RQ_ERR_SHAPE = -2,     /* bad n, m, k, ld, or k not a multiple of the group  */
+  RQ_ERR_ALIGN = -3,     /* pointer or leading dimension misaligned            */
+  RQ_ERR_FORMAT = -4,    /* unknown format/group, or wrong entry for format    */
+  RQ_ERR_NONFINITE = -5, /* NaN or Inf in quantizer input                      */
+  RQ_ERR_RANGE = -6,     /* a scale overflows its storage type                 */
+  RQ_ERR_HIP = -7,       /* a HIP runtime call failed                          */
+  RQ_ERR_ALIAS = -8      /* an output overlaps an input                        */
+};
+
+/*
+ * Weight formats.  Layouts are row-major over W[N][K]; "group" runs along K
+ * inside one row.
+ *
+ * RQ_W8_SYM, RQ_W4_SYM (group 16, 32 or 64; k % group == 0)
+ *   Symmetric round-to-nearest codes with one fp16 scale per (row, group):
+ *   Q = 127 (int8) or 7 (int4), s = fp16(absmax / Q), q = clamp(RNE(w/s), -Q, Q),
+ *   W_hat = q * s.  Model card, "Format & loading" (GROUP=64 symmetric int4)
+ *   and accuracy warning (int8 w8g64 tier); rwkv-quant news article, section
+ *   "Dois presets e seis tamanhos" (8-bit symmetric projections, group 16).
+ *     codes : int8 [n][k]                          (W8)
+ *             uint8 [n][k/2], u = q + 8, even k in the low nibble   (W4)
+ *     scales: fp16 [n][k/group]
+ * RQ_W4_ASYM_SB256 (group must be 32; k % 256 == 0)
+ *   Asymmetric 4-bit codes in superblocks of 256 = 8 groups of 32 (news
+ *   article, "Dois presets e seis tamanhos": 4-bit asymmetric superblocks,
+ *   group 32).  Per group j: S_j = d * sc_j, M_j = dmin * mc_j,
+ *   W_hat = S_j * q - M_j with q in 0..15.
+ *     codes : uint8 [n][k/2] (q nibbles, even k low)
+ *     scales: fp16 d    [n][k/256]
+ *     mins  : fp16 dmin [n][k/256]
+ *     sub   : uint8 [n][k/256][12]: 96-bit little-endian stream, sc_j at bit
+ *             6j and mc_j at bit 48 + 6j (6-bit codes)
+ * RQ_FP8_E4M3_CH, RQ_I8_CH (group ignored; k % 16 == 0; the MFMA GEMMs need
+ *   k % 128 == 0)
+ *   One fp32 scale per output row: s_n = fp32(absmax_n / 448) with OCP e4m3fn
+ *   codes (saturating RNE), or fp32(absmax_n / 127) with int8 codes in
+ *   -127..127 (RWKV-7 Quantization Toolkit, Key Design: FP8 weights on FP8
+ *   tensor cores, INT8 through int8 x int8 dot products).
+ *     codes : uint8 (e4m3fn) or int8 [n][k];  scales: fp32 [n]
+ * RQ_F16 (group ignored; k % 8 == 0)
+ *   Unquantized fp16 weights, used for the output head, which the toolkit
+ *   keeps in FP16 (Key Design) and the model card keeps full precision.
+ *     codes : fp16 [n][k];  scales, mins, sub: unused
+ *
+ * For quantizers, a zero scale (all-zero group, or a scale that rounds to
+ * zero) gives all-zero codes.
+ */
+enum rq_format {
+  RQ_W8_SYM = 1,
+  RQ_W4_SYM = 2,
+  RQ_W4_ASYM_SB256 = 3,
+  RQ_FP8_E4M3_CH = 4,
+  RQ_I8_CH = 5,
+  RQ_F16 = 6
+};
+
+/* Host-side descriptor of one quantized weight; the four buffers are device
+ * pointers laid out as described for the format (unused ones may be NULL). */
+typedef struct rq_qweight {
+  int32_t format;
+  int32_t group;
+  int64_t n;
+  int64_t k;
+  void *codes;
+  void *scales;
+  void *mins;
+  void *sub;
+} rq_qweight;
+
+/* ABI version of the loaded library (RQ_ABI_VERSION). */
+int rq_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *rq_status_str(int status);
+
+/* Byte sizes of the four buffers of a (format, group, n, k) weight.  Any of
+ * the output pointers may be NULL.  Host-only; launches nothing.
+ * Errors: RQ_ERR_FORMAT, RQ_ERR_SHAPE. */
+int rq_qweight_bytes(int format, int group, int64_t n, int64_t k, size_t *codes_bytes,
+                     size_t *scales_bytes, size_t *mins_bytes, size_t *sub_bytes);
+
+/* Round-to-nearest quantization of fp32 weights w[n][k] (device, contiguous)
+ * into the format, group, n and k named by *out, whose buffers the caller has
+ * allocated with rq_qweight_bytes sizes.  Every quotient is an IEEE fp64
+ * division followed by one rounding to the target grid, so the codes and
+ * scales are exactly those of the format's definition.  Synchronizes `stream`
+ * (it reads back a status word); allocates and frees 4 bytes of device memory
+ * per call.  Errors: validation codes, RQ_ERR_NONFINITE (NaN/Inf in w),
+ * RQ_ERR_RANGE (a scale overflows fp16/fp32); after those two the output
+ * buffers hold unspecified bytes.  RQ_F16 converts to fp16 (RNE). */
+int rq_quantize_rtn(const float *w, const rq_qweight *out, void *stream);
+
+/* M = 1 products y[n] = sum_k x[k] * W_hat[n][k], fp32 accumulation, fp16
+ * output (RNE).  x: fp16 [k]; y: fp16 [n].  Each entry point accepts exactly
+ * its format and group (RQ_ERR_FORMAT otherwise):
+ *   w4gG: RQ_W4_SYM, group G;  w8gG: RQ_W8_SYM, group G;
+ *   w4sb256: RQ_W4_ASYM_SB256;  f16: RQ_F16. */
+int rq_gemv_w4g16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_w4g32(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_w4g64(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_w8g16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_w8g32(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_w8g64(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_w4sb256(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+
+/* Small-M products for decode batches 1 <= m <= 32 (model card, summary:
+ * batch sizes up to 32).  x: fp16 [m][ldx], ldx >= k, ldx % 8 == 0;
+ * y: fp16 [m][ldy], ldy >= n.  Accepts RQ_W8_SYM, RQ_W4_SYM,
+ * RQ_W4_ASYM_SB256 and RQ_F16.  The weights are read once per call.
+ * Errors: RQ_ERR_SHAPE for m outside 0..32. */
+int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w,
+                    uint16_t *y, int64_t ldy, void *stream);
+
+/* The R, K and V projections in one launch (RWKV-7 Quantization Toolkit,
+ * Key Design: "R/K/V projections computed in a single kernel launch").
+ * Three independent small-M products with a shared m, ldx and ldy; the three
+ * weights must have the same format, group and k (their n may differ).
+ * xr, xk, xv may be the same pointer (a shared input); the outputs may not
+ * overlap each other or any input. */
+int rq_fused_rkv(const uint16_t *xr, const uint16_t *xk, const uint16_t *xv, int64_t m,
+                 int64_t ldx, const rq_qweight *wr, const rq_qweight *wk, const rq_qweight *wv,
+                 uint16_t *yr, uint16_t *yk, uint16_t *yv, int64_t ldy, void *stream);
+
+/* Per-token dynamic activation quantization for the W8A8 / FP8 GEMMs (both
+ * operands of the toolkit's int8 x int8 and fp8 x fp8 products are
+ * quantized): for each row m of x (fp16 [m][ldx]), s_x[m] = fp32(absmax/448)
+ * with e4m3fn codes (format RQ_FP8_E4M3_CH) or fp32(absmax/127) with int8
+ * codes in -127..127 (RQ_I8_CH), quotients in fp64.  xq: [m][k] bytes,
+ * contiguous; sx: fp32 [m].  k % 16 == 0. */
+int rq_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int format, void *xq,
+                    float *sx, void *stream);
+
+/* FP8 x FP8 GEMM on MFMA: y[m][n] = fp16(s_x[m] * s_w[n] * sum_k dec(xq[m][k]) *
+ * dec(wq[n][k])) with fp32 accumulation (toolkit, Key Design and
+ * Architecture: FP8 GEMM with shape-aware tile configurations).  xq: e4m3fn
+ * [m][k]; w: RQ_FP8_E4M3_CH with k % 128 == 0; y: fp16 [m][ldy], ldy >= n.
+ * Any m >= 0. */
+int rq_gemm_fp8(const uint8_t *xq, const float *sx, int64_t m, const rq_qweight *w, uint16_t *y,
+                int64_t ldy, void *stream);
+
+/* INT8 x INT8 GEMM on MFMA with exact int32 accumulation ("INT8 via DP4A" on
+ * the toolkit page): y[m][n] = fp16(float(acc) * s_x[m] * s_w[n]).
+ * w: RQ_I8_CH with k % 128 == 0 and k <= 131072 (|acc| < 2^31). */
+int rq_gemm_int8(const int8_t *xq, const float *sx, int64_t m, const rq_qweight *w, uint16_t *y,
+                 int64_t ldy, void *stream);
+
+/* The int32 accumulators of rq_gemm_int8 (acc: int32 [m][n], contiguous),
+ * for bit-exact checking of the integer contraction. */
+int rq_gemm_int8_acc(const int8_t *xq, int64_t m, const rq_qweight *w, int32_t *acc, void *stream);
+
+/* Test aid: the library's own fp64 -> fp16 (kind 0, uint16 out), fp64 ->
+ * fp32 (kind 1, uint32 out) and fp64 -> e4m3fn (kind 2, uint8 out)
+ * round-to-nearest-even conversions, run on the host over `count` values of
+ * host arrays.  These are the conversions the quantizer kernels use.
+ * Errors: RQ_ERR_NULL, RQ_ERR_SHAPE (count < 0), RQ_ERR_FORMAT (kind). */
+int rq_host_convert(int kind, const double *in, void *out, int64_t count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H */
