@@ -20,10 +20,11 @@
 //     formats), or by S_j and corrected by M_j * sum(x) (asymmetric
 //     superblocks, with sum(x) from one MFMA against ones), so the effective
 //     weight q*s is exact.
-//   * Decoding packs codes in the order (0,4,1,5,2,6,3,7) (int4) or
-//     (0,2,1,3,...) (int8); the activation fragment is permuted to match with
-//     v_perm_b32, which is free to choose because a dot product does not
-//     depend on the order of its terms.
+//   * Where a decoder yields codes out of k order ((0,2,1,3,...) for int8 in
+//     this kernel, one parity of an int4 word for int4 group 16) the
+//     activation fragment is permuted to match with v_perm_b32, which is free
+//     to choose because a dot product does not depend on the order of its
+//     terms.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -73,23 +74,32 @@ __device__ __forceinline__ uint32_t hsub2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// 8 int4 codes (one word, k order 0..7) -> fp16 (q - bias) in order 0,4,1,5,2,6,3,7.
-// bias_lo/bias_hi: 1032 / 72 for offset-binary symmetric codes, 1024 / 64 for
-// unsigned superblock codes.
-template <bool SIGNED>
-__device__ __forceinline__ half8 dec_w4x8(uint32_t v) {
-  const uint32_t b1024 = SIGNED ? 0x64086408u : 0x64006400u;  // 1032 : 1024
-  const uint32_t b64 = SIGNED ? 0x54805480u : 0x54005400u;    // 72 : 64
-  uint32_t v8 = v >> 8;
-  uint32_t h0 = hsub2((v & 0x000f000fu) | 0x64006400u, b1024);
-  uint32_t h1 = hsub2((v & 0x00f000f0u) | 0x54005400u, b64);
-  uint32_t h2 = hsub2((v8 & 0x000f000fu) | 0x64006400u, b1024);
-  uint32_t h3 = hsub2((v8 & 0x00f000f0u) | 0x54005400u, b64);
-  uint4 r = make_uint4(h0, h1, h2, h3);
-  return __builtin_bit_cast(half8, r);
+// (v & m) | o in one instruction (v_bitop3_b32, truth table 0xEA)
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t o) {
+  return __builtin_amdgcn_bitop3_b32(v, m, o, 0xEA);
 }
 
-// 4 int4 codes (16 bits, k order 0..3) -> fp16 in order 0,2,1,3
+// One int4 code word (8 consecutive k: even k in nibbles 0..3 of the low
+// half-word, odd k in those of the high half-word) -> fp16 (u - bias) for
+// k = 0..7 in natural order.  Nibbles 0 and 2 of both halves land in the
+// mantissa of 1024 (ulp 1), nibbles 1 and 3 in that of 64 (ulp 1/16), so each
+// pair (2i, 2i + 1) is one AND-OR and one packed subtract of the bias:
+// 1032 / 72 for offset-binary symmetric codes (u = q + 8), 1024 / 64 for the
+// unsigned superblock codes.
+template <bool SIGNED>
+__device__ __forceinline__ half8 dec4n(uint32_t v) {
+  const uint32_t blo = SIGNED ? 0x64086408u : 0x64006400u;  // 1032 : 1024
+  const uint32_t bhi = SIGNED ? 0x54805480u : 0x54005400u;  // 72 : 64
+  const uint32_t v8 = v >> 8;
+  const uint32_t h0 = hsub2(and_or(v, 0x000f000fu, 0x64006400u), blo);
+  const uint32_t h1 = hsub2(and_or(v, 0x00f000f0u, 0x54005400u), bhi);
+  const uint32_t h2 = hsub2(and_or(v8, 0x000f000fu, 0x64006400u), blo);
+  const uint32_t h3 = hsub2(and_or(v8, 0x00f000f0u, 0x54005400u), bhi);
+  return __builtin_bit_cast(half8, make_uint4(h0, h1, h2, h3));
+}
+
+// One half-word of an int4 code word (4 codes of one parity: k offsets
+// 0, 2, 4, 6 from the lane's first k) -> fp16 q in order 0, 4, 2, 6
 __device__ __forceinline__ half4 dec_w4x4(uint32_t v) {
   uint32_t t = perm(0u, v, 0x0c010c00u);  // bytes: b0, 0, b1, 0
   uint32_t h0 = hsub2((t & 0x000f000fu) | 0x64006400u, 0x64086408u);
@@ -108,15 +118,16 @@ __device__ __forceinline__ uint2 dec_w8x4_raw(uint32_t v) {
 
 // activation permutations matching the decoders
 // natural halves d0=(x0,x1) d1=(x2,x3) d2=(x4,x5) d3=(x6,x7)
-__device__ __forceinline__ half8 xperm_w4x8(uint4 d) {
-  uint4 r = make_uint4(perm(d.z, d.x, 0x05040100u), perm(d.z, d.x, 0x07060302u),
-                       perm(d.w, d.y, 0x05040100u), perm(d.w, d.y, 0x07060302u));
-  return __builtin_bit_cast(half8, r);
-}
 __device__ __forceinline__ half8 xperm_w8x8(uint4 d) {
   uint4 r = make_uint4(perm(d.y, d.x, 0x05040100u), perm(d.y, d.x, 0x07060302u),
                        perm(d.w, d.z, 0x05040100u), perm(d.w, d.z, 0x07060302u));
   return __builtin_bit_cast(half8, r);
+}
+// x for dec_w4x4: natural halves d (8 k from the word's first k), the
+// lane's parity picked by sel (0x05040100 even, 0x07060302 odd)
+__device__ __forceinline__ half4 xsel_w4x4(uint4 d, uint32_t sel) {
+  uint2 r = make_uint2(perm(d.z, d.x, sel), perm(d.w, d.y, sel));
+  return __builtin_bit_cast(half4, r);
 }
 __device__ __forceinline__ half4 xperm_x4(uint2 d) {
   uint2 r = make_uint2(perm(d.y, d.x, 0x05040100u), perm(d.y, d.x, 0x07060302u));
@@ -175,14 +186,19 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
     subrow = A.sub + (size_t)nrow * (ng / 8) * 3;
   }
   // activation rows held by this lane (A operand rows), zero beyond m
+  constexpr bool W4Q = FMT == GF_W4 && F::LK == 4;
   bool mval[MT];
   const uint16_t* xrow[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = t * 16 + j;
     mval[t] = m < p.m;
-    xrow[t] = A.x + (size_t)(mval[t] ? m : 0) * p.ldx + kq * F::LK;
+    // int4 with 4 k per lane: the lane's codes are one parity of the code
+    // word at k 8 * (kq / 2); its x come from the 8 k of that word
+    xrow[t] = A.x + (size_t)(mval[t] ? m : 0) * p.ldx + (W4Q ? 8 * (kq >> 1) : kq * F::LK);
   }
+  const uint32_t xsel = (kq & 1) ? 0x07060302u : 0x05040100u;
+  (void)xsel;
 
   float4v acc[MT];
 #pragma unroll
@@ -230,6 +246,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
             if constexpr (NT > 1) xv[u][t][NT > 1 ? 1 : 0] = *(const uint4*)(xp + 8);
           } else if constexpr (F::LK == 8) {
             xv[u][t][0] = *(const uint4*)xp;
+          } else if constexpr (W4Q) {
+            xv[u][t][0] = *(const uint4*)xp;
           } else {
             uint2 h = *(const uint2*)xp;
             xv[u][t][0] = make_uint4(h.x, h.y, 0u, 0u);
@@ -255,9 +273,9 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
         if constexpr (LKM == 8) {
           half8 b;
           if constexpr (FMT == GF_W4) {
-            b = dec_w4x8<true>(w_at(cw[u], s));
+            b = dec4n<true>(w_at(cw[u], s));
           } else if constexpr (FMT == GF_SB) {
-            b = dec_w4x8<false>(w_at(cw[u], s));
+            b = dec4n<false>(w_at(cw[u], s));
           } else if constexpr (FMT == GF_W8) {
             uint2 lo = dec_w8x4_raw(w_at(cw[u], 2 * s));
             uint2 hi = dec_w8x4_raw(w_at(cw[u], 2 * s + 1));
@@ -268,9 +286,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             half8 a;
-            if constexpr (FMT == GF_W4 || FMT == GF_SB)
-              a = xperm_w4x8(xv[u][t][s]);
-            else if constexpr (FMT == GF_W8)
+            if constexpr (FMT == GF_W8)
               a = xperm_w8x8(xv[u][t][s]);
             else
               a = __builtin_bit_cast(half8, xv[u][t][s]);
@@ -294,7 +310,11 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
           }
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
-            half4 a = xperm_x4(make_uint2(xv[u][t][0].x, xv[u][t][0].y));
+            half4 a;
+            if constexpr (FMT == GF_W4)
+              a = xsel_w4x4(xv[u][t][0], xsel);
+            else
+              a = xperm_x4(make_uint2(xv[u][t][0].x, xv[u][t][0].y));
             grp[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, grp[t], 0, 0, 0);
           }
         }
@@ -341,6 +361,665 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
 }
 
 // ---------------------------------------------------------------------------
+// streaming kernel: 16-byte code loads per lane through a prefetch ring
+// ---------------------------------------------------------------------------
+// A "chunk" is 16 bytes of codes per lane, 64 bytes per row (4 lanes), i.e.
+// CK = 128 (int4), 64 (int8) or 32 (fp16) values of k.  A chunk holds GPC
+// scale groups; before the MFMAs the four lanes of a row exchange words with
+// v_permlane32_swap / v_permlane16_swap so that every MFMA's 32 (or 16) k
+// belong to one group:
+//   GPC = 2: swap32(w0,w2), swap32(w1,w3): lanes keep the half of each group
+//            at k offsets {0,32,16,48}[kq] (int4) or {0,16,8,24}[kq] (int8);
+//   GPC = 4: a 4x4 word transpose across the four lanes (two swap32, two
+//            swap16): lane kq then holds word kq of every group.
+// Codes decode into fp16 in natural k order, so activations are used as
+// stored.  Codes and scales come through raw buffer loads (scalar base,
+// 32-bit lane offset; an invalid chunk reads zeros through an out-of-range
+// scalar offset, so the loop body has no branches).
+//
+// Vector loads of one wave complete in issue order.  So activations either
+//   XL: sit in LDS, copied there once per workgroup by an extra staging wave
+//       with global_load_lds (its wait does not hold up the compute waves'
+//       code loads), rows m >= M reading a zero row; or
+//   !XL: travel in each ring slot beside the codes of the same chunk.
+template <int FMT, int G>
+struct F2 {
+  static constexpr int CK = (FMT == GF_W4 || FMT == GF_SB) ? 128 : (FMT == GF_W8 ? 64 : 32);
+  static constexpr int GK = (FMT == GF_SB || FMT == GF_F16) ? 32 : G;
+  static constexpr int GPC = CK / GK;
+  static constexpr int KPM = (FMT == GF_W8 && G == 16) ? 16 : 32;  // k per MFMA
+  static constexpr int MPG = GK / KPM;                             // MFMAs per group
+  static constexpr int NM = GPC * MPG;                             // MFMAs per chunk
+  static constexpr int XH = KPM / 4;                               // x halves per lane per MFMA
+};
+
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+// 4 int8 codes -> fp16 q in natural order (q + 128 lands in the mantissa of 1024)
+__device__ __forceinline__ uint2 dec8n(uint32_t v) {
+  const uint32_t u = v ^ 0x80808080u;
+  const uint32_t lo = perm(0x64646464u, u, 0x04010400u);
+  const uint32_t hi = perm(0x64646464u, u, 0x04030402u);
+  return make_uint2(hsub2(lo, 0x64806480u), hsub2(hi, 0x64806480u));
+}
+
+// k offset (within the chunk) of the x values matching MFMA (g, p) on lane kq
+template <int FMT, int G>
+__device__ __forceinline__ int x_base(int kq) {
+  typedef F2<FMT, G> F;
+  if constexpr (F::GPC == 1) {
+    if constexpr (FMT == GF_F16) return 8 * kq;
+    return 16 * kq;  // int8 g64
+  } else if constexpr (F::GPC == 2) {
+    if constexpr (FMT == GF_W4) return (kq & 1) * 32 + (kq >> 1) * 16;
+    return (kq & 1) * 16 + (kq >> 1) * 8;  // int8 g32
+  } else {
+    return kq * F::XH;  // int4 g32 / SB (8 k), int8 g16 (4 k)
+  }
+}
+template <int FMT, int G>
+constexpr int x_const(int g, int p) {
+  typedef F2<FMT, G> F;
+  if constexpr (F::GPC == 1) return FMT == GF_F16 ? 0 : 8 * p;
+  else if constexpr (F::GPC == 2) return FMT == GF_W4 ? 64 * g + 8 * p : 32 * g;
+  else return g * F::GK;
+}
+
+template <int FMT, int G, int MT, bool XL>
+struct RingSlot {
+  uint4 c;      // codes
+  uint32_t s;   // scales (1-2 fp16) or SB d | dmin << 16
+  uint32_t s2;  // scales 3-4 (int4 g32, int8 g16)
+  uint32_t sub[FMT == GF_SB ? 3 : 1];
+  uint4 x[XL ? 1 : F2<FMT, G>::NM][XL ? 1 : MT];  // activation fragments (!XL)
+};
+
+template <int FMT, int G, int MT, int NW, int P, bool XL>
+__global__ void __launch_bounds__((NW + (XL ? 1 : 0)) * 64)
+gemv3_kernel(const GemvBatch p, int cpw) {
+  typedef F2<FMT, G> F;
+  typedef RingSlot<FMT, G, MT, XL> S;
+  constexpr int NM = F::NM;
+  // dynamic LDS: (XL) the activations [(m + 1) rows][k + 8 halves] during the
+  // loop, then the waves' partial sums [NW][MT][4][64] (after a barrier)
+  extern __shared__ uint4 lds4[];
+  uint16_t* xl = (uint16_t*)lds4;
+  float (*red)[MT][4][64] = (float (*)[MT][4][64])lds4;
+
+  int tile = blockIdx.x;
+  int mi = 0;
+  if (tile >= p.mat[0].tiles) {
+    tile -= p.mat[0].tiles;
+    mi = 1;
+    if (tile >= p.mat[1].tiles) {
+      tile -= p.mat[1].tiles;
+      mi = 2;
+    }
+  }
+  const GemvMatrix& A = p.mat[mi];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15;
+  const int kq = lane >> 4;
+  const int n = tile * 16 + j;
+  const bool nvalid = n < A.n;
+  const int k = p.k;
+  const int M = p.m;
+  const int nchunks = k / F::CK;
+  const int ldl = k + 8;                          // LDS row stride (halves)
+  constexpr uint32_t kOOB = 0x7ffff000u;          // scalar offset past any buffer
+
+  if constexpr (XL) {
+    if (wave == NW) {
+      // staging wave: x rows < M into LDS (64 blocks of 8 halves per
+      // instruction), then the zero row; wait for its own copies only
+      const int blocks = k / 8;
+      for (int m = 0; m < M; ++m) {
+        for (int b0 = 0; b0 < blocks; b0 += 64) {
+          const int b = b0 + lane;
+          if (b < blocks) {
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(A.x + (size_t)m * p.ldx + (size_t)b * 8),
+                (__attribute__((address_space(3))) void*)((uint8_t*)lds4 + ((size_t)m * ldl + b0 * 8) * 2), 16,
+                0, 0);
+          }
+        }
+      }
+      for (int b = lane; b < blocks; b += 64) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
+      __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the copies have landed
+    }
+  }
+
+  // buffer resources (num_records in bytes).  Rows >= n read row 0: their
+  // output columns are never stored and MFMA columns are independent.
+  const uint32_t rowbytes = (uint32_t)nchunks * 64u;
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A.codes, (short)0, (int)((uint32_t)A.n * rowbytes), 0x00020000);
+  const uint32_t coff = (nvalid ? (uint32_t)n * rowbytes : 0u) + (uint32_t)kq * 16u;
+  __amdgpu_buffer_rsrc_t rs = rc, rm = rc, rb = rc;
+  uint32_t soff = 0, sboff = 0, subb = 0;
+  if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+    const uint32_t srow = (uint32_t)(k / F::GK) * 2u;
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * srow), 0x00020000);
+    soff = nvalid ? (uint32_t)n * srow : 0u;
+  } else if constexpr (FMT == GF_SB) {
+    const uint32_t nsb = (uint32_t)(k / 256);
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * nsb * 2u), 0x00020000);
+    rm = __builtin_amdgcn_make_buffer_rsrc((void*)A.mins, (short)0, (int)((uint32_t)A.n * nsb * 2u), 0x00020000);
+    rb = __builtin_amdgcn_make_buffer_rsrc((void*)A.sub, (short)0, (int)((uint32_t)A.n * nsb * 12u), 0x00020000);
+    sboff = nvalid ? (uint32_t)n * nsb * 2u : 0u;
+    subb = nvalid ? (uint32_t)n * nsb * 12u : 0u;
+  }
+  // activation rows of this lane (A operand), !XL: from global, zero beyond M
+  bool mval[MT];
+  const uint16_t* xg[MT];
+  int xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = t * 16 + j;
+    mval[t] = m < M;
+    xg[t] = A.x + (size_t)(mval[t] ? m : 0) * p.ldx + x_base<FMT, G>(kq);
+    xrow[t] = (mval[t] ? m : M) * ldl + x_base<FMT, G>(kq);
+  }
+
+  auto load = [&](S& sl, int c, bool valid) {
+    const uint32_t so = valid ? (uint32_t)c * 64u : kOOB;
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, so, 0);
+    sl.c = make_uint4(v[0], v[1], v[2], v[3]);
+    if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+      const uint32_t ss = valid ? (uint32_t)c * (F::GPC * 2) : kOOB;
+      if constexpr (F::GPC == 1) {
+        sl.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, ss, 0);
+      } else if constexpr (F::GPC == 2) {
+        sl.s = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, ss, 0);
+      } else {
+        auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, ss, 0);
+        sl.s = t[0];
+        sl.s2 = t[1];
+      }
+    } else if constexpr (FMT == GF_SB) {
+      const uint32_t sb = (uint32_t)c >> 1;
+      const uint32_t s2 = valid ? sb * 2u : kOOB;
+      const uint32_t s12 = valid ? sb * 12u : kOOB;
+      const uint32_t d = __builtin_amdgcn_raw_buffer_load_b16(rs, sboff, s2, 0);
+      const uint32_t dm = __builtin_amdgcn_raw_buffer_load_b16(rm, sboff, s2, 0);
+      sl.s = d | (dm << 16);
+      auto t = __builtin_amdgcn_raw_buffer_load_b96(rb, subb, s12, 0);
+      sl.sub[0] = t[0];
+      sl.sub[1] = t[1];
+      sl.sub[2] = t[2];
+    }
+    if constexpr (!XL) {
+      const int cc = valid ? c : 0;  // an invalid chunk's codes and scales are zero
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        const int off = cc * F::CK + x_const<FMT, G>(q / F::MPG, q % F::MPG);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          if constexpr (F::XH == 8) {
+            sl.x[q][t] = mval[t] ? *(const uint4*)(xg[t] + off) : make_uint4(0u, 0u, 0u, 0u);
+          } else {
+            uint2 h = mval[t] ? *(const uint2*)(xg[t] + off) : make_uint2(0u, 0u);
+            sl.x[q][t] = make_uint4(h.x, h.y, 0u, 0u);
+          }
+        }
+      }
+    }
+  };
+
+  float4v acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+  const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // kk: chunk start (halves); for an invalid chunk a valid start (its codes
+  // and scales are zero)
+  auto compute = [&](const S& sl, int c, int kk) {
+    uint32_t w[4] = {sl.c.x, sl.c.y, sl.c.z, sl.c.w};
+    uint32_t gw[4][2];
+    if constexpr (F::GPC == 2) {
+      swap32(w[0], w[2]);
+      swap32(w[1], w[3]);
+      gw[0][0] = w[0]; gw[0][1] = w[1];
+      gw[1][0] = w[2]; gw[1][1] = w[3];
+    } else if constexpr (F::GPC == 4) {
+      swap32(w[0], w[2]);
+      swap32(w[1], w[3]);
+      swap16(w[0], w[1]);
+      swap16(w[2], w[3]);
+      gw[0][0] = w[0]; gw[1][0] = w[1]; gw[2][0] = w[2]; gw[3][0] = w[3];
+    }
+    float scl[4], mnv[4];
+    if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+      scl[0] = f16_bits_to_f32((uint16_t)(sl.s & 0xffffu));
+      scl[1] = f16_bits_to_f32((uint16_t)(sl.s >> 16));
+      if constexpr (F::GPC == 4) {
+        scl[2] = f16_bits_to_f32((uint16_t)(sl.s2 & 0xffffu));
+        scl[3] = f16_bits_to_f32((uint16_t)(sl.s2 >> 16));
+      }
+    } else if constexpr (FMT == GF_SB) {
+      const float d = f16_bits_to_f32((uint16_t)(sl.s & 0xffffu));
+      const float dm = f16_bits_to_f32((uint16_t)(sl.s >> 16));
+      const uint64_t lo48 = (uint64_t)sl.sub[0] | ((uint64_t)(sl.sub[1] & 0xffffu) << 32);
+      const uint64_t hi48 = (uint64_t)(sl.sub[1] >> 16) | ((uint64_t)sl.sub[2] << 16);
+      const int half = (c & 1) * 4;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        scl[g] = d * (float)((uint32_t)(lo48 >> (6 * (half + g))) & 63u);  // exact
+        mnv[g] = dm * (float)((uint32_t)(hi48 >> (6 * (half + g))) & 63u);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < F::GPC; ++g) {
+      float4v grp[MT], xs[MT];
+#pragma unroll
+      for (int pp = 0; pp < F::MPG; ++pp) {
+        const int q = g * F::MPG + pp;
+        const int xo = kk + x_const<FMT, G>(g, pp);
+        if constexpr (F::KPM == 32) {
+          half8 b;
+          if constexpr (FMT == GF_F16) {
+            b = __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));
+          } else if constexpr (FMT == GF_W4 || FMT == GF_SB) {
+            b = dec4n<FMT == GF_W4>(F::GPC == 2 ? gw[g][pp] : gw[g][0]);
+          } else {  // int8: 8 k per MFMA
+            uint32_t wa, wb;
+            if constexpr (F::GPC == 1) {
+              wa = w[2 * pp];
+              wb = w[2 * pp + 1];
+            } else {
+              wa = gw[g][0];
+              wb = gw[g][1];
+            }
+            const uint2 lo = dec8n(wa), hi = dec8n(wb);
+            b = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          }
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            half8 a;
+            if constexpr (XL) a = *(const half8*)(xl + xrow[t] + xo);
+            else a = __builtin_bit_cast(half8, sl.x[q][t]);
+            if constexpr (FMT == GF_F16) {
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+            } else {
+              grp[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, pp == 0 ? zero4 : grp[t], 0, 0, 0);
+              if constexpr (FMT == GF_SB) {
+                const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+                xs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, zero4, 0, 0, 0);
+              }
+            }
+          }
+        } else {  // int8 group 16: 4 k per lane, 16x16x16
+          const uint2 r = dec8n(gw[g][0]);
+          const half4 b = __builtin_bit_cast(half4, r);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            half4 a;
+            if constexpr (XL) a = *(const half4*)(xl + xrow[t] + xo);
+            else a = __builtin_bit_cast(half4, make_uint2(sl.x[q][t].x, sl.x[q][t].y));
+            grp[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, zero4, 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (FMT != GF_F16) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            acc[t][r] += scl[g] * grp[t][r];
+            if constexpr (FMT == GF_SB) acc[t][r] -= mnv[g] * xs[t][r];
+          }
+      }
+    }
+  };
+
+  if (wave < NW) {
+    const int w0 = wave * cpw;  // this wave's first chunk
+    S ring[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) load(ring[q], w0 + q, w0 + q < nchunks);
+    if constexpr (XL) __syncthreads();  // the staging wave's copies are in LDS
+    for (int s0 = 0; s0 < cpw; s0 += P) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int c = w0 + s0 + q;
+        const int cv = c < nchunks ? c : nchunks - 1;  // keep the activation offset in range
+        compute(ring[q], cv, cv * F::CK);
+        const int cn = c + P;
+        if (s0 + P < cpw) load(ring[q], cn, cn < nchunks && s0 + q + P < cpw);
+      }
+    }
+  } else {
+    if constexpr (XL) __syncthreads();
+  }
+
+  if constexpr (NW > 1 || XL) {
+    __syncthreads();  // every wave is done with the staged activations
+    if (wave < NW) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][t][r][lane] = acc[t][r];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < MT * 4 * 64; idx += (NW + (XL ? 1 : 0)) * 64) {
+      const int t = idx / 256, r = (idx / 64) & 3, l = idx & 63;
+      float v = red[0][t][r][l];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) v += red[w2][t][r][l];
+      const int m = t * 16 + 4 * (l >> 4) + r;
+      const int nn = tile * 16 + (l & 15);
+      if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = t * 16 + 4 * kq + r;
+        if (m < M && nvalid) A.y[(size_t)m * p.ldy + n] = f32_to_f16_bits(acc[t][r]);
+      }
+  }
+}
+
+constexpr int kXBudget = 80 * 1024;  // bytes of LDS for staged activations
+
+// ---------------------------------------------------------------------------
+// upfront kernel (activations in LDS): every wave owns CPW chunks of one
+// 16-row tile and issues all of their loads before computing
+// ---------------------------------------------------------------------------
+// With only a few chunks per wave a refilling ring adds a round trip per
+// refill; issuing everything at once keeps the most bytes in flight.  The
+// workgroup's waves split K (NW = blockDim / 64 waves, a launch parameter);
+// each copies its share of the activations into LDS with global_load_lds
+// after issuing its code loads, then all wait and meet at a barrier.
+// MR: activation rows that can be non-zero among a lane's four outputs
+// (m <= MR), so scale multiplications skip rows that are known to be zero.
+template <int FMT, int G, int MT, int CPW, int MR>
+__global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
+  typedef F2<FMT, G> F;
+  typedef RingSlot<FMT, G, MT, true> S;
+  extern __shared__ uint4 lds4[];
+  uint16_t* xl = (uint16_t*)lds4;
+
+  // pick the matrix of this tile; every field of the three descriptors is
+  // read unconditionally so the choice costs no dependent scalar load
+  int tile = blockIdx.x;
+  const int t0 = p.mat[0].tiles, t1 = p.mat[1].tiles;
+  const bool in1 = tile >= t0, in2 = tile >= t0 + t1;
+  tile -= in2 ? t0 + t1 : (in1 ? t0 : 0);
+  GemvMatrix A;
+  A.codes = in2 ? p.mat[2].codes : (in1 ? p.mat[1].codes : p.mat[0].codes);
+  A.scales = in2 ? p.mat[2].scales : (in1 ? p.mat[1].scales : p.mat[0].scales);
+  A.mins = in2 ? p.mat[2].mins : (in1 ? p.mat[1].mins : p.mat[0].mins);
+  A.sub = in2 ? p.mat[2].sub : (in1 ? p.mat[1].sub : p.mat[0].sub);
+  A.x = in2 ? p.mat[2].x : (in1 ? p.mat[1].x : p.mat[0].x);
+  A.y = in2 ? p.mat[2].y : (in1 ? p.mat[1].y : p.mat[0].y);
+  A.n = in2 ? p.mat[2].n : (in1 ? p.mat[1].n : p.mat[0].n);
+  const int NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15;
+  const int kq = lane >> 4;
+  const int n = tile * 16 + j;
+  const bool nvalid = n < A.n;
+  const int k = p.k;
+  const int M = p.m;
+  const int nchunks = k / F::CK;
+  const int ldl = k + 8;
+  constexpr uint32_t kOOB = 0x7ffff000u;
+
+  const uint32_t rowbytes = (uint32_t)nchunks * 64u;
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A.codes, (short)0, (int)((uint32_t)A.n * rowbytes), 0x00020000);
+  const uint32_t coff = (nvalid ? (uint32_t)n * rowbytes : 0u) + (uint32_t)kq * 16u;
+  __amdgpu_buffer_rsrc_t rs = rc, rm = rc, rb = rc;
+  uint32_t soff = 0, sboff = 0, subb = 0;
+  if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+    const uint32_t srow = (uint32_t)(k / F::GK) * 2u;
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * srow), 0x00020000);
+    soff = nvalid ? (uint32_t)n * srow : 0u;
+  } else if constexpr (FMT == GF_SB) {
+    const uint32_t nsb = (uint32_t)(k / 256);
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * nsb * 2u), 0x00020000);
+    rm = __builtin_amdgcn_make_buffer_rsrc((void*)A.mins, (short)0, (int)((uint32_t)A.n * nsb * 2u), 0x00020000);
+    rb = __builtin_amdgcn_make_buffer_rsrc((void*)A.sub, (short)0, (int)((uint32_t)A.n * nsb * 12u), 0x00020000);
+    sboff = nvalid ? (uint32_t)n * nsb * 2u : 0u;
+    subb = nvalid ? (uint32_t)n * nsb * 12u : 0u;
+  }
+
+  // 1. this wave's codes and scales, all at once.  Invalid chunks read zero
+  //    codes; their scales are zeroed after loading (the scale span is read
+  //    in one piece and may run into the next row)
+  const int c0 = wave * CPW;
+  S sl[CPW];
+  constexpr int SW = (FMT == GF_W4 || FMT == GF_W8) ? (CPW * F::GPC * 2 + 3) / 4 : 1;  // scale words
+  uint32_t sw[SW];
+  if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+    const uint32_t ss = (uint32_t)c0 * (F::GPC * 2);
+    if constexpr (SW >= 4) {
+#pragma unroll
+      for (int q = 0; q < SW / 4; ++q) {
+        auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, soff, ss + 16u * q, 0);
+        sw[4 * q] = t[0]; sw[4 * q + 1] = t[1]; sw[4 * q + 2] = t[2]; sw[4 * q + 3] = t[3];
+      }
+    } else if constexpr (SW == 2) {
+      auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, ss, 0);
+      sw[0] = t[0]; sw[1] = t[1];
+    } else {
+      sw[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, ss, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = c0 + i;
+    const bool valid = c < nchunks;
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, valid ? (uint32_t)c * 64u : kOOB, 0);
+    sl[i].c = make_uint4(v[0], v[1], v[2], v[3]);
+    if constexpr (FMT == GF_SB) {
+      const uint32_t sb = (uint32_t)c >> 1;
+      const uint32_t s2 = valid ? sb * 2u : kOOB;
+      const uint32_t s12 = valid ? sb * 12u : kOOB;
+      const uint32_t d = __builtin_amdgcn_raw_buffer_load_b16(rs, sboff, s2, 0);
+      const uint32_t dm = __builtin_amdgcn_raw_buffer_load_b16(rm, sboff, s2, 0);
+      sl[i].s = d | (dm << 16);
+      auto t = __builtin_amdgcn_raw_buffer_load_b96(rb, subb, s12, 0);
+      sl[i].sub[0] = t[0];
+      sl[i].sub[1] = t[1];
+      sl[i].sub[2] = t[2];
+    }
+  }
+
+  // 2. this wave's share of the activations: rows < M, 64 blocks of 8
+  //    halves per copy instruction, copy instructions dealt round-robin
+  {
+    const int blocks = k / 8;
+    const int per_row = (blocks + 63) / 64;
+    for (int q = wave; q < M * per_row; q += NW) {
+      const int m = q / per_row;
+      const int b0 = (q - m * per_row) * 64;
+      const int b = b0 + lane;
+      if (b < blocks)
+        __builtin_amdgcn_global_load_lds((const void*)(A.x + (size_t)m * p.ldx + (size_t)b * 8),
+                                         (__attribute__((address_space(3))) void*)((uint8_t*)lds4 + ((size_t)m * ldl + b0 * 8) * 2),
+                                         16, 0, 0);
+    }
+    for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and codes) have landed
+    __syncthreads();
+  }
+
+  int xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = t * 16 + j;
+    xrow[t] = (m < M ? m : M) * ldl + x_base<FMT, G>(kq);
+  }
+  float4v acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+  const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // 3. compute, chunk by chunk
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = c0 + i < nchunks ? c0 + i : nchunks - 1;  // activation offset in range
+    const int kk = c * F::CK;
+    uint32_t w[4] = {sl[i].c.x, sl[i].c.y, sl[i].c.z, sl[i].c.w};
+    uint32_t gw[4][2];
+    if constexpr (F::GPC == 2) {
+      swap32(w[0], w[2]);
+      swap32(w[1], w[3]);
+      gw[0][0] = w[0]; gw[0][1] = w[1];
+      gw[1][0] = w[2]; gw[1][1] = w[3];
+    } else if constexpr (F::GPC == 4) {
+      swap32(w[0], w[2]);
+      swap32(w[1], w[3]);
+      swap16(w[0], w[1]);
+      swap16(w[2], w[3]);
+      gw[0][0] = w[0]; gw[1][0] = w[1]; gw[2][0] = w[2]; gw[3][0] = w[3];
+    }
+    float scl[4], mnv[4];
+    if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+      const bool valid = c0 + i < nchunks;
+#pragma unroll
+      for (int g = 0; g < F::GPC; ++g) {
+        const int h = i * F::GPC + g;  // half-word index in the wave's scale span
+        const uint32_t word = sw[h >> 1];
+        const float v = f16_bits_to_f32((uint16_t)((h & 1) ? (word >> 16) : (word & 0xffffu)));
+        scl[g] = valid ? v : 0.f;
+      }
+    } else if constexpr (FMT == GF_SB) {
+      const float d = f16_bits_to_f32((uint16_t)(sl[i].s & 0xffffu));
+      const float dm = f16_bits_to_f32((uint16_t)(sl[i].s >> 16));
+      const uint64_t lo48 = (uint64_t)sl[i].sub[0] | ((uint64_t)(sl[i].sub[1] & 0xffffu) << 32);
+      const uint64_t hi48 = (uint64_t)(sl[i].sub[1] >> 16) | ((uint64_t)sl[i].sub[2] << 16);
+      const int half = (c & 1) * 4;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        scl[g] = d * (float)((uint32_t)(lo48 >> (6 * (half + g))) & 63u);  // exact
+        mnv[g] = dm * (float)((uint32_t)(hi48 >> (6 * (half + g))) & 63u);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < F::GPC; ++g) {
+      float4v grp[MT], xs[MT];
+#pragma unroll
+      for (int pp = 0; pp < F::MPG; ++pp) {
+        const int xo = kk + x_const<FMT, G>(g, pp);
+        if constexpr (F::KPM == 32) {
+          half8 b;
+          if constexpr (FMT == GF_F16) {
+            b = __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));
+          } else if constexpr (FMT == GF_W4 || FMT == GF_SB) {
+            b = dec4n<FMT == GF_W4>(F::GPC == 2 ? gw[g][pp] : gw[g][0]);
+          } else {
+            uint32_t wa, wb;
+            if constexpr (F::GPC == 1) {
+              wa = w[2 * pp];
+              wb = w[2 * pp + 1];
+            } else {
+              wa = gw[g][0];
+              wb = gw[g][1];
+            }
+            const uint2 lo = dec8n(wa), hi = dec8n(wb);
+            b = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          }
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const half8 a = *(const half8*)(xl + xrow[t] + xo);
+            if constexpr (FMT == GF_F16) {
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+            } else {
+              grp[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, pp == 0 ? zero4 : grp[t], 0, 0, 0);
+              if constexpr (FMT == GF_SB) {
+                const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+                xs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, zero4, 0, 0, 0);
+              }
+            }
+          }
+        } else {
+          const uint2 r = dec8n(gw[g][0]);
+          const half4 b = __builtin_bit_cast(half4, r);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const half4 a = *(const half4*)(xl + xrow[t] + xo);
+            grp[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, zero4, 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (FMT != GF_F16) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int r = 0; r < (MT == 1 ? MR : 4); ++r) {
+            acc[t][r] += scl[g] * grp[t][r];
+            if constexpr (FMT == GF_SB) acc[t][r] -= mnv[g] * xs[t][r];
+          }
+      }
+    }
+  }
+
+  // 4. combine the waves' partial sums in wave order and store fp16
+  float (*red)[MT][4][64] = (float (*)[MT][4][64])lds4;
+  __syncthreads();  // everyone is done with the activations
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][t][r][lane] = acc[t][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MT * 4 * 64; idx += blockDim.x) {
+    const int t = idx / 256, r = (idx / 64) & 3, l = idx & 63;
+    float v = red[0][t][r][l];
+    for (int w2 = 1; w2 < NW; ++w2) v += red[w2][t][r][l];
+    const int m = t * 16 + 4 * (l >> 4) + r;
+    const int nn = tile * 16 + (l & 15);
+    if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
+  }
+}
+
+// activations staged in LDS, loads up front; returns false when the shape
+// needs another kernel (activations too large, or more than 16 waves)
+template <int FMT, int G>
+static bool launch4(const GemvBatch& b, hipStream_t st, hipError_t& err) {
+  typedef F2<FMT, G> F;
+  const size_t xb = (size_t)(b.m + 1) * (b.k + 8) * 2;
+  if (xb > (size_t)kXBudget) return false;
+  int tiles = 0;
+  for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
+  const int nchunks = b.k / F::CK;
+  const int cpw = nchunks <= 64 ? 4 : 8;
+  const int nw = (nchunks + cpw - 1) / cpw;
+  if (nw > 16) return false;
+  const int mt = b.m <= 16 ? 1 : 2;
+  const size_t red = (size_t)nw * mt * 4 * 64 * 4;
+  const size_t lds = xb > red ? xb : red;
+  const dim3 grid(tiles), block(nw * 64);
+#define RQ_L4(MT, CPW, MR) hipLaunchKernelGGL((gemv4_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b)
+  if (mt == 2) {
+    if (cpw == 4) RQ_L4(2, 4, 4); else RQ_L4(2, 8, 4);
+  } else if (b.m == 1) {
+    if (cpw == 4) RQ_L4(1, 4, 1); else RQ_L4(1, 8, 1);
+  } else if (b.m == 2) {
+    if (cpw == 4) RQ_L4(1, 4, 2); else RQ_L4(1, 8, 2);
+  } else {
+    if (cpw == 4) RQ_L4(1, 4, 4); else RQ_L4(1, 8, 4);
+  }
+#undef RQ_L4
+  err = hipGetLastError();
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 template <int FMT, int G, int MT, int NW>
@@ -364,8 +1043,75 @@ static hipError_t launch_nw(const GemvBatch& b, hipStream_t st) {
   return launch_t<FMT, G, MT, 1>(b, st);
 }
 
+
+template <int FMT, int G, int MT, int NW, bool XL>
+static hipError_t launch3_p(const GemvBatch& b, hipStream_t st, int tiles, int cpw, size_t lds) {
+  constexpr int PMAX = XL ? 8 : (MT == 1 ? 4 : 2);
+  const int threads = (NW + (XL ? 1 : 0)) * 64;
+  if (cpw <= 4 || PMAX == 4) {
+    const int c = (cpw + 3) / 4 * 4;
+    if constexpr (PMAX >= 4) {
+      hipLaunchKernelGGL((gemv3_kernel<FMT, G, MT, NW, 4, XL>), dim3(tiles), dim3(threads), lds, st, b, c);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (PMAX == 8) {
+    const int c = (cpw + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemv3_kernel<FMT, G, MT, NW, 8, XL>), dim3(tiles), dim3(threads), lds, st, b, c);
+  } else {
+    const int c = (cpw + 1) / 2 * 2;
+    hipLaunchKernelGGL((gemv3_kernel<FMT, G, MT, NW, 2, XL>), dim3(tiles), dim3(threads), lds, st, b, c);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int G, int MT, int NW>
+static hipError_t launch3_t(const GemvBatch& b, hipStream_t st, int tiles) {
+  const int nchunks = b.k / F2<FMT, G>::CK;
+  const int cpw = (nchunks + NW - 1) / NW;
+  const size_t xb = (size_t)(b.m + 1) * (b.k + 8) * 2;
+  const size_t red = (size_t)NW * MT * 4 * 64 * 4;
+  if (xb <= (size_t)kXBudget) return launch3_p<FMT, G, MT, NW, true>(b, st, tiles, cpw, xb > red ? xb : red);
+  if constexpr (NW <= 8) return launch3_p<FMT, G, MT, NW, false>(b, st, tiles, cpw, NW > 1 ? red : 0);
+  return hipErrorInvalidValue;
+}
+
+// waves per workgroup: enough waves in the grid to keep HBM busy, at least
+// two chunks per wave
+template <int FMT, int G, int MT>
+static hipError_t launch3_nw(const GemvBatch& b, hipStream_t st) {
+  typedef F2<FMT, G> F;
+  int tiles = 0;
+  for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
+  if (tiles == 0) return hipSuccess;
+  const int nchunks = b.k / F::CK;
+  const bool xl = (size_t)(b.m + 1) * (b.k + 8) * 2 <= (size_t)kXBudget;
+  int nw = xl ? 15 : 8;
+  if (xl) {
+    nw = 8;
+    while (nw > 1 && (nchunks / nw < 2 || tiles * (nw / 2) >= 4096)) nw /= 2;
+  } else {
+    while (nw > 1 && (nchunks / nw < 2 || tiles * (nw / 2) >= 4096)) nw /= 2;
+  }
+  switch (nw) {
+    case 8: return launch3_t<FMT, G, MT, 8>(b, st, tiles);
+    case 4: return launch3_t<FMT, G, MT, 4>(b, st, tiles);
+    case 2: return launch3_t<FMT, G, MT, 2>(b, st, tiles);
+    default: return launch3_t<FMT, G, MT, 1>(b, st, tiles);
+  }
+}
+
 template <int FMT, int G>
 static hipError_t launch_mt(const GemvBatch& b, hipStream_t st) {
+  constexpr bool v2ok = !(FMT == GF_W4 && G == 16);
+  if constexpr (v2ok) {
+    if (b.k % F2<FMT, G>::CK == 0) {
+      hipError_t err;
+      if (launch4<FMT, G>(b, st, err)) return err;
+      if (b.m <= 16) return launch3_nw<FMT, G, 1>(b, st);
+      return launch3_nw<FMT, G, 2>(b, st);
+    }
+  }
   if (b.m <= 16) return launch_nw<FMT, G, 1>(b, st);
   return launch_nw<FMT, G, 2>(b, st);
 }

@@ -19,6 +19,18 @@
 
 namespace rq {
 
+// Four 4-bit values of consecutive k (k % 8 == 0 for the even lane of a pair,
+// 4 for the odd lane) -> the whole 32-bit code word of those 8 k, assembled
+// with the partner lane: in a word even k fill the low half-word and odd k the
+// high half-word, nibble i of each half holding pair i (k = 2i, 2i + 1).
+// Called by both lanes of every pair (it shuffles); only the even lane stores.
+__device__ __forceinline__ uint32_t nibble_word_part(uint32_t u0, uint32_t u1, uint32_t u2,
+                                                     uint32_t u3, int odd) {
+  const uint32_t lo = u0 | (u2 << 4), hi = u1 | (u3 << 4);  // pairs 0,1 or 2,3
+  const uint32_t mine = odd ? ((lo << 8) | (hi << 24)) : (lo | (hi << 16));
+  return mine | (uint32_t)__shfl_xor((int)mine, 1);
+}
+
 // flags[0] <- 1 on a non-finite input, flags[1] <- 1 on a scale overflow
 // (flags may be null: per-token activation quantization reports nothing).
 __device__ __forceinline__ void raise_flag(int* flags, int which) {
@@ -44,7 +56,6 @@ __global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict
   a = group_max<LPG>(a);
   const uint16_t sbits = f64_to_f16_bits((double)a / (double)Q);
   if (sbits == 0x7c00u) raise_flag(flags, 1);
-  if (!active) return;
   const double s = f16_bits_to_f64(sbits);
   int q[4];
   const float e[4] = {v.x, v.y, v.z, v.w};
@@ -57,19 +68,19 @@ __global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict
   if (BITS == 8) {
     uint32_t packed = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
                       ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
-    ((uint32_t*)codes)[t] = packed;
+    if (active) ((uint32_t*)codes)[t] = packed;
   } else {
-    uint32_t u0 = q[0] + 8, u1 = q[1] + 8, u2 = q[2] + 8, u3 = q[3] + 8;
-    ((uint16_t*)codes)[t] = (uint16_t)(u0 | (u1 << 4) | (u2 << 8) | (u3 << 12));
+    const uint32_t w = nibble_word_part(q[0] + 8, q[1] + 8, q[2] + 8, q[3] + 8, t & 1);
+    if (active && (t & 1) == 0) ((uint32_t*)codes)[t >> 1] = w;
   }
-  if ((t % LPG) == 0) scales[t / LPG] = sbits;
+  if (active && (t % LPG) == 0) scales[t / LPG] = sbits;
 }
 
 // ---------------------------------------------------------------------------
 // asymmetric 4-bit superblocks: one wave per 256 weights, 8 lanes per group
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) quant_sb256_kernel(const float4* __restrict__ w, int64_t nsb,
-                                                          uint16_t* __restrict__ qs,
+                                                          uint32_t* __restrict__ qs,
                                                           uint16_t* __restrict__ dout,
                                                           uint16_t* __restrict__ mout,
                                                           uint32_t* __restrict__ sub,
@@ -99,14 +110,15 @@ __global__ void __launch_bounds__(256) quant_sb256_kernel(const float4* __restri
   const double S = dd * sc;
   const double M = dm * mc;
   const float e[4] = {v.x, v.y, v.z, v.w};
-  uint32_t packed = 0;
+  uint32_t u[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     double r = S == 0.0 ? 0.0 : __builtin_rint(((double)e[i] + M) / S);
     r = r < 0.0 ? 0.0 : (r > 15.0 ? 15.0 : r);
-    packed |= (uint32_t)r << (4 * i);
+    u[i] = (uint32_t)r;
   }
-  qs[sbi * 64 + lane] = (uint16_t)packed;
+  const uint32_t qw = nibble_word_part(u[0], u[1], u[2], u[3], lane & 1);
+  if ((lane & 1) == 0) qs[sbi * 32 + (lane >> 1)] = qw;
   // gather the eight 6-bit pairs into lane 0
   const uint32_t isc = (uint32_t)sc, imc = (uint32_t)mc;
   uint64_t lo48 = 0, hi48 = 0;
@@ -244,7 +256,7 @@ hipError_t launch_quant_sb256(const float* w, int64_t n, int64_t k, void* qs, vo
   const int64_t nsb = n * k / 256;
   if (nsb == 0) return hipSuccess;
   hipLaunchKernelGGL(quant_sb256_kernel, dim3(grid_for(nsb * 64)), dim3(256), 0, st, (const float4*)w,
-                     nsb, (uint16_t*)qs, (uint16_t*)d, (uint16_t*)dmin, (uint32_t*)sub, flags);
+                     nsb, (uint32_t*)qs, (uint16_t*)d, (uint16_t*)dmin, (uint32_t*)sub, flags);
   return hipGetLastError();
 }
 

@@ -21,8 +21,8 @@ W8_SYM / W4_SYM, group G in {16, 32, 64} along K
     (codes -7..7, -8 unused) extends the int8 rule; the pages do not print it
     ("parity unpinned by the pages": pinned by the exact round-trip tests).
     int8 codes: two's complement int8 [N][K].
-    int4 codes: offset binary u = q + 8 in 1..15, two per byte, the even k in
-    the low nibble: uint8 [N][K/2].  Scales: fp16 [N][K/G].
+    int4 codes: offset binary u = q + 8 in 1..15, eight per little-endian
+    32-bit word (see pack_nibbles): uint8 [N][K/2].  Scales: fp16 [N][K/G].
 
 W4_ASYM_SB256
     Asymmetric 4-bit codes in superblocks of 256 = 8 groups of 32 (news
@@ -35,7 +35,7 @@ W4_ASYM_SB256
     q = clamp(RNE((w + M_j) / S_j), 0, 15); w_hat = S_j * q - M_j.
     The article chooses scale and offset by an activation-weighted search; this
     format uses plain RTN for them ("parity unpinned by the pages").
-    Storage: qs uint8 [N][K/2] (nibbles, even k low), d fp16 [N][K/256],
+    Storage: qs uint8 [N][K/2] (nibbles as pack_nibbles), d fp16 [N][K/256],
     dmin fp16 [N][K/256], sub uint8 [N][K/256][12] = a little-endian 96-bit
     stream with sc_j at bit 6j and mc_j at bit 48 + 6j.
 
@@ -118,25 +118,55 @@ def quantize_sym(w, bits, group):
     return {"codes": pack_sym(q, bits), "scales": s16, "q": q}
 
 
+def pack_nibbles(u):
+    """4-bit values u[N][K] (0..15, K % 8 == 0) -> uint8 [N][K/2].
+
+    The library's int4 layout (the pages give none): each run of 8
+    consecutive k is one little-endian 32-bit word; bits 4i..4i+3 hold
+    k = 2i (even k in the low half-word) and bits 16+4i..16+4i+3 hold
+    k = 2i+1.  As bytes: [u0|u2<<4, u4|u6<<4, u1|u3<<4, u5|u7<<4].
+    """
+    u = np.asarray(u, dtype=np.uint8)
+    n, k = u.shape
+    w = u.reshape(n, k // 8, 8)
+    out = np.empty((n, k // 8, 4), dtype=np.uint8)
+    out[..., 0] = w[..., 0] | (w[..., 2] << 4)
+    out[..., 1] = w[..., 4] | (w[..., 6] << 4)
+    out[..., 2] = w[..., 1] | (w[..., 3] << 4)
+    out[..., 3] = w[..., 5] | (w[..., 7] << 4)
+    return out.reshape(n, k // 2)
+
+
+def unpack_nibbles(c):
+    """uint8 [N][K/2] in the pack_nibbles layout -> 4-bit values [N][K] (uint8)."""
+    c = np.asarray(c, dtype=np.uint8)
+    n, kh = c.shape
+    b = c.reshape(n, kh // 4, 4)
+    u = np.empty((n, kh // 4, 8), dtype=np.uint8)
+    u[..., 0] = b[..., 0] & 0xF
+    u[..., 2] = b[..., 0] >> 4
+    u[..., 4] = b[..., 1] & 0xF
+    u[..., 6] = b[..., 1] >> 4
+    u[..., 1] = b[..., 2] & 0xF
+    u[..., 3] = b[..., 2] >> 4
+    u[..., 5] = b[..., 3] & 0xF
+    u[..., 7] = b[..., 3] >> 4
+    return u.reshape(n, 2 * kh)
+
+
 def pack_sym(q, bits):
     """Unpacked int codes [N][K] -> stored layout (int8, or int4 offset nibbles)."""
     q = np.asarray(q)
     if bits == 8:
         return q.astype(np.int8)
-    u = (q.astype(np.int16) + 8).astype(np.uint8)
-    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    return pack_nibbles((q.astype(np.int16) + 8).astype(np.uint8))
 
 
 def unpack_sym(codes, bits):
     """Stored layout -> unpacked int codes [N][K] (int8)."""
     if bits == 8:
         return np.asarray(codes).view(np.int8)
-    c = np.asarray(codes, dtype=np.uint8)
-    n, kh = c.shape
-    u = np.empty((n, 2 * kh), dtype=np.int16)
-    u[:, 0::2] = c & 0xF
-    u[:, 1::2] = c >> 4
-    return (u - 8).astype(np.int8)
+    return (unpack_nibbles(codes).astype(np.int16) - 8).astype(np.int8)
 
 
 def dequant_sym(codes, scales, bits, group):
@@ -186,7 +216,7 @@ def quantize_sb256(w):
     q = q.astype(np.uint8).reshape(n, k)
     sc = sc.astype(np.uint8)
     mc = mc.astype(np.uint8)
-    qs = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    qs = pack_nibbles(q)
     return {"qs": qs, "d": d16, "dmin": m16, "sub": pack_sub(sc, mc),
             "q": q, "sc": sc, "mc": mc}
 
@@ -225,12 +255,8 @@ def unpack_sub(sub):
 
 
 def dequant_sb256(qs, d, dmin, sub):
-    qs = np.asarray(qs, dtype=np.uint8)
-    n, kh = qs.shape
-    k = 2 * kh
-    q = np.empty((n, k), dtype=np.float64)
-    q[:, 0::2] = qs & 0xF
-    q[:, 1::2] = qs >> 4
+    q = unpack_nibbles(qs).astype(np.float64)
+    n, k = q.shape
     sc, mc = unpack_sub(sub)
     dd = np.asarray(d, dtype=np.float16).astype(np.float64)[:, :, None]
     dm = np.asarray(dmin, dtype=np.float16).astype(np.float64)[:, :, None]

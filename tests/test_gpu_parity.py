@@ -178,7 +178,7 @@ def test_integer_special_case_exact(fmt, group):
     if fmt == quant.W4_ASYM_SB256:
         q = g.integers(0, 16, (n, k))
         nsb = k // 256
-        parts = {"qs": (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8),
+        parts = {"qs": quant.pack_nibbles(q),
                  "d": np.ones((n, nsb), np.float16), "dmin": np.ones((n, nsb), np.float16),
                  "sub": quant.pack_sub(np.ones((n, nsb, 8), np.uint8), np.full((n, nsb, 8), 8, np.uint8))}
         wint = q - 8

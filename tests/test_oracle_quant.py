@@ -190,10 +190,8 @@ def check_sb_brute(seed, n=6, k=512):
     sc, mc = quant.unpack_sub(r["sub"])
     d = r["d"].astype(np.float64)
     dm = r["dmin"].astype(np.float64)
-    q = np.empty((n, k), dtype=np.int64)
-    q[:, 0::2] = r["qs"] & 0xF
-    q[:, 1::2] = r["qs"] >> 4
-    q = q.reshape(n, nsb, 8, 32)
+    # the nibble layout itself is pinned bit by bit in test_nibble_layout_bitwise
+    q = quant.unpack_nibbles(r["qs"]).astype(np.int64).reshape(n, nsb, 8, 32)
     for i in range(n):
         for b in range(nsb):
             hi = wg[i, b].max(-1)
@@ -469,11 +467,27 @@ def test_mutation_fp16_double_rounding(monkeypatch):
         __import__("test_oracle_codecs").test_f16_encode_midpoints_and_neighbours()
 
 
+def test_nibble_layout_bitwise():
+    # bit-by-bit construction of each 32-bit word, independent of the packer:
+    # code k = 8w + 2i sits at bits 4i, code k = 8w + 2i + 1 at bits 16 + 4i
+    g = np.random.default_rng(17)
+    u = g.integers(0, 16, (5, 64)).astype(np.uint8)
+    packed = quant.pack_nibbles(u)
+    for r in range(5):
+        for w in range(8):
+            word = 0
+            for i in range(4):
+                word |= int(u[r, 8 * w + 2 * i]) << (4 * i)
+                word |= int(u[r, 8 * w + 2 * i + 1]) << (16 + 4 * i)
+            assert packed[r, 4 * w:4 * w + 4].tolist() == [(word >> (8 * b)) & 0xFF for b in range(4)]
+    assert np.array_equal(quant.unpack_nibbles(packed), u)
+
+
 def test_mutation_nibble_order(monkeypatch):
-    def swapped(q, bits):
+    def naive(q, bits):
         u = (np.asarray(q).astype(np.int16) + 8).astype(np.uint8)
-        return (u[:, 1::2] | (u[:, 0::2] << 4)).astype(np.uint8)
-    monkeypatch.setattr(quant, "pack_sym", swapped)
+        return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    monkeypatch.setattr(quant, "pack_sym", naive)
     with pytest.raises(AssertionError):
         test_sym_hand_examples("sym_int4_g16", 4)
 

@@ -72,7 +72,7 @@ def test_sb256_integer_closed_form():
     w = (q - 8).astype(np.float32)
     # one group per superblock with range [-63, 0] pins dmin = 1 and another
     # with range 63*15 pins d = 1; skip that and build the parts directly
-    parts = {"qs": (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8),
+    parts = {"qs": quant.pack_nibbles(q),
              "d": np.ones((n, 2), np.float16), "dmin": np.ones((n, 2), np.float16),
              "sub": quant.pack_sub(np.ones((n, 2, 8), np.uint8), np.full((n, 2, 8), 8, np.uint8))}
     x = g.integers(-2, 3, (1, k))
