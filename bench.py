@@ -2,17 +2,24 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step = one decode pass of the RWKV-7 1.5B projection stack (24 layers x
-{fused R/K/V, O, cmix key, cmix value}, symmetric int4 group 64, fp16
-activations with the massive channel 1202) at each batch M in {1, 8, 32},
-followed by one prefill pass of the 7.2B projection set (R, K, V, O, cmix key,
-cmix value; per-token fp8 activations x per-channel fp8 weights) at M = 256.
-Every pass is a captured HIP graph; inputs are resident in HBM before timing.
+One step = the width-2048 (RWKV-7 1.5B) layer of symmetric int4 group-64
+projections (fused R/K/V, O, cmix key, cmix value), fp16 activations with
+channel 1202 scaled x50, decoded at each batch M in {1, 8, 32}, followed by
+the width-4096 (7.2B) prefill set (per-token fp8 activation quantization, then
+R, K, V, O, cmix key and cmix value as fp8 e4m3 per-channel GEMMs) at M = 256.
+Every pass is a captured HIP graph over rotated copies of the weights (more
+than 1 GiB in each rotation, so the 256 MB last-level cache cannot hold them);
+inputs are resident in HBM before timing.
 
-The JSON line's value is the int4 weight stream: packed weight bytes of the
-decode passes / their wall time (GB/s, % of 8 TB/s).  The fp8 prefill GEMM
-rate is reported beside it.  Synthetic weights: N(0, 1/K) drawn on the GPU
-from a seeded generator, quantized with rq_quantize_rtn.
+value = packed weight bytes streamed by the decode passes / their time (GB/s).
+The JSON line also carries the fp8 prefill rate, the roofline of the dominant
+kernel (the kernel class with the largest share of a step's time, its
+average launch duration measured with HIP events around back-to-back
+launches on the launching stream), and the CPU oracle on a bounded sample.
+
+Synthetic weights: N(0, 1/K) from a seeded generator on the GPU, quantized
+with rq_quantize_rtn.  --kernel-only runs just the dominant kernel's launch
+loop and a calibration copy (for hardware-counter runs).
 """
 
 import argparse
@@ -33,78 +40,248 @@ from gemm_rwkv_amd import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "weight-stream GB/s (% HBM peak) W4g64 GEMV M=1..32; TFLOPS fp8 GEMM M=256"
+ROTATE_BYTES = 1 << 30
+C1, MS = 2048, (1, 8, 32)   # decode layer width, batches
+C3, M3 = 4096, 256          # prefill width, batch
+CALIB_BYTES = 256 << 20     # calibration copy for the traffic counters
 
 
 def f16_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16).view(np.int16)).to(dev)
 
 
-class Layer:
-    """The six quantized projections of one RWKV-7 layer (W[N][K])."""
-
-    def __init__(self, c, fmt, group, gen, dev):
-        self.w = {}
-        for mat, n, k in synth.layer_shapes(c):
-            wf = torch.randn(n, k, generator=gen, device=dev, dtype=torch.float32) * (1.0 / k ** 0.5)
-            self.w[mat] = rq.quantize(wf, fmt, group)
-            del wf
-
-    def weight_bytes(self):
-        return sum(q.nbytes() for q in self.w.values())
-
-
-def decode_pass(layers, xc, x4c, y, m, c):
-    """Launch one layer stack: fused R/K/V, O, cmix key, cmix value."""
-    ldx = c
-    for L in layers:
-        w = L.w
-        rq.rq_fused_rkv(xc, xc, xc, m, ldx, w[synth.MAT_R], w[synth.MAT_K], w[synth.MAT_V],
-                        y["r"], y["k"], y["v"], c)
-        rq.rq_gemm_small_m(xc, m, ldx, w[synth.MAT_O], y["o"], c)
-        rq.rq_gemm_small_m(xc, m, ldx, w[synth.MAT_KEY], y["key"], 4 * c)
-        rq.rq_gemm_small_m(x4c, m, 4 * c, w[synth.MAT_VALUE], y["val"], c)
+_CAPTURE_STREAM = None
 
 
 def capture(fn):
-    fn()  # eager run first: loads code objects outside the capture
+    """Graph of fn's launches.  The eager run goes first on the capture stream
+    itself: it loads the code objects and gives that stream its K-split
+    workspace (the library allocates nothing while a stream is capturing)."""
+    global _CAPTURE_STREAM
+    if _CAPTURE_STREAM is None:
+        _CAPTURE_STREAM = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(_CAPTURE_STREAM):
+        fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=_CAPTURE_STREAM):
         fn()
     torch.cuda.synchronize()
     return g
 
 
-def timed(graphs, steps, warmup):
-    """Replay each graph per step; return per-graph mean ms (events) and wall ms/step."""
+def time_graph(g, reps, warmup=2):
+    """Mean ms per replay, HIP events on the current stream (where the graph runs)."""
     for _ in range(warmup):
-        for g in graphs:
-            g.replay()
+        g.replay()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for s in range(steps):
-        ev[s][0].record()
-        for i, g in enumerate(graphs):
-            g.replay()
-            ev[s][i + 1].record()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = [np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]) for i in range(len(graphs))]
-    return per, wall
+    return e0.elapsed_time(e1) / reps
+
+
+class Decode:
+    """Rotated copies of the width-C int4 g64 layer and the decode launches."""
+
+    def __init__(self, c, gen, dev):
+        self.c = c
+        shapes = synth.layer_shapes(c)
+        per_set = sum(rq.rq_qweight_bytes(rq.RQ_W4_SYM, 64, n, k)[0] + rq.rq_qweight_bytes(rq.RQ_W4_SYM, 64, n, k)[1]
+                      for _, n, k in shapes)
+        self.copies = -(-ROTATE_BYTES // per_set)
+        self.sets = []
+        for _ in range(self.copies):
+            s = {}
+            for mat, n, k in shapes:
+                wf = torch.randn(n, k, generator=gen, device=dev, dtype=torch.float32) * (1.0 / k ** 0.5)
+                s[mat] = rq.quantize(wf, rq.RQ_W4_SYM, 64)
+                del wf
+            self.sets.append(s)
+        self.set_bytes = per_set
+        self.x = {m: f16_dev(synth.act_channel_1202(m, c), dev) for m in MS}
+        self.x4 = {m: f16_dev(synth.act_normal(m, 4 * c, 1), dev) for m in MS}
+        self.y = {m: {nm: torch.empty(m * (4 * c if nm == "key" else c), dtype=torch.int16, device=dev)
+                      for nm in ("r", "k", "v", "o", "key", "val")} for m in MS}
+
+    def rkv(self, s, m):
+        y = self.y[m]
+        rq.rq_fused_rkv(self.x[m], self.x[m], self.x[m], m, self.c, s[synth.MAT_R], s[synth.MAT_K],
+                        s[synth.MAT_V], y["r"], y["k"], y["v"], self.c)
+
+    def o(self, s, m):
+        rq.rq_gemm_small_m(self.x[m], m, self.c, s[synth.MAT_O], self.y[m]["o"], self.c)
+
+    def key(self, s, m):
+        rq.rq_gemm_small_m(self.x[m], m, self.c, s[synth.MAT_KEY], self.y[m]["key"], 4 * self.c)
+
+    def value(self, s, m):
+        rq.rq_gemm_small_m(self.x4[m], m, 4 * self.c, s[synth.MAT_VALUE], self.y[m]["val"], self.c)
+
+    def passes(self, m):
+        for s in self.sets:
+            self.rkv(s, m)
+            self.o(s, m)
+            self.key(s, m)
+            self.value(s, m)
+
+    def classes(self, m):
+        """(name, launch-one(s), weight bytes per launch, launches per step)."""
+        c = self.c
+        b = lambda n, k: sum(rq.rq_qweight_bytes(rq.RQ_W4_SYM, 64, n, k)[:2])  # noqa: E731
+        return [
+            ("gemv w4g64 fused R/K/V 3x%dx%d M=%d" % (c, c, m), lambda s: self.rkv(s, m), 3 * b(c, c), self.copies),
+            ("gemv w4g64 O %dx%d M=%d" % (c, c, m), lambda s: self.o(s, m), b(c, c), self.copies),
+            ("gemv w4g64 cmix key %dx%d M=%d" % (4 * c, c, m), lambda s: self.key(s, m), b(4 * c, c), self.copies),
+            ("gemv w4g64 cmix value %dx%d M=%d" % (c, 4 * c, m), lambda s: self.value(s, m), b(c, 4 * c),
+             self.copies),
+        ]
+
+
+class Prefill:
+    """Rotated copies of the width-C fp8 per-channel set and the M=256 prefill launches."""
+
+    def __init__(self, c, m, gen, dev):
+        self.c, self.m = c, m
+        shapes = synth.layer_shapes(c)
+        per_set = sum(n * k + 4 * n for _, n, k in shapes)
+        self.copies = -(-ROTATE_BYTES // per_set)
+        self.sets = []
+        for _ in range(self.copies):
+            s = {}
+            for mat, n, k in shapes:
+                wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
+                s[mat] = rq.quantize(wf, rq.RQ_FP8_E4M3_CH)
+                del wf
+            self.sets.append(s)
+        self.set_bytes = per_set
+        self.flops = sum(2.0 * m * n * k for _, n, k in shapes)
+        self.xa = f16_dev(synth.act_normal(m, c, 3), dev)
+        self.xa4 = f16_dev(synth.act_normal(m, 4 * c, 3, salt=1), dev)
+        self.xq = torch.empty(m * c, dtype=torch.uint8, device=dev)
+        self.xq4 = torch.empty(m * 4 * c, dtype=torch.uint8, device=dev)
+        self.sx = torch.empty(m, dtype=torch.float32, device=dev)
+        self.sx4 = torch.empty(m, dtype=torch.float32, device=dev)
+        self.y = torch.empty(m * 4 * c, dtype=torch.int16, device=dev)
+
+    def aq(self, _s=None):
+        rq.rq_quantize_act(self.xa, self.m, self.c, self.c, rq.RQ_FP8_E4M3_CH, self.xq, self.sx)
+
+    def aq4(self, _s=None):
+        rq.rq_quantize_act(self.xa4, self.m, 4 * self.c, 4 * self.c, rq.RQ_FP8_E4M3_CH, self.xq4, self.sx4)
+
+    def gemm(self, s, mat):
+        w = s[mat]
+        if mat == synth.MAT_VALUE:
+            rq.rq_gemm_fp8(self.xq4, self.sx4, self.m, w, self.y, w.n)
+        else:
+            rq.rq_gemm_fp8(self.xq, self.sx, self.m, w, self.y, w.n)
+
+    def passes(self):
+        for s in self.sets:
+            self.aq()
+            for mat in (synth.MAT_R, synth.MAT_K, synth.MAT_V, synth.MAT_O, synth.MAT_KEY):
+                self.gemm(s, mat)
+            self.aq4()
+            self.gemm(s, synth.MAT_VALUE)
+
+    def classes(self):
+        c, m = self.c, self.m
+        fl = lambda n, k: 2.0 * m * n * k  # noqa: E731
+        return [
+            ("fp8 act quant %dx%d" % (m, c), self.aq, 0, self.copies, 0.0),
+            ("fp8 act quant %dx%d" % (m, 4 * c), self.aq4, 0, self.copies, 0.0),
+            ("gemm fp8 %dx%dx%d (R,K,V,O)" % (m, c, c), lambda s: self.gemm(s, synth.MAT_R),
+             c * c + 4 * c, 4 * self.copies, fl(c, c)),
+            ("gemm fp8 %dx%dx%d (cmix key)" % (m, 4 * c, c), lambda s: self.gemm(s, synth.MAT_KEY),
+             4 * c * c + 16 * c, self.copies, fl(4 * c, c)),
+            ("gemm fp8 %dx%dx%d (cmix value)" % (m, c, 4 * c), lambda s: self.gemm(s, synth.MAT_VALUE),
+             4 * c * c + 4 * c, self.copies, fl(c, 4 * c)),
+        ]
+
+
+def class_graph(launch, sets):
+    """One graph: the kernel class launched once per rotated weight copy."""
+    return capture(lambda: [launch(s) for s in sets])
+
+
+def measure_classes(dec, pre, reps):
+    """Average launch duration (ms) of every kernel class, back to back in a graph."""
+    rows = []
+    for m in MS:
+        for name, fn, wbytes, per_step in dec.classes(m):
+            g = class_graph(fn, dec.sets)
+            ms = time_graph(g, reps) / len(dec.sets)
+            rows.append({"name": name, "ms": ms, "weight_bytes": wbytes, "per_step": per_step, "flops": 0.0,
+                         "m": m, "graph": g, "launches": len(dec.sets)})
+    for name, fn, wbytes, per_step, flops in pre.classes():
+        g = class_graph(fn, pre.sets)
+        ms = time_graph(g, reps) / len(pre.sets)
+        rows.append({"name": name, "ms": ms, "weight_bytes": wbytes, "per_step": per_step, "flops": flops,
+                     "m": pre.m, "graph": g, "launches": len(pre.sets)})
+    return rows
+
+
+FP8_RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per HBM byte
+
+
+def roofline(row, traffic=None):
+    """Roofline of one kernel class from its average launch duration: the
+    algorithmic bytes (weights, scales, x, y) per launch against 8 TB/s, or,
+    for a product above the fp8 ridge, its flops against the fp8 MFMA peak."""
+    sec = row["ms"] * 1e-3
+    out = {"kernel": row["name"], "launch_us": round(row["ms"] * 1e3, 3),
+           "alg_bytes_per_launch": int(row["alg_bytes"])}
+    if row["flops"] > 0:
+        out["tflops"] = round(row["flops"] / sec / 1e12, 2)
+    if row["flops"] > 0 and row["flops"] / row["alg_bytes"] >= FP8_RIDGE:
+        a = row["flops"] / sec / 1e12
+        out.update({"bound": "mfma", "achieved": round(a, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(a / FP8_PEAK_TFLOPS, 4)})
+    else:
+        a = row["alg_bytes"] / sec / 1e9
+        out.update({"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(a / HBM_PEAK_GBS, 4)})
+    out["traffic"] = traffic
+    return out
+
+
+def alg_bytes(row, c1, c3, m3):
+    """Algorithmic HBM bytes of one launch: weights (+ scales), x and y."""
+    name, m = row["name"], row["m"]
+    if "act quant" in name:
+        k = 4 * c3 if "x%d" % (4 * c3) in name else c3
+        return m3 * k * 2 + m3 * k + 4 * m3
+    if row["flops"] > 0:
+        n_k = row["flops"] / (2.0 * m3)
+        k = 4 * c3 if "value" in name else c3
+        n = n_k / k
+        return row["weight_bytes"] + m3 * k + 4 * m3 + m3 * n * 2
+    if "fused" in name:
+        return row["weight_bytes"] + 3 * m * c1 * 2 + 3 * m * c1 * 2
+    if "cmix key" in name:
+        return row["weight_bytes"] + m * c1 * 2 + m * 4 * c1 * 2
+    if "cmix value" in name:
+        return row["weight_bytes"] + m * 4 * c1 * 2 + m * c1 * 2
+    return row["weight_bytes"] + 2 * m * c1 * 2
 
 
 def cpu_baseline(c, budget_s=20.0):
-    """The oracle (dequantize + fp64 product) on host cores over a bounded
-    sample of the decode pass: whole layers of the width-c stack at M = 1, 8, 32."""
+    """The oracle (RTN quantize, dequantize, fp64 product) on host cores over a
+    bounded sample of the decode step: whole width-c layers at M = 1, 8, 32."""
     from oracle import quant, ref
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = os.cpu_count()
-    xs = {m: synth.act_channel_1202(m, c) for m in (1, 8, 32)}
-    x4 = {m: synth.act_normal(m, 4 * c, 1) for m in (1, 8, 32)}
+    xs = {m: synth.act_channel_1202(m, c) for m in MS}
+    x4 = {m: synth.act_normal(m, 4 * c, 1) for m in MS}
     t0 = time.perf_counter()
     nbytes = 0
     layers = 0
@@ -112,99 +289,114 @@ def cpu_baseline(c, budget_s=20.0):
         for mat, n, k in synth.layer_shapes(c):
             w = synth.weight(1, layers, mat, n, k)
             parts = quant.quantize_sym(w, 4, 64)
-            nbytes += 3 * (parts["codes"].nbytes + parts["scales"].nbytes)
-            for m in (1, 8, 32):
+            nbytes += len(MS) * (parts["codes"].nbytes + parts["scales"].nbytes)
+            for m in MS:
                 x = xs[m] if k == c else x4[m]
                 ref.weight_only_ref(x, quant.W4_SYM, parts, 64)
         layers += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d layer(s) of the width-%d stack (6 matrices, w4g64), quantize + dequantize "
-                      "+ fp64 product at M=1,8,32, %.1f s" % (layers, c, dt)}
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d layer(s) of the width-%d int4 g64 set (6 matrices) through the oracle's RTN "
+                      "quantizer, dequantization and fp64 product at M=1,8,32: %.1f s; value = packed "
+                      "weight bytes of the decode passes / time" % (layers, c, dt)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--phases", action="store_true", help="print per-phase timings to stderr")
+    ap.add_argument("--phases", action="store_true", help="per-class timings to stderr")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="replay only the dominant kernel class (and a calibration copy), print nothing")
+    ap.add_argument("--class-reps", type=int, default=20)
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file of counter-derived HBM bytes per launch of the dominant kernel")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the library and this benchmark have no multi-GPU "
-              "path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
 
-    # ---- 1.5B decode stack, w4g64
-    C, NL = 2048, synth.RWKV7_SIZES["1.5B"][0]
-    layers = [Layer(C, rq.RQ_W4_SYM, 64, gen, dev) for _ in range(NL)]
-    wbytes = sum(L.weight_bytes() for L in layers)
-    Ms = (1, 8, 32)
-    xc = {m: f16_dev(synth.act_channel_1202(m, C), dev) for m in Ms}
-    x4c = {m: f16_dev(synth.act_normal(m, 4 * C, 1), dev) for m in Ms}
-    ys = {m: {name: torch.empty(m * (4 * C if name == "key" else C), dtype=torch.int16, device=dev)
-              for name in ("r", "k", "v", "o", "key", "val")} for m in Ms}
-    graphs = [capture(lambda m=m: decode_pass(layers, xc[m], x4c[m], ys[m], m, C)) for m in Ms]
+    dec = Decode(C1, gen, dev)
+    pre = Prefill(C3, M3, gen, dev)
 
-    # ---- 7.2B prefill set, fp8, M = 256 (six copies: > 1 GiB of weights)
-    C3, M3 = 4096, 256
-    sets = []
-    for _ in range(6):
-        s = {}
-        for mat, n, k in synth.layer_shapes(C3):
-            wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
-            s[mat] = rq.quantize(wf, rq.RQ_FP8_E4M3_CH)
-            del wf
-        sets.append(s)
-    xa = f16_dev(synth.act_normal(M3, C3, 3), dev)
-    xa4 = f16_dev(synth.act_normal(M3, 4 * C3, 3, salt=1), dev)
-    xq = torch.empty(M3 * C3, dtype=torch.uint8, device=dev)
-    xq4 = torch.empty(M3 * 4 * C3, dtype=torch.uint8, device=dev)
-    sx = torch.empty(M3, dtype=torch.float32, device=dev)
-    sx4 = torch.empty(M3, dtype=torch.float32, device=dev)
-    yp = torch.empty(M3 * 4 * C3, dtype=torch.int16, device=dev)
+    if args.kernel_only:
+        rows = measure_classes(dec, pre, 1)
+        dom = max(rows, key=lambda r: r["ms"] * r["per_step"])
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        for _ in range(args.steps):
+            dom["graph"].replay()
+        torch.cuda.synchronize()
+        print("dominant: %s (%d launches per replay, %d replays); calibration copy %d bytes"
+              % (dom["name"], dom["launches"], args.steps, CALIB_BYTES), file=sys.stderr)
+        return
 
-    def prefill():
-        for s in sets:
-            rq.rq_quantize_act(xa, M3, C3, C3, rq.RQ_FP8_E4M3_CH, xq, sx)
-            for mat in (synth.MAT_R, synth.MAT_K, synth.MAT_V, synth.MAT_O, synth.MAT_KEY):
-                rq.rq_gemm_fp8(xq, sx, M3, s[mat], yp, s[mat].n)
-            rq.rq_quantize_act(xa4, M3, 4 * C3, 4 * C3, rq.RQ_FP8_E4M3_CH, xq4, sx4)
-            rq.rq_gemm_fp8(xq4, sx4, M3, s[synth.MAT_VALUE], yp, C3)
+    graphs = [capture(lambda m=m: dec.passes(m)) for m in MS] + [capture(pre.passes)]
+    for _ in range(args.warmup):
+        for g in graphs:
+            g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+    per = np.zeros(len(graphs))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev[0].record()
+        for i, g in enumerate(graphs):
+            g.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per += [ev[i].elapsed_time(ev[i + 1]) for i in range(len(graphs))]
+    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    per /= args.steps
+    dec_ms = float(per[:len(MS)].sum())
+    value = len(MS) * dec.copies * dec.set_bytes / (dec_ms * 1e-3) / 1e9
+    fp8_tflops = pre.copies * pre.flops / (per[-1] * 1e-3) / 1e12
 
-    graphs.append(capture(prefill))
-    flops = 6 * sum(2.0 * M3 * n * k for _, n, k in synth.layer_shapes(C3))
-
-    per, wall = timed(graphs, args.steps, args.warmup)
-    dec_ms = sum(per[:3])
-    value = 3 * wbytes / (dec_ms * 1e-3) / 1e9
-    fp8_tflops = flops / (per[3] * 1e-3) / 1e12
+    rows = measure_classes(dec, pre, args.class_reps)
+    for r in rows:
+        r["alg_bytes"] = alg_bytes(r, C1, C3, M3)
+    dom = max(rows, key=lambda r: r["ms"] * r["per_step"])
+    traffic = None
+    if args.traffic:
+        with open(args.traffic) as f:
+            t = json.load(f)
+        if t.get("kernel") == dom["name"]:
+            traffic = t["bytes_per_launch"]
     if args.phases:
-        for name, t, b in zip(("M=1", "M=8", "M=32"), per[:3], [wbytes] * 3):
-            print("decode %s: %.3f ms, %.0f GB/s" % (name, t, b / t / 1e6), file=sys.stderr)
-        print("prefill fp8 M=256: %.3f ms, %.1f TFLOP/s" % (per[3], fp8_tflops), file=sys.stderr)
+        for name, t in zip(["decode M=%d" % m for m in MS] + ["prefill fp8 M=%d" % M3], per):
+            print("%-22s %8.3f ms" % (name, t), file=sys.stderr)
+        for r in rows:
+            rl = roofline(r)
+            print("%-46s %8.2f us  x%-4d %7.1f %s (%.1f%%)" % (r["name"], r["ms"] * 1e3, r["per_step"],
+                  rl["achieved"], rl["unit"], 100 * rl["frac"]), file=sys.stderr)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": "rwkv7-1.5B decode: 24 layers x (fused RKV, O, cmix key, cmix value), "
-                               "int4 sym g64, M in {1,8,32}; plus rwkv7-7.2B fp8 prefill set at M=256",
-                   "width": C, "layers": NL, "M": list(Ms), "weight_bytes_per_pass": wbytes,
-                   "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
+        "data": "synthetic: weights N(0,1/K) quantized on the GPU; x N(0,1) fp16, channel 1202 x50",
+        "config": {"workload": "rwkv7 1.5B-width (C=2048) int4 sym g64 layer set (fused R/K/V, O, cmix "
+                               "key, cmix value) decoded at M=1,8,32, then the 7.2B-width (C=4096) fp8 "
+                               "per-channel prefill set at M=256",
+                   "decode_copies": dec.copies, "decode_weight_bytes_per_set": dec.set_bytes,
+                   "prefill_copies": pre.copies, "prefill_weight_bytes_per_set": pre.set_bytes,
+                   "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+                   "decode_ms": {str(m): round(float(t), 4) for m, t in zip(MS, per)}},
         "fp8_gemm_m256": {"tflops": round(fp8_tflops, 1), "frac_of_peak": round(fp8_tflops / FP8_PEAK_TFLOPS, 4),
-                          "ms": round(per[3], 4)},
+                          "pass_ms": round(float(per[-1]), 4)},
+        "roofline": roofline(dom, traffic),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(C)
+        out["cpu_baseline"] = cpu_baseline(C1)
     print(json.dumps(out))
 
 

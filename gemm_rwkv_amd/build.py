@@ -29,9 +29,15 @@ FLAGS = [
 ]
 
 
+# per-source options: the dense GEMM keeps its accumulators in VGPRs (with
+# them in AGPRs the allocator shuttles them between the two files every
+# k step of the double-buffered loop)
+EXTRA = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))

@@ -3,6 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "rq.h"
@@ -44,6 +47,38 @@ void fill_matrix(rq::GemvMatrix& g, const rq_qweight* w, const uint16_t* x, uint
   g.tiles = (int)((w->n + 15) / 16);
 }
 
+// Workspace of the K-split weight-streaming products (fp32 partial tiles),
+// one per (device, stream) so that products on different streams never share
+// it.  It is allocated on the first product on that stream.  During graph
+// capture nothing is allocated: a stream without a workspace runs unsplit
+// launch shapes (same results).
+struct Workspace {
+  int dev;
+  hipStream_t stream;
+  void* mem;
+};
+std::mutex g_ws_mu;
+std::vector<Workspace> g_ws;
+
+void gemv_workspace(hipStream_t st, rq::GemvBatch& b) {
+  b.ws = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  for (const Workspace& w : g_ws) {
+    if (w.dev == dev && w.stream == st) {
+      b.ws = (float*)w.mem;
+      return;
+    }
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  void* mem = nullptr;
+  if (hipMalloc(&mem, rq::kGemvWsPartialBytes) != hipSuccess) return;
+  g_ws.push_back(Workspace{dev, st, mem});
+  b.ws = (float*)mem;
+}
+
 // Shared path of the gemv entry points and rq_gemm_small_m.
 int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
             void* stream, int want_format, int want_group) {
@@ -69,6 +104,7 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   b.m = (int)m;
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
+  gemv_workspace(S(stream), b);
   return hip_status(rq::launch_gemv(b, gf, w->group, S(stream)));
 }
 
@@ -237,6 +273,7 @@ int rq_fused_rkv(const uint16_t* xr, const uint16_t* xk, const uint16_t* xv, int
   b.m = (int)m;
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
+  gemv_workspace(S(stream), b);
   return hip_status(rq::launch_gemv(b, gf, wr->group, S(stream)));
 }
 

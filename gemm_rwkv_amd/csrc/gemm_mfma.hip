@@ -6,9 +6,9 @@
 // Architecture: FP8 + INT8 GEMM kernels with shape-aware tile configurations.)
 //
 // gfx950 mapping: v_mfma_f32_16x16x128_f8f6f4 (both operands OCP e4m3) and
-// v_mfma_i32_16x16x64_i8.  A lane holds 32 (fp8) or 16 (int8) consecutive k
-// of one row of each operand; A and B use the same lane -> k assignment, so
-// every k meets its partner whatever order the instruction sums in.
+// v_mfma_i32_16x16x64_i8.  A lane holds 32 (fp8) or 16 (int8) k of one row of
+// each operand; x and w use the same lane -> k assignment, so every k meets
+// its partner whatever order the instruction sums in.
 #include <type_traits>
 
 #include "device_common.h"
@@ -16,126 +16,228 @@
 
 namespace rq {
 
-// BM x BN output tile per workgroup of 4 waves (2 x 2), each wave
-// (BM/2) x (BN/2) as 16 x 16 MFMA blocks.
-template <bool FP8, int BM, int BN>
-__global__ void __launch_bounds__(256) gemm_w8a8_kernel(const uint8_t* __restrict__ xq,
-                                                        const float* __restrict__ sx, int M,
-                                                        const uint8_t* __restrict__ wq,
-                                                        const float* __restrict__ sw, int N, int K,
-                                                        uint16_t* __restrict__ y, int ldy,
-                                                        int32_t* __restrict__ acc_out) {
-  constexpr int WM = BM / 2 / 16;  // 16-row blocks per wave along m
-  constexpr int WN = BN / 2 / 16;
-  const int wave = threadIdx.x >> 6;
+// One workgroup computes a (16 TM) x (16 TN) output tile.  Its KW waves
+// split K (wave w takes the 128-wide k blocks w, w + KW, ...) and each covers
+// the whole tile, so no operand byte is read twice within a workgroup; the
+// KW partial tiles are summed through LDS in wave order (deterministic),
+// scaled and stored.
+//
+// Operands reach the MFMA layout through LDS.  A lane's operand is 32 bytes
+// of one row (row = lane % 16), so loading straight into registers makes each
+// instruction touch 16 rows x 64 B, half of every 128-byte line, which
+// halves what L2 delivers per instruction.  Instead each wave copies its k
+// block with LDS DMA reads of 8 rows x 128 B (whole lines) into a private
+// 2-stage ring and reads the fragments back with ds_read_b128.  The 16-byte
+// segments of row r are stored at slot (segment ^ ((r / 2) % 8)), so the 16
+// rows a fragment read touches fall in distinct banks.  While block j is
+// multiplied, block j + 1 is in flight.
+//
+// The DMA and its waits are issued as inline asm: the compiler cannot tell
+// which LDS bytes an LDS DMA writes, and would otherwise wait for every DMA
+// in flight before any LDS read.  The DMA writes no register, and every read
+// of its LDS bytes comes after an explicit wait with a memory clobber.
+//
+// Rows past m (n) read row m - 1 (n - 1): they only reach outputs that are
+// never stored.  fp8: a lane's 32 bytes are one operand of v_mfma 16x16x128
+// f8f6f4; int8: each 16-byte half feeds one v_mfma_i32_16x16x64_i8.
+template <bool FP8, int TM, int TN, int KW>
+__global__ void __launch_bounds__(64 * KW) gemm_w8a8_kernel(const uint8_t* __restrict__ xq,
+                                                            const float* __restrict__ sx, int M,
+                                                            const uint8_t* __restrict__ wq,
+                                                            const float* __restrict__ sw, int N, int K,
+                                                            uint16_t* __restrict__ y, int ldy,
+                                                            int32_t* __restrict__ acc_out) {
+  constexpr int BM = 16 * TM, BN = 16 * TN;
+  constexpr int SA = BM * 128, STAGE = (BM + BN) * 128;  // bytes of one staged k block
+  constexpr int NB = 2;                                   // stages per wave
+  typedef typename std::conditional<FP8, float4v, int4v>::type AccT;
+  extern __shared__ uint4 lds4[];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int q = lane >> 4;
-  const int m0 = blockIdx.y * BM + (wave >> 1) * (BM / 2);
-  const int n0 = blockIdx.x * BN + (wave & 1) * (BN / 2);
+  const int m0 = blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int nkb = K >> 7;
 
-  const uint8_t* arow[WM];
-  bool av[WM];
+  // LDS DMA sources: instruction i covers tile rows 8i .. 8i + 7, lane ->
+  // row 8i + lane / 8, LDS slot lane % 8 holding segment slot ^ ((row / 2) % 8)
+  const int drow = lane >> 3, dslot = lane & 7;
+  const uint8_t* asrc[TM * 2];
+  const uint8_t* bsrc[TN * 2];
 #pragma unroll
-  for (int a = 0; a < WM; ++a) {
-    const int m = m0 + a * 16 + r16;
-    av[a] = m < M;
-    arow[a] = xq + (size_t)(av[a] ? m : 0) * K;
+  for (int i = 0; i < TM * 2; ++i) {
+    const int r = 8 * i + drow;
+    asrc[i] = xq + (size_t)min(m0 + r, M - 1) * K + ((dslot ^ ((r >> 1) & 7)) << 4);
   }
-  const uint8_t* brow[WN];
-  bool bv[WN];
 #pragma unroll
-  for (int b = 0; b < WN; ++b) {
-    const int n = n0 + b * 16 + r16;
-    bv[b] = n < N;
-    brow[b] = wq + (size_t)(bv[b] ? n : 0) * K;
+  for (int i = 0; i < TN * 2; ++i) {
+    const int r = 8 * i + drow;
+    bsrc[i] = wq + (size_t)min(n0 + r, N - 1) * K + ((dslot ^ ((r >> 1) & 7)) << 4);
   }
-
-  typedef typename std::conditional<FP8, float4v, int4v>::type AccT;
-  AccT acc[WM][WN];
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4 + wave * NB * STAGE;
+  auto dma = [&](int st, int kb) {
+    const uint32_t base = ring + st * STAGE;
 #pragma unroll
-  for (int a = 0; a < WM; ++a)
-#pragma unroll
-    for (int b = 0; b < WN; ++b) acc[a][b] = AccT{0, 0, 0, 0};
-
-  for (int k0 = 0; k0 < K; k0 += 128) {
-    if (FP8) {
-      int8v fa[WM], fb[WN];
-#pragma unroll
-      for (int a = 0; a < WM; ++a) {
-        const uint4* p = (const uint4*)(arow[a] + k0 + 32 * q);
-        uint4 lo = av[a] ? p[0] : make_uint4(0, 0, 0, 0);
-        uint4 hi = av[a] ? p[1] : make_uint4(0, 0, 0, 0);
-        fa[a] = int8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int b = 0; b < WN; ++b) {
-        const uint4* p = (const uint4*)(brow[b] + k0 + 32 * q);
-        uint4 lo = bv[b] ? p[0] : make_uint4(0, 0, 0, 0);
-        uint4 hi = bv[b] ? p[1] : make_uint4(0, 0, 0, 0);
-        fb[b] = int8v{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int a = 0; a < WM; ++a)
-#pragma unroll
-        for (int b = 0; b < WN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0, 0,
-                                                                       0, 0, 0);
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int4v fa[WM], fb[WN];
-#pragma unroll
-        for (int a = 0; a < WM; ++a) {
-          uint4 v = av[a] ? *(const uint4*)(arow[a] + k0 + 64 * h + 16 * q) : make_uint4(0, 0, 0, 0);
-          fa[a] = int4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-        }
-#pragma unroll
-        for (int b = 0; b < WN; ++b) {
-          uint4 v = bv[b] ? *(const uint4*)(brow[b] + k0 + 64 * h + 16 * q) : make_uint4(0, 0, 0, 0);
-          fb[b] = int4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-        }
-#pragma unroll
-        for (int a = 0; a < WM; ++a)
-#pragma unroll
-          for (int b = 0; b < WN; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
-      }
+    for (int i = 0; i < TM * 2; ++i) {
+      const uint8_t* g = asrc[i] + (size_t)kb * 128;
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(g), "s"(base + i * 1024) : "memory", "m0");
     }
+#pragma unroll
+    for (int i = 0; i < TN * 2; ++i) {
+      const uint8_t* g = bsrc[i] + (size_t)kb * 128;
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(g), "s"(base + SA + i * 1024) : "memory", "m0");
+    }
+  };
+
+  // fragment reads: row r16 of a 16-row block, segments 2q and 2q + 1
+  const int swz = (r16 >> 1) & 7;
+  const int o0 = r16 * 128 + (((2 * q) ^ swz) << 4);
+  const int o1 = r16 * 128 + (((2 * q + 1) ^ swz) << 4);
+  const uint8_t* my = (const uint8_t*)lds4 + wave * NB * STAGE;
+
+  AccT acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = AccT{0, 0, 0, 0};
+
+  auto compute = [&](int st) {
+    const uint8_t* base = my + st * STAGE;
+    uint4 fa[TM][2], fb[TN][2];
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      fa[a][0] = *(const uint4*)(base + a * 2048 + o0);
+      fa[a][1] = *(const uint4*)(base + a * 2048 + o1);
+    }
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      fb[b][0] = *(const uint4*)(base + SA + b * 2048 + o0);
+      fb[b][1] = *(const uint4*)(base + SA + b * 2048 + o1);
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const uint4 al = fa[a][0], ah = fa[a][1];
+        const uint4 bl = fb[b][0], bh = fb[b][1];
+        if constexpr (FP8) {
+          const int8v av = {(int)al.x, (int)al.y, (int)al.z, (int)al.w, (int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
+          const int8v bv = {(int)bl.x, (int)bl.y, (int)bl.z, (int)bl.w, (int)bh.x, (int)bh.y, (int)bh.z, (int)bh.w};
+          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[a][b], 0, 0, 0, 0, 0, 0);
+        } else {
+          const int4v a0 = {(int)al.x, (int)al.y, (int)al.z, (int)al.w};
+          const int4v b0 = {(int)bl.x, (int)bl.y, (int)bl.z, (int)bl.w};
+          const int4v a1 = {(int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
+          const int4v b1 = {(int)bh.x, (int)bh.y, (int)bh.z, (int)bh.w};
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[a][b], 0, 0, 0);
+        }
+      }
+  };
+
+  // this wave's blocks j = 0 .. nmine - 1 are k blocks wave + j KW; block j
+  // lives in stage j % 2 and block j + 1 is in flight while j is multiplied
+  constexpr int PER = (TM + TN) * 2;  // DMA instructions per block
+  const int nmine = nkb > wave ? (nkb - wave + KW - 1) / KW : 0;
+  if (nmine > 0) dma(0, wave);
+  for (int j = 0; j < nmine; ++j) {
+    if (j + 1 < nmine) {
+      dma((j + 1) & 1, wave + (j + 1) * KW);
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");  // block j has landed
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    compute(j & 1);
   }
 
-  // epilogue: lane holds D[m = 4q + r][n = r16] of each 16 x 16 block
+  // epilogue, one block row at a time, in the (now free) staging area: lane
+  // holds D[m = 4q + r][n = r16] of each 16 x 16 block
+  AccT (*red)[TN][64] = (AccT (*)[TN][64])lds4;
 #pragma unroll
-  for (int a = 0; a < WM; ++a)
+  for (int a = 0; a < TM; ++a) {
+    __syncthreads();  // staging reads, or the previous row's sums, are done
 #pragma unroll
-    for (int b = 0; b < WN; ++b) {
+    for (int b = 0; b < TN; ++b) red[wave][b][lane] = acc[a][b];
+    __syncthreads();
+    for (int b = wave; b < TN; b += KW) {
+      AccT v = red[0][b][lane];
+#pragma unroll
+      for (int w = 1; w < KW; ++w) {
+        const AccT u = red[w][b][lane];
+        v[0] += u[0];
+        v[1] += u[1];
+        v[2] += u[2];
+        v[3] += u[3];
+      }
       const int n = n0 + b * 16 + r16;
       if (n >= N) continue;
-      const float swn = sw[n];
+      const float swn = y ? sw[n] : 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + a * 16 + 4 * q + r;
         if (m >= M) continue;
-        const float v = FP8 ? (float)acc[a][b][r] : (float)acc[a][b][r];
-        if (acc_out) acc_out[(size_t)m * N + n] = (int32_t)acc[a][b][r];
-        if (y) y[(size_t)m * ldy + n] = f32_to_f16_bits(v * sx[m] * swn);
+        if (acc_out) acc_out[(size_t)m * N + n] = (int32_t)v[r];
+        if (y) y[(size_t)m * ldy + n] = f32_to_f16_bits((float)v[r] * sx[m] * swn);
       }
     }
+  }
+}
+
+// Tile shape: the largest of 64x64, 32x64, 32x32, 16x32 that still gives at
+// least one workgroup per compute unit (256), else the smallest.
+// blockIdx.x runs over n, so with N / BN a multiple of 8 the workgroups that
+// share a weight tile land on the same XCD (dispatch is round-robin over 8).
+template <bool FP8>
+static hipError_t launch_w8a8_t(const void* xq, const float* sx, int m, const void* wq, const float* sw,
+                                int n, int k, uint16_t* y, int ldy, int32_t* acc_out, hipStream_t st) {
+  struct Shape {
+    int tm, tn;
+  };
+  const Shape shapes[] = {{4, 4}, {2, 4}, {2, 2}, {1, 2}};
+  int pick = 3;
+  for (int i = 0; i < 4; ++i) {
+    const long wg = (long)((m + 16 * shapes[i].tm - 1) / (16 * shapes[i].tm)) *
+                    (long)((n + 16 * shapes[i].tn - 1) / (16 * shapes[i].tn));
+    if (wg >= 256) {
+      pick = i;
+      break;
+    }
+  }
+  const int bm = 16 * shapes[pick].tm, bn = 16 * shapes[pick].tn;
+  const dim3 grid((unsigned)((n + bn - 1) / bn), (unsigned)((m + bm - 1) / bm));
+  const uint8_t* a = (const uint8_t*)xq;
+  const uint8_t* b = (const uint8_t*)wq;
+#define RQ_W8A8(TM, TN)                                                                              \
+  {                                                                                                  \
+    constexpr size_t lds = (size_t)4 * 2 * (16 * (TM) + 16 * (TN)) * 128;                            \
+    static_assert(lds >= (size_t)4 * (TN) * 64 * 16, "reduction fits in the staging area");          \
+    static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w8a8_kernel<FP8, TM, TN, 4>,     \
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,       \
+                                                     (int)lds) == hipSuccess;                         \
+    (void)attr_set;                                                                                  \
+    hipLaunchKernelGGL((gemm_w8a8_kernel<FP8, TM, TN, 4>), grid, dim3(256), lds, st, a, sx, m, b, sw, n, \
+                       k, y, ldy, acc_out);                                                          \
+  }
+  switch (pick) {
+    case 0: RQ_W8A8(4, 4); break;
+    case 1: RQ_W8A8(2, 4); break;
+    case 2: RQ_W8A8(2, 2); break;
+    default: RQ_W8A8(1, 2); break;
+  }
+#undef RQ_W8A8
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_w8a8(const void* xq, const float* sx, int m, const void* wq, const float* sw,
                             int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out,
                             hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
-  constexpr int BM = 64, BN = 64;
-  const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
-  if (fp8)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<true, BM, BN>), grid, dim3(256), 0, st, (const uint8_t*)xq, sx, m,
-                       (const uint8_t*)wq, sw, n, k, y, ldy, acc_out);
-  else
-    hipLaunchKernelGGL((gemm_w8a8_kernel<false, BM, BN>), grid, dim3(256), 0, st, (const uint8_t*)xq, sx,
-                       m, (const uint8_t*)wq, sw, n, k, y, ldy, acc_out);
-  return hipGetLastError();
+  if (fp8) return launch_w8a8_t<true>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, st);
+  return launch_w8a8_t<false>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, st);
 }
 
 }  // namespace rq

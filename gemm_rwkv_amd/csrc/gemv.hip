@@ -361,7 +361,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
 }
 
 // ---------------------------------------------------------------------------
-// streaming kernel: 16-byte code loads per lane through a prefetch ring
+// chunks, lanes and groups of the streaming kernel
 // ---------------------------------------------------------------------------
 // A "chunk" is 16 bytes of codes per lane, 64 bytes per row (4 lanes), i.e.
 // CK = 128 (int4), 64 (int8) or 32 (fp16) values of k.  A chunk holds GPC
@@ -376,12 +376,6 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
 // stored.  Codes and scales come through raw buffer loads (scalar base,
 // 32-bit lane offset; an invalid chunk reads zeros through an out-of-range
 // scalar offset, so the loop body has no branches).
-//
-// Vector loads of one wave complete in issue order.  So activations either
-//   XL: sit in LDS, copied there once per workgroup by an extra staging wave
-//       with global_load_lds (its wait does not hold up the compute waves'
-//       code loads), rows m >= M reading a zero row; or
-//   !XL: travel in each ring slot beside the codes of the same chunk.
 template <int FMT, int G>
 struct F2 {
   static constexpr int CK = (FMT == GF_W4 || FMT == GF_SB) ? 128 : (FMT == GF_W8 ? 64 : 32);
@@ -434,70 +428,86 @@ constexpr int x_const(int g, int p) {
   else return g * F::GK;
 }
 
-template <int FMT, int G, int MT, bool XL>
-struct RingSlot {
-  uint4 c;      // codes
-  uint32_t s;   // scales (1-2 fp16) or SB d | dmin << 16
-  uint32_t s2;  // scales 3-4 (int4 g32, int8 g16)
-  uint32_t sub[FMT == GF_SB ? 3 : 1];
-  uint4 x[XL ? 1 : F2<FMT, G>::NM][XL ? 1 : MT];  // activation fragments (!XL)
+
+constexpr int kXBudget = 80 * 1024;  // bytes of LDS for a workgroup's activation slice
+
+// ---------------------------------------------------------------------------
+// the streaming kernel: a workgroup = RT row tiles x one slice of K
+// ---------------------------------------------------------------------------
+// Every wave owns CPW chunks of one 16-row tile and issues all of their code
+// and scale loads before it computes (with few chunks per wave that keeps the
+// most bytes in flight; vector loads of a wave complete in issue order, so
+// nothing is loaded behind them).  The workgroup's waves then copy its slice
+// of the activations (rows < M) into LDS with global_load_lds, a zero row
+// stands for m >= M, and after one barrier the waves compute from LDS.
+//
+// K is cut into `split` slices of cps chunks.  The waves of a tile reduce
+// through LDS in wave order; with split = 1 they store fp16, otherwise each
+// workgroup stores its fp32 partial tile group in the workspace and a second
+// kernel adds the `split` partials in slice order (deterministic, no atomics
+// or cross-workgroup fences).  Splitting feeds the compute units when there
+// are few row tiles, and keeps the LDS slice of x small when M * K is large;
+// RT tiles per workgroup share one slice.
+struct Split5 {
+  int split;      // K slices
+  int cps;        // chunks per slice
+  int wpt;        // waves per row tile
+  int rt;         // row tiles per workgroup
+  int groups[3];  // tile groups (workgroups per slice) of each matrix
 };
 
-template <int FMT, int G, int MT, int NW, int P, bool XL>
-__global__ void __launch_bounds__((NW + (XL ? 1 : 0)) * 64)
-gemv3_kernel(const GemvBatch p, int cpw) {
+template <int FMT, int G>
+struct CodeSlot {
+  uint4 c;                              // codes
+  uint32_t s;                           // SB: d | dmin << 16
+  uint32_t sub[FMT == GF_SB ? 3 : 1];   // SB: packed 6-bit sub-scale codes
+};
+
+// MR: activation rows that can be non-zero among a lane's four outputs
+// (m <= MR), so scale multiplications skip rows that are known to be zero.
+template <int FMT, int G, int MT, int CPW, int MR>
+__global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
-  typedef RingSlot<FMT, G, MT, XL> S;
-  constexpr int NM = F::NM;
-  // dynamic LDS: (XL) the activations [(m + 1) rows][k + 8 halves] during the
-  // loop, then the waves' partial sums [NW][MT][4][64] (after a barrier)
+  typedef CodeSlot<FMT, G> S;
   extern __shared__ uint4 lds4[];
   uint16_t* xl = (uint16_t*)lds4;
-  float (*red)[MT][4][64] = (float (*)[MT][4][64])lds4;
 
-  int tile = blockIdx.x;
-  int mi = 0;
-  if (tile >= p.mat[0].tiles) {
-    tile -= p.mat[0].tiles;
-    mi = 1;
-    if (tile >= p.mat[1].tiles) {
-      tile -= p.mat[1].tiles;
-      mi = 2;
-    }
-  }
-  const GemvMatrix& A = p.mat[mi];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  // slice and tile group; every field of the three descriptors is read
+  // unconditionally so picking the matrix costs no dependent scalar load
+  const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
+  const int s = blockIdx.x / gtot;
+  const int gall = blockIdx.x - s * gtot;
+  const int g0 = sp.groups[0], g1 = sp.groups[1];
+  const bool in1 = gall >= g0, in2 = gall >= g0 + g1;
+  const int grp = gall - (in2 ? g0 + g1 : (in1 ? g0 : 0));
+  GemvMatrix A;
+  A.codes = in2 ? p.mat[2].codes : (in1 ? p.mat[1].codes : p.mat[0].codes);
+  A.scales = in2 ? p.mat[2].scales : (in1 ? p.mat[1].scales : p.mat[0].scales);
+  A.mins = in2 ? p.mat[2].mins : (in1 ? p.mat[1].mins : p.mat[0].mins);
+  A.sub = in2 ? p.mat[2].sub : (in1 ? p.mat[1].sub : p.mat[0].sub);
+  A.x = in2 ? p.mat[2].x : (in1 ? p.mat[1].x : p.mat[0].x);
+  A.y = in2 ? p.mat[2].y : (in1 ? p.mat[1].y : p.mat[0].y);
+  A.n = in2 ? p.mat[2].n : (in1 ? p.mat[1].n : p.mat[0].n);
+  A.tiles = in2 ? p.mat[2].tiles : (in1 ? p.mat[1].tiles : p.mat[0].tiles);
+
+  const int NW = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = wave / sp.wpt;  // row tile of this wave within the group
+  const int wv = wave - r * sp.wpt;
   const int lane = threadIdx.x & 63;
   const int j = lane & 15;
   const int kq = lane >> 4;
+  const int tile = grp * sp.rt + r;
+  const bool tvalid = tile < A.tiles;
   const int n = tile * 16 + j;
   const bool nvalid = n < A.n;
   const int k = p.k;
   const int M = p.m;
   const int nchunks = k / F::CK;
-  const int ldl = k + 8;                          // LDS row stride (halves)
-  constexpr uint32_t kOOB = 0x7ffff000u;          // scalar offset past any buffer
-
-  if constexpr (XL) {
-    if (wave == NW) {
-      // staging wave: x rows < M into LDS (64 blocks of 8 halves per
-      // instruction), then the zero row; wait for its own copies only
-      const int blocks = k / 8;
-      for (int m = 0; m < M; ++m) {
-        for (int b0 = 0; b0 < blocks; b0 += 64) {
-          const int b = b0 + lane;
-          if (b < blocks) {
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(A.x + (size_t)m * p.ldx + (size_t)b * 8),
-                (__attribute__((address_space(3))) void*)((uint8_t*)lds4 + ((size_t)m * ldl + b0 * 8) * 2), 16,
-                0, 0);
-          }
-        }
-      }
-      for (int b = lane; b < blocks; b += 64) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
-      __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): the copies have landed
-    }
-  }
+  const int cbeg = s * sp.cps;
+  const int cend = min(nchunks, cbeg + sp.cps);
+  const int ldl = sp.cps * F::CK + 8;  // LDS row stride (halves)
+  constexpr uint32_t kOOB = 0x7ffff000u;  // scalar offset past any buffer: loads read zero
 
   // buffer resources (num_records in bytes).  Rows >= n read row 0: their
   // output columns are never stored and MFMA columns are independent.
@@ -519,293 +529,17 @@ gemv3_kernel(const GemvBatch p, int cpw) {
     sboff = nvalid ? (uint32_t)n * nsb * 2u : 0u;
     subb = nvalid ? (uint32_t)n * nsb * 12u : 0u;
   }
-  // activation rows of this lane (A operand), !XL: from global, zero beyond M
-  bool mval[MT];
-  const uint16_t* xg[MT];
-  int xrow[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int m = t * 16 + j;
-    mval[t] = m < M;
-    xg[t] = A.x + (size_t)(mval[t] ? m : 0) * p.ldx + x_base<FMT, G>(kq);
-    xrow[t] = (mval[t] ? m : M) * ldl + x_base<FMT, G>(kq);
-  }
 
-  auto load = [&](S& sl, int c, bool valid) {
-    const uint32_t so = valid ? (uint32_t)c * 64u : kOOB;
-    auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, so, 0);
-    sl.c = make_uint4(v[0], v[1], v[2], v[3]);
-    if constexpr (FMT == GF_W4 || FMT == GF_W8) {
-      const uint32_t ss = valid ? (uint32_t)c * (F::GPC * 2) : kOOB;
-      if constexpr (F::GPC == 1) {
-        sl.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, ss, 0);
-      } else if constexpr (F::GPC == 2) {
-        sl.s = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, ss, 0);
-      } else {
-        auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, ss, 0);
-        sl.s = t[0];
-        sl.s2 = t[1];
-      }
-    } else if constexpr (FMT == GF_SB) {
-      const uint32_t sb = (uint32_t)c >> 1;
-      const uint32_t s2 = valid ? sb * 2u : kOOB;
-      const uint32_t s12 = valid ? sb * 12u : kOOB;
-      const uint32_t d = __builtin_amdgcn_raw_buffer_load_b16(rs, sboff, s2, 0);
-      const uint32_t dm = __builtin_amdgcn_raw_buffer_load_b16(rm, sboff, s2, 0);
-      sl.s = d | (dm << 16);
-      auto t = __builtin_amdgcn_raw_buffer_load_b96(rb, subb, s12, 0);
-      sl.sub[0] = t[0];
-      sl.sub[1] = t[1];
-      sl.sub[2] = t[2];
-    }
-    if constexpr (!XL) {
-      const int cc = valid ? c : 0;  // an invalid chunk's codes and scales are zero
-#pragma unroll
-      for (int q = 0; q < NM; ++q) {
-        const int off = cc * F::CK + x_const<FMT, G>(q / F::MPG, q % F::MPG);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          if constexpr (F::XH == 8) {
-            sl.x[q][t] = mval[t] ? *(const uint4*)(xg[t] + off) : make_uint4(0u, 0u, 0u, 0u);
-          } else {
-            uint2 h = mval[t] ? *(const uint2*)(xg[t] + off) : make_uint2(0u, 0u);
-            sl.x[q][t] = make_uint4(h.x, h.y, 0u, 0u);
-          }
-        }
-      }
-    }
-  };
-
-  float4v acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
-  const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
-
-  // kk: chunk start (halves); for an invalid chunk a valid start (its codes
-  // and scales are zero)
-  auto compute = [&](const S& sl, int c, int kk) {
-    uint32_t w[4] = {sl.c.x, sl.c.y, sl.c.z, sl.c.w};
-    uint32_t gw[4][2];
-    if constexpr (F::GPC == 2) {
-      swap32(w[0], w[2]);
-      swap32(w[1], w[3]);
-      gw[0][0] = w[0]; gw[0][1] = w[1];
-      gw[1][0] = w[2]; gw[1][1] = w[3];
-    } else if constexpr (F::GPC == 4) {
-      swap32(w[0], w[2]);
-      swap32(w[1], w[3]);
-      swap16(w[0], w[1]);
-      swap16(w[2], w[3]);
-      gw[0][0] = w[0]; gw[1][0] = w[1]; gw[2][0] = w[2]; gw[3][0] = w[3];
-    }
-    float scl[4], mnv[4];
-    if constexpr (FMT == GF_W4 || FMT == GF_W8) {
-      scl[0] = f16_bits_to_f32((uint16_t)(sl.s & 0xffffu));
-      scl[1] = f16_bits_to_f32((uint16_t)(sl.s >> 16));
-      if constexpr (F::GPC == 4) {
-        scl[2] = f16_bits_to_f32((uint16_t)(sl.s2 & 0xffffu));
-        scl[3] = f16_bits_to_f32((uint16_t)(sl.s2 >> 16));
-      }
-    } else if constexpr (FMT == GF_SB) {
-      const float d = f16_bits_to_f32((uint16_t)(sl.s & 0xffffu));
-      const float dm = f16_bits_to_f32((uint16_t)(sl.s >> 16));
-      const uint64_t lo48 = (uint64_t)sl.sub[0] | ((uint64_t)(sl.sub[1] & 0xffffu) << 32);
-      const uint64_t hi48 = (uint64_t)(sl.sub[1] >> 16) | ((uint64_t)sl.sub[2] << 16);
-      const int half = (c & 1) * 4;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        scl[g] = d * (float)((uint32_t)(lo48 >> (6 * (half + g))) & 63u);  // exact
-        mnv[g] = dm * (float)((uint32_t)(hi48 >> (6 * (half + g))) & 63u);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < F::GPC; ++g) {
-      float4v grp[MT], xs[MT];
-#pragma unroll
-      for (int pp = 0; pp < F::MPG; ++pp) {
-        const int q = g * F::MPG + pp;
-        const int xo = kk + x_const<FMT, G>(g, pp);
-        if constexpr (F::KPM == 32) {
-          half8 b;
-          if constexpr (FMT == GF_F16) {
-            b = __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));
-          } else if constexpr (FMT == GF_W4 || FMT == GF_SB) {
-            b = dec4n<FMT == GF_W4>(F::GPC == 2 ? gw[g][pp] : gw[g][0]);
-          } else {  // int8: 8 k per MFMA
-            uint32_t wa, wb;
-            if constexpr (F::GPC == 1) {
-              wa = w[2 * pp];
-              wb = w[2 * pp + 1];
-            } else {
-              wa = gw[g][0];
-              wb = gw[g][1];
-            }
-            const uint2 lo = dec8n(wa), hi = dec8n(wb);
-            b = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          }
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            half8 a;
-            if constexpr (XL) a = *(const half8*)(xl + xrow[t] + xo);
-            else a = __builtin_bit_cast(half8, sl.x[q][t]);
-            if constexpr (FMT == GF_F16) {
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
-            } else {
-              grp[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, pp == 0 ? zero4 : grp[t], 0, 0, 0);
-              if constexpr (FMT == GF_SB) {
-                const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-                xs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, zero4, 0, 0, 0);
-              }
-            }
-          }
-        } else {  // int8 group 16: 4 k per lane, 16x16x16
-          const uint2 r = dec8n(gw[g][0]);
-          const half4 b = __builtin_bit_cast(half4, r);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            half4 a;
-            if constexpr (XL) a = *(const half4*)(xl + xrow[t] + xo);
-            else a = __builtin_bit_cast(half4, make_uint2(sl.x[q][t].x, sl.x[q][t].y));
-            grp[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, zero4, 0, 0, 0);
-          }
-        }
-      }
-      if constexpr (FMT != GF_F16) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            acc[t][r] += scl[g] * grp[t][r];
-            if constexpr (FMT == GF_SB) acc[t][r] -= mnv[g] * xs[t][r];
-          }
-      }
-    }
-  };
-
-  if (wave < NW) {
-    const int w0 = wave * cpw;  // this wave's first chunk
-    S ring[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) load(ring[q], w0 + q, w0 + q < nchunks);
-    if constexpr (XL) __syncthreads();  // the staging wave's copies are in LDS
-    for (int s0 = 0; s0 < cpw; s0 += P) {
-#pragma unroll
-      for (int q = 0; q < P; ++q) {
-        const int c = w0 + s0 + q;
-        const int cv = c < nchunks ? c : nchunks - 1;  // keep the activation offset in range
-        compute(ring[q], cv, cv * F::CK);
-        const int cn = c + P;
-        if (s0 + P < cpw) load(ring[q], cn, cn < nchunks && s0 + q + P < cpw);
-      }
-    }
-  } else {
-    if constexpr (XL) __syncthreads();
-  }
-
-  if constexpr (NW > 1 || XL) {
-    __syncthreads();  // every wave is done with the staged activations
-    if (wave < NW) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][t][r][lane] = acc[t][r];
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < MT * 4 * 64; idx += (NW + (XL ? 1 : 0)) * 64) {
-      const int t = idx / 256, r = (idx / 64) & 3, l = idx & 63;
-      float v = red[0][t][r][l];
-#pragma unroll
-      for (int w2 = 1; w2 < NW; ++w2) v += red[w2][t][r][l];
-      const int m = t * 16 + 4 * (l >> 4) + r;
-      const int nn = tile * 16 + (l & 15);
-      if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = t * 16 + 4 * kq + r;
-        if (m < M && nvalid) A.y[(size_t)m * p.ldy + n] = f32_to_f16_bits(acc[t][r]);
-      }
-  }
-}
-
-constexpr int kXBudget = 80 * 1024;  // bytes of LDS for staged activations
-
-// ---------------------------------------------------------------------------
-// upfront kernel (activations in LDS): every wave owns CPW chunks of one
-// 16-row tile and issues all of their loads before computing
-// ---------------------------------------------------------------------------
-// With only a few chunks per wave a refilling ring adds a round trip per
-// refill; issuing everything at once keeps the most bytes in flight.  The
-// workgroup's waves split K (NW = blockDim / 64 waves, a launch parameter);
-// each copies its share of the activations into LDS with global_load_lds
-// after issuing its code loads, then all wait and meet at a barrier.
-// MR: activation rows that can be non-zero among a lane's four outputs
-// (m <= MR), so scale multiplications skip rows that are known to be zero.
-template <int FMT, int G, int MT, int CPW, int MR>
-__global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
-  typedef F2<FMT, G> F;
-  typedef RingSlot<FMT, G, MT, true> S;
-  extern __shared__ uint4 lds4[];
-  uint16_t* xl = (uint16_t*)lds4;
-
-  // pick the matrix of this tile; every field of the three descriptors is
-  // read unconditionally so the choice costs no dependent scalar load
-  int tile = blockIdx.x;
-  const int t0 = p.mat[0].tiles, t1 = p.mat[1].tiles;
-  const bool in1 = tile >= t0, in2 = tile >= t0 + t1;
-  tile -= in2 ? t0 + t1 : (in1 ? t0 : 0);
-  GemvMatrix A;
-  A.codes = in2 ? p.mat[2].codes : (in1 ? p.mat[1].codes : p.mat[0].codes);
-  A.scales = in2 ? p.mat[2].scales : (in1 ? p.mat[1].scales : p.mat[0].scales);
-  A.mins = in2 ? p.mat[2].mins : (in1 ? p.mat[1].mins : p.mat[0].mins);
-  A.sub = in2 ? p.mat[2].sub : (in1 ? p.mat[1].sub : p.mat[0].sub);
-  A.x = in2 ? p.mat[2].x : (in1 ? p.mat[1].x : p.mat[0].x);
-  A.y = in2 ? p.mat[2].y : (in1 ? p.mat[1].y : p.mat[0].y);
-  A.n = in2 ? p.mat[2].n : (in1 ? p.mat[1].n : p.mat[0].n);
-  const int NW = blockDim.x >> 6;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15;
-  const int kq = lane >> 4;
-  const int n = tile * 16 + j;
-  const bool nvalid = n < A.n;
-  const int k = p.k;
-  const int M = p.m;
-  const int nchunks = k / F::CK;
-  const int ldl = k + 8;
-  constexpr uint32_t kOOB = 0x7ffff000u;
-
-  const uint32_t rowbytes = (uint32_t)nchunks * 64u;
-  const __amdgpu_buffer_rsrc_t rc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)A.codes, (short)0, (int)((uint32_t)A.n * rowbytes), 0x00020000);
-  const uint32_t coff = (nvalid ? (uint32_t)n * rowbytes : 0u) + (uint32_t)kq * 16u;
-  __amdgpu_buffer_rsrc_t rs = rc, rm = rc, rb = rc;
-  uint32_t soff = 0, sboff = 0, subb = 0;
-  if constexpr (FMT == GF_W4 || FMT == GF_W8) {
-    const uint32_t srow = (uint32_t)(k / F::GK) * 2u;
-    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * srow), 0x00020000);
-    soff = nvalid ? (uint32_t)n * srow : 0u;
-  } else if constexpr (FMT == GF_SB) {
-    const uint32_t nsb = (uint32_t)(k / 256);
-    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * nsb * 2u), 0x00020000);
-    rm = __builtin_amdgcn_make_buffer_rsrc((void*)A.mins, (short)0, (int)((uint32_t)A.n * nsb * 2u), 0x00020000);
-    rb = __builtin_amdgcn_make_buffer_rsrc((void*)A.sub, (short)0, (int)((uint32_t)A.n * nsb * 12u), 0x00020000);
-    sboff = nvalid ? (uint32_t)n * nsb * 2u : 0u;
-    subb = nvalid ? (uint32_t)n * nsb * 12u : 0u;
-  }
-
-  // 1. this wave's codes and scales, all at once.  Invalid chunks read zero
-  //    codes; their scales are zeroed after loading (the scale span is read
-  //    in one piece and may run into the next row)
-  const int c0 = wave * CPW;
+  // 1. this wave's codes and scales, all at once.  Chunks outside the slice
+  //    (or of a tile past the matrix) read zero codes; their scales are zeroed
+  //    after loading (the scale span is read in one piece and may run into
+  //    the next slice or row)
+  const int c0 = cbeg + wv * CPW;
   S sl[CPW];
   constexpr int SW = (FMT == GF_W4 || FMT == GF_W8) ? (CPW * F::GPC * 2 + 3) / 4 : 1;  // scale words
   uint32_t sw[SW];
   if constexpr (FMT == GF_W4 || FMT == GF_W8) {
-    const uint32_t ss = (uint32_t)c0 * (F::GPC * 2);
+    const uint32_t ss = tvalid ? (uint32_t)c0 * (F::GPC * 2) : kOOB;
     if constexpr (SW >= 4) {
 #pragma unroll
       for (int q = 0; q < SW / 4; ++q) {
@@ -822,7 +556,7 @@ __global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int c = c0 + i;
-    const bool valid = c < nchunks;
+    const bool valid = tvalid && c < cend;
     auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, valid ? (uint32_t)c * 64u : kOOB, 0);
     sl[i].c = make_uint4(v[0], v[1], v[2], v[3]);
     if constexpr (FMT == GF_SB) {
@@ -839,17 +573,18 @@ __global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
     }
   }
 
-  // 2. this wave's share of the activations: rows < M, 64 blocks of 8
-  //    halves per copy instruction, copy instructions dealt round-robin
+  // 2. the workgroup's activation slice: rows < M, 64 blocks of 8 halves per
+  //    copy instruction, copy instructions dealt round-robin to the waves
   {
-    const int blocks = k / 8;
+    const int blocks = (cend - cbeg) * (F::CK / 8);
     const int per_row = (blocks + 63) / 64;
+    const uint16_t* xs = A.x + (size_t)cbeg * F::CK;
     for (int q = wave; q < M * per_row; q += NW) {
       const int m = q / per_row;
       const int b0 = (q - m * per_row) * 64;
       const int b = b0 + lane;
       if (b < blocks)
-        __builtin_amdgcn_global_load_lds((const void*)(A.x + (size_t)m * p.ldx + (size_t)b * 8),
+        __builtin_amdgcn_global_load_lds((const void*)(xs + (size_t)m * p.ldx + (size_t)b * 8),
                                          (__attribute__((address_space(3))) void*)((uint8_t*)lds4 + ((size_t)m * ldl + b0 * 8) * 2),
                                          16, 0, 0);
     }
@@ -872,8 +607,9 @@ __global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
   // 3. compute, chunk by chunk
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    const int c = c0 + i < nchunks ? c0 + i : nchunks - 1;  // activation offset in range
-    const int kk = c * F::CK;
+    const bool valid = tvalid && c0 + i < cend;
+    const int c = c0 + i < cend ? c0 + i : cend - 1;  // activation offset inside the slice
+    const int kk = (c - cbeg) * F::CK;
     uint32_t w[4] = {sl[i].c.x, sl[i].c.y, sl[i].c.z, sl[i].c.w};
     uint32_t gw[4][2];
     if constexpr (F::GPC == 2) {
@@ -890,7 +626,6 @@ __global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
     }
     float scl[4], mnv[4];
     if constexpr (FMT == GF_W4 || FMT == GF_W8) {
-      const bool valid = c0 + i < nchunks;
 #pragma unroll
       for (int g = 0; g < F::GPC; ++g) {
         const int h = i * F::GPC + g;  // half-word index in the wave's scale span
@@ -948,8 +683,8 @@ __global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
             }
           }
         } else {
-          const uint2 r = dec8n(gw[g][0]);
-          const half4 b = __builtin_bit_cast(half4, r);
+          const uint2 rr = dec8n(gw[g][0]);
+          const half4 b = __builtin_bit_cast(half4, rr);
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             const half4 a = *(const half4*)(xl + xrow[t] + xo);
@@ -961,61 +696,150 @@ __global__ void __launch_bounds__(1024) gemv4_kernel(const GemvBatch p) {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int r = 0; r < (MT == 1 ? MR : 4); ++r) {
-            acc[t][r] += scl[g] * grp[t][r];
-            if constexpr (FMT == GF_SB) acc[t][r] -= mnv[g] * xs[t][r];
+          for (int q = 0; q < (MT == 1 ? MR : 4); ++q) {
+            acc[t][q] += scl[g] * grp[t][q];
+            if constexpr (FMT == GF_SB) acc[t][q] -= mnv[g] * xs[t][q];
           }
       }
     }
   }
 
-  // 4. combine the waves' partial sums in wave order and store fp16
+  // 4. reduce the waves of each row tile in wave order
   float (*red)[MT][4][64] = (float (*)[MT][4][64])lds4;
   __syncthreads();  // everyone is done with the activations
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][t][r][lane] = acc[t][r];
+    for (int q = 0; q < 4; ++q) red[wave][t][q][lane] = acc[t][q];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < MT * 4 * 64; idx += blockDim.x) {
-    const int t = idx / 256, r = (idx / 64) & 3, l = idx & 63;
-    float v = red[0][t][r][l];
-    for (int w2 = 1; w2 < NW; ++w2) v += red[w2][t][r][l];
-    const int m = t * 16 + 4 * (l >> 4) + r;
-    const int nn = tile * 16 + (l & 15);
-    if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
+  constexpr int E = MT * 4 * 64;  // outputs of one row tile (rows m < 16 MT)
+  const int ent = sp.rt * E;
+  float* part = sp.split > 1 ? p.ws + ((size_t)gall * sp.split + s) * ent : nullptr;
+  for (int idx = threadIdx.x; idx < ent; idx += blockDim.x) {
+    const int rr = idx / E, e = idx - rr * E;
+    const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
+    float v = red[rr * sp.wpt][t][q][l];
+    for (int w2 = 1; w2 < sp.wpt; ++w2) v += red[rr * sp.wpt + w2][t][q][l];
+    if (part) {
+      part[idx] = v;
+    } else {
+      const int m = t * 16 + 4 * (l >> 4) + q;
+      const int nn = (grp * sp.rt + rr) * 16 + (l & 15);
+      if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
+    }
   }
 }
 
-// activations staged in LDS, loads up front; returns false when the shape
-// needs another kernel (activations too large, or more than 16 waves)
+// Split K, second step: y = fp16(sum of the `split` partial tiles, in slice
+// order), one thread per output of a tile group.  The kernel boundary orders
+// it after every slice's stores.
+template <int MT>
+__global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, const Split5 sp) {
+  constexpr int E = MT * 4 * 64;
+  const int ent = sp.rt * E;
+  const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
+  const int gi = blockIdx.x * 256 + threadIdx.x;
+  const int gall = gi / ent;
+  if (gall >= gtot) return;
+  const int idx = gi - gall * ent;
+  const float* base = p.ws + (size_t)gall * sp.split * ent + idx;
+  float v = base[0];
+  for (int s2 = 1; s2 < sp.split; ++s2) v += base[(size_t)s2 * ent];
+  const int g0 = sp.groups[0], g1 = sp.groups[1];
+  const bool in1 = gall >= g0, in2 = gall >= g0 + g1;
+  const int grp = gall - (in2 ? g0 + g1 : (in1 ? g0 : 0));
+  const GemvMatrix& A = p.mat[in2 ? 2 : (in1 ? 1 : 0)];
+  const int rr = idx / E, e = idx - rr * E;
+  const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
+  const int m = t * 16 + 4 * (l >> 4) + q;
+  const int nn = (grp * sp.rt + rr) * 16 + (l & 15);
+  if (m < p.m && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
+}
+
+// Launch shape for gemv5_kernel, or false when none fits (activation slice
+// too large for LDS even at the finest split, or no workspace for a split).
+// Preference: the fewest slices that give at least one workgroup per compute
+// unit; then as many row tiles per workgroup (up to 4, sharing the x slice)
+// as still keep that many workgroups.
 template <int FMT, int G>
-static bool launch4(const GemvBatch& b, hipStream_t st, hipError_t& err) {
+static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
   typedef F2<FMT, G> F;
-  const size_t xb = (size_t)(b.m + 1) * (b.k + 8) * 2;
-  if (xb > (size_t)kXBudget) return false;
-  int tiles = 0;
-  for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
   const int nchunks = b.k / F::CK;
-  const int cpw = nchunks <= 64 ? 4 : 8;
-  const int nw = (nchunks + cpw - 1) / cpw;
-  if (nw > 16) return false;
   const int mt = b.m <= 16 ? 1 : 2;
+  bool found = false;
+  for (int split = 1; split <= 16; split *= 2) {
+    if (split > nchunks) break;
+    if (split > 1 && !b.ws) break;
+    // a wave's scale span is loaded from byte c0 * 2 * GPC and must start on a
+    // 4-byte boundary: with one scale per chunk (int8 group 64) slices hold an
+    // even number of chunks (CPW is even)
+    constexpr int cmult = (F::GPC == 1 && (FMT == GF_W4 || FMT == GF_W8)) ? 2 : 1;
+    const int cps = ((nchunks + split - 1) / split + cmult - 1) / cmult * cmult;
+    if ((split - 1) * cps >= nchunks) continue;  // an empty slice
+    const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
+    if (xb > (size_t)kXBudget) continue;
+    const int cpw = cps <= 64 ? 4 : 8;
+    const int wpt = (cps + cpw - 1) / cpw;
+    if (wpt > 16) continue;
+    int rt = 1;
+    auto groups = [&](int r) {
+      int g = 0;
+      for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
+      return g;
+    };
+    if (b.m > 1)
+      while (rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) * split >= 256) rt *= 2;
+    if (split > 1 && (size_t)groups(rt) * rt * split * mt * 1024 > kGemvWsPartialBytes) break;
+    sp.split = split;
+    sp.cps = cps;
+    sp.wpt = wpt;
+    sp.rt = rt;
+    for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
+    cpw_out = cpw;
+    found = true;
+    // a split costs a second launch: worth it only to occupy more than half
+    // of the compute units, or to fit the activations
+    if (groups(rt) * split >= (split == 1 ? 128 : 256)) break;
+  }
+  return found;
+}
+
+template <int FMT, int G>
+static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
+  typedef F2<FMT, G> F;
+  Split5 sp;
+  int cpw = 4;
+  if (!plan5<FMT, G>(b, sp, cpw)) return false;
+  const int mt = b.m <= 16 ? 1 : 2;
+  const int nw = sp.rt * sp.wpt;
+  const size_t xb = (size_t)(b.m + 1) * (sp.cps * F::CK + 8) * 2;
   const size_t red = (size_t)nw * mt * 4 * 64 * 4;
   const size_t lds = xb > red ? xb : red;
-  const dim3 grid(tiles), block(nw * 64);
-#define RQ_L4(MT, CPW, MR) hipLaunchKernelGGL((gemv4_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b)
+  const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
+  err = hipSuccess;
+  if (gtot == 0) return true;
+  const dim3 grid((unsigned)(gtot * sp.split)), block((unsigned)(nw * 64));
+#define RQ_L5(MT, CPW, MR) hipLaunchKernelGGL((gemv5_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b, sp)
   if (mt == 2) {
-    if (cpw == 4) RQ_L4(2, 4, 4); else RQ_L4(2, 8, 4);
+    if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
   } else if (b.m == 1) {
-    if (cpw == 4) RQ_L4(1, 4, 1); else RQ_L4(1, 8, 1);
+    if (cpw == 4) RQ_L5(1, 4, 1); else RQ_L5(1, 8, 1);
   } else if (b.m == 2) {
-    if (cpw == 4) RQ_L4(1, 4, 2); else RQ_L4(1, 8, 2);
+    if (cpw == 4) RQ_L5(1, 4, 2); else RQ_L5(1, 8, 2);
   } else {
-    if (cpw == 4) RQ_L4(1, 4, 4); else RQ_L4(1, 8, 4);
+    if (cpw == 4) RQ_L5(1, 4, 4); else RQ_L5(1, 8, 4);
   }
-#undef RQ_L4
+#undef RQ_L5
   err = hipGetLastError();
+  if (err == hipSuccess && sp.split > 1) {
+    const int outs = gtot * sp.rt * mt * 256;
+    const dim3 rgrid((unsigned)((outs + 255) / 256));
+    if (mt == 2)
+      hipLaunchKernelGGL(gemv5_reduce_kernel<2>, rgrid, dim3(256), 0, st, b, sp);
+    else
+      hipLaunchKernelGGL(gemv5_reduce_kernel<1>, rgrid, dim3(256), 0, st, b, sp);
+    err = hipGetLastError();
+  }
   return true;
 }
 
@@ -1044,72 +868,13 @@ static hipError_t launch_nw(const GemvBatch& b, hipStream_t st) {
 }
 
 
-template <int FMT, int G, int MT, int NW, bool XL>
-static hipError_t launch3_p(const GemvBatch& b, hipStream_t st, int tiles, int cpw, size_t lds) {
-  constexpr int PMAX = XL ? 8 : (MT == 1 ? 4 : 2);
-  const int threads = (NW + (XL ? 1 : 0)) * 64;
-  if (cpw <= 4 || PMAX == 4) {
-    const int c = (cpw + 3) / 4 * 4;
-    if constexpr (PMAX >= 4) {
-      hipLaunchKernelGGL((gemv3_kernel<FMT, G, MT, NW, 4, XL>), dim3(tiles), dim3(threads), lds, st, b, c);
-      return hipGetLastError();
-    }
-  }
-  if constexpr (PMAX == 8) {
-    const int c = (cpw + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemv3_kernel<FMT, G, MT, NW, 8, XL>), dim3(tiles), dim3(threads), lds, st, b, c);
-  } else {
-    const int c = (cpw + 1) / 2 * 2;
-    hipLaunchKernelGGL((gemv3_kernel<FMT, G, MT, NW, 2, XL>), dim3(tiles), dim3(threads), lds, st, b, c);
-  }
-  return hipGetLastError();
-}
-
-template <int FMT, int G, int MT, int NW>
-static hipError_t launch3_t(const GemvBatch& b, hipStream_t st, int tiles) {
-  const int nchunks = b.k / F2<FMT, G>::CK;
-  const int cpw = (nchunks + NW - 1) / NW;
-  const size_t xb = (size_t)(b.m + 1) * (b.k + 8) * 2;
-  const size_t red = (size_t)NW * MT * 4 * 64 * 4;
-  if (xb <= (size_t)kXBudget) return launch3_p<FMT, G, MT, NW, true>(b, st, tiles, cpw, xb > red ? xb : red);
-  if constexpr (NW <= 8) return launch3_p<FMT, G, MT, NW, false>(b, st, tiles, cpw, NW > 1 ? red : 0);
-  return hipErrorInvalidValue;
-}
-
-// waves per workgroup: enough waves in the grid to keep HBM busy, at least
-// two chunks per wave
-template <int FMT, int G, int MT>
-static hipError_t launch3_nw(const GemvBatch& b, hipStream_t st) {
-  typedef F2<FMT, G> F;
-  int tiles = 0;
-  for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
-  if (tiles == 0) return hipSuccess;
-  const int nchunks = b.k / F::CK;
-  const bool xl = (size_t)(b.m + 1) * (b.k + 8) * 2 <= (size_t)kXBudget;
-  int nw = xl ? 15 : 8;
-  if (xl) {
-    nw = 8;
-    while (nw > 1 && (nchunks / nw < 2 || tiles * (nw / 2) >= 4096)) nw /= 2;
-  } else {
-    while (nw > 1 && (nchunks / nw < 2 || tiles * (nw / 2) >= 4096)) nw /= 2;
-  }
-  switch (nw) {
-    case 8: return launch3_t<FMT, G, MT, 8>(b, st, tiles);
-    case 4: return launch3_t<FMT, G, MT, 4>(b, st, tiles);
-    case 2: return launch3_t<FMT, G, MT, 2>(b, st, tiles);
-    default: return launch3_t<FMT, G, MT, 1>(b, st, tiles);
-  }
-}
-
 template <int FMT, int G>
 static hipError_t launch_mt(const GemvBatch& b, hipStream_t st) {
   constexpr bool v2ok = !(FMT == GF_W4 && G == 16);
   if constexpr (v2ok) {
     if (b.k % F2<FMT, G>::CK == 0) {
       hipError_t err;
-      if (launch4<FMT, G>(b, st, err)) return err;
-      if (b.m <= 16) return launch3_nw<FMT, G, 1>(b, st);
-      return launch3_nw<FMT, G, 2>(b, st);
+      if (launch5<FMT, G>(b, st, err)) return err;
     }
   }
   if (b.m <= 16) return launch_nw<FMT, G, 1>(b, st);

@@ -38,7 +38,12 @@ struct GemvBatch {
   int m;
   int ldx;
   int ldy;
+  // workspace for products split along K (null: no split): fp32 partial
+  // tiles, summed by a second kernel
+  float* ws;
 };
+
+constexpr size_t kGemvWsPartialBytes = 64u << 20;
 
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 
