@@ -271,6 +271,145 @@ def alg_bytes(row, c1, c3, m3):
     return row["weight_bytes"] + 2 * m * c1 * 2
 
 
+def kernel_only(dec, pre, name, steps, dev):
+    """Counter run: one calibration copy of CALIB_BYTES, then the class graph
+    replayed `steps` times; every dispatch after the last copy belongs to it."""
+    classes = [(n, fn, dec.sets) for m in MS for n, fn, _, _ in dec.classes(m)]
+    classes += [(n, fn, pre.sets) for n, fn, _, _, _ in pre.classes()]
+    if not name:
+        rows = measure_classes(dec, pre, 1)
+        name = max(rows, key=lambda r: r["ms"] * r["per_step"])["name"]
+    match = [c for c in classes if c[0] == name]
+    if not match:
+        sys.exit("no kernel class named %r" % name)
+    _, fn, sets = match[0]
+    g = class_graph(fn, sets)
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    print("kernel-only: %s, %d launches per replay, %d replays, after a %d-byte calibration copy"
+          % (name, len(sets), steps, CALIB_BYTES), file=sys.stderr)
+
+
+def _counter_rows(path):
+    """{dispatch id: (kernel name, summed counter value)} from a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_from(fetch_csv, write_csv):
+    """HBM bytes per launch of a --kernel-only class: every dispatch after the
+    last calibration copy, scaled by what the counters read for that copy."""
+    res = {}
+    for label, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = _counter_rows(path)
+        ids = sorted(rows)
+        copies = [d for d in ids if "copyBuffer" in rows[d][0] or "copy" in rows[d][0].lower()]
+        if not copies:
+            sys.exit("%s: no calibration copy dispatch found" % path)
+        c = copies[-1]
+        calib = rows[c][1] * 1024.0  # the counters read KiB
+        after = [d for d in ids if d > c]
+        total = sum(rows[d][1] for d in after) * 1024.0
+        res[label] = (calib, total, len(after), sorted({rows[d][0].split("(")[0] for d in after}))
+    return res
+
+
+def trace_summary(path):
+    """Library kernels of a rocprofv3 kernel trace grouped by name and launch
+    shape (workgroups x threads): dispatches, mean and median duration."""
+    import csv
+    groups = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "rq::" not in name:
+                continue
+            short = name.split("(")[0].replace("void ", "")
+            wg = int(r["Workgroup_Size_X"])
+            key = (short, int(r["Grid_Size_X"]) // wg * int(r.get("Grid_Size_Y", 1) or 1), wg)
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("%-44s %9s %7s %9s %10s %10s" % ("kernel", "wgs", "threads", "dispatches", "mean_us", "median_us"))
+    for (short, wgs, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        print("%-44s %9d %7d %9d %10.2f %10.2f" % (short[:44], wgs, wg, len(v), sum(v) / len(v) / 1e3,
+                                                  v[len(v) // 2] / 1e3))
+
+
+def copies_for(name):
+    """Weight copies in rotation for a kernel class (without a GPU)."""
+    if "fp8" in name:
+        per_set = sum(n * k + 4 * n for _, n, k in synth.layer_shapes(C3))
+    else:
+        per_set = sum(sum(rq.rq_qweight_bytes(rq.RQ_W4_SYM, 64, n, k)[:2]) for _, n, k in synth.layer_shapes(C1))
+    return -(-ROTATE_BYTES // per_set)
+
+
+def print_traffic(csvs, name, steps):
+    """The lines of profiles/traffic.txt for class `name` (a --kernel-only run
+    with `steps` replays), from the FETCH_SIZE and WRITE_SIZE counter CSVs."""
+    if not name:
+        sys.exit("--traffic-from needs the class name in --kernel-only")
+    res = traffic_from(*csvs)
+    launches = steps * copies_for(name)
+    per = {}
+    for label in ("fetch", "write"):
+        calib, total, ndisp, kernels = res[label]
+        per[label] = total / calib * CALIB_BYTES / launches
+    print("class: %s" % name)
+    print("bytes_per_launch: %.0f" % (per["fetch"] + per["write"]))
+    print("fetch_bytes_per_launch: %.0f" % per["fetch"])
+    print("write_bytes_per_launch: %.0f" % per["write"])
+    for label, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        calib, total, ndisp, kernels = res[label]
+        print("%s_calibration: %s read %.0f KiB for the %d-byte copy (factor %.4f); %d dispatches after it: %s"
+              % (label, ctr, calib / 1024, CALIB_BYTES, CALIB_BYTES / calib, ndisp, ", ".join(kernels)))
+    print("launches: %d" % launches)
+    print("sources_sha256: %s" % sources_hash())
+
+
+def stored_traffic(name):
+    """Counter-derived bytes per launch for kernel class `name` from
+    profiles/traffic.txt, or None when absent, for another class, or taken
+    from kernel sources that have changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("class") != name or fields.get("sources_sha256") != sources_hash():
+        return None
+    try:
+        return float(fields["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_rwkv_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
 def cpu_baseline(c, budget_s=20.0):
     """The oracle (RTN quantize, dequantize, fp64 product) on host cores over a
     bounded sample of the decode step: whole width-c layers at M = 1, 8, 32."""
@@ -310,12 +449,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phases", action="store_true", help="per-class timings to stderr")
-    ap.add_argument("--kernel-only", action="store_true",
-                    help="replay only the dominant kernel class (and a calibration copy), print nothing")
+    ap.add_argument("--kernel-only", nargs="?", const="", default=None, metavar="CLASS",
+                    help="for counter runs: a calibration copy, then only the named kernel class "
+                         "(default: the dominant one) replayed --steps times")
     ap.add_argument("--class-reps", type=int, default=20)
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file of counter-derived HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="per kernel and launch shape: dispatches and mean duration, from a "
+                         "rocprofv3 --kernel-trace CSV")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs of a --kernel-only run into HBM "
+                         "bytes per launch (printed as the lines of a profiles/ summary)")
     args = ap.parse_args()
+    if args.traffic_from:
+        print_traffic(args.traffic_from, args.kernel_only, args.steps)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -326,18 +476,11 @@ def main():
 
     dec = Decode(C1, gen, dev)
     pre = Prefill(C3, M3, gen, dev)
+    if args.kernel_only is not None:
+        print("weights ready", file=sys.stderr, flush=True)
 
-    if args.kernel_only:
-        rows = measure_classes(dec, pre, 1)
-        dom = max(rows, key=lambda r: r["ms"] * r["per_step"])
-        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        for _ in range(args.steps):
-            dom["graph"].replay()
-        torch.cuda.synchronize()
-        print("dominant: %s (%d launches per replay, %d replays); calibration copy %d bytes"
-              % (dom["name"], dom["launches"], args.steps, CALIB_BYTES), file=sys.stderr)
+    if args.kernel_only is not None:
+        kernel_only(dec, pre, args.kernel_only, args.steps, dev)
         return
 
     graphs = [capture(lambda m=m: dec.passes(m)) for m in MS] + [capture(pre.passes)]
@@ -365,12 +508,7 @@ def main():
     for r in rows:
         r["alg_bytes"] = alg_bytes(r, C1, C3, M3)
     dom = max(rows, key=lambda r: r["ms"] * r["per_step"])
-    traffic = None
-    if args.traffic:
-        with open(args.traffic) as f:
-            t = json.load(f)
-        if t.get("kernel") == dom["name"]:
-            traffic = t["bytes_per_launch"]
+    traffic = stored_traffic(dom["name"])
     if args.phases:
         for name, t in zip(["decode M=%d" % m for m in MS] + ["prefill fp8 M=%d" % M3], per):
             print("%-22s %8.3f ms" % (name, t), file=sys.stderr)

@@ -429,7 +429,11 @@ constexpr int x_const(int g, int p) {
 }
 
 
-constexpr int kXBudget = 80 * 1024;  // bytes of LDS for a workgroup's activation slice
+// bytes of LDS for a workgroup's activation slice: 80 KB keeps two
+// workgroups per compute unit; an unsplit launch may take up to 150 KB (one
+// per compute unit) rather than pay for a second, reducing kernel
+constexpr int kXBudget = 80 * 1024;
+constexpr int kXBudgetUnsplit = 150 * 1024;
 
 // ---------------------------------------------------------------------------
 // the streaming kernel: a workgroup = RT row tiles x one slice of K
@@ -767,6 +771,31 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
   const int nchunks = b.k / F::CK;
   const int mt = b.m <= 16 ? 1 : 2;
   bool found = false;
+  // unsplit with a large activation slice, if that occupies at least half
+  // of the compute units
+  {
+    const size_t xb = (size_t)(b.m + 1) * (nchunks * F::CK + 8) * 2;
+    const int cpw = nchunks <= 64 ? 4 : 8;
+    const int wpt = (nchunks + cpw - 1) / cpw;
+    int tiles = 0;
+    for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
+    if (xb > (size_t)kXBudget && xb <= (size_t)kXBudgetUnsplit && wpt <= 16 && tiles >= 128) {
+      int rt = 1;
+      auto groups = [&](int r) {
+        int g = 0;
+        for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
+        return g;
+      };
+      while (rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) >= 128) rt *= 2;
+      sp.split = 1;
+      sp.cps = nchunks;
+      sp.wpt = wpt;
+      sp.rt = rt;
+      for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
+      cpw_out = cpw;
+      return true;
+    }
+  }
   for (int split = 1; split <= 16; split *= 2) {
     if (split > nchunks) break;
     if (split > 1 && !b.ws) break;
@@ -819,7 +848,15 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   err = hipSuccess;
   if (gtot == 0) return true;
   const dim3 grid((unsigned)(gtot * sp.split)), block((unsigned)(nw * 64));
-#define RQ_L5(MT, CPW, MR) hipLaunchKernelGGL((gemv5_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b, sp)
+#define RQ_L5(MT, CPW, MR)                                                                        \
+  do {                                                                                            \
+    static const bool attr_set =                                                                  \
+        hipFuncSetAttribute((const void*)gemv5_kernel<FMT, G, MT, CPW, MR>,                       \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kXBudgetUnsplit + 1024) == \
+        hipSuccess;                                                                               \
+    (void)attr_set;                                                                               \
+    hipLaunchKernelGGL((gemv5_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b, sp);         \
+  } while (0)
   if (mt == 2) {
     if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
   } else if (b.m == 1) {

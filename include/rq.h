@@ -15,7 +15,17 @@
  *   - Every buffer pointer is a DEVICE pointer on the current HIP device,
  *     except the rq_qweight descriptor itself and the size_t outputs of
  *     rq_qweight_bytes, which live in host memory.  The caller allocates and
- *     frees every buffer; the library keeps no pointer after returning.
+ *     frees every buffer it passes; the library keeps no pointer to them
+ *     after returning.
+ *   - Workspace: the weight-streaming products (rq_gemv_*, rq_gemm_small_m,
+ *     rq_fused_rkv) may cut K across workgroups and add the partial sums in
+ *     a second kernel.  Those partials live in a 64 MiB device buffer that
+ *     the library allocates on the first such call on each (device, stream)
+ *     pair and keeps until the process ends, so calls on different streams
+ *     never share one.  While a stream is being captured into a graph
+ *     nothing is allocated: a stream that has no workspace yet runs unsplit
+ *     launch shapes, with the same results (warm up on the capture stream
+ *     to capture the split shapes).
  *   - fp16 values are IEEE binary16 bit patterns (uint16_t).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it; product calls return without synchronizing.
@@ -30,9 +40,14 @@
  *     still be valid), k >= 1, n and k below 2^31, and the per-format rules of
  *     rq_qweight.
  *   - Determinism: the same inputs on the same device give bit-identical
- *     outputs (fixed reduction order, no floating-point atomics).
- *   - Thread safety: the library is stateless; calls on different streams
- *     may run concurrently.
+ *     outputs (fixed reduction order, no floating-point atomics).  Different
+ *     entry points over the same weights (a fused call and three single
+ *     calls, or a stream with and without a workspace) may split K
+ *     differently and differ within the fp32 summation tolerance.
+ *   - Thread safety: apart from the per-stream workspaces (guarded by a
+ *     lock) the library keeps no state; calls on different streams may run
+ *     concurrently.  A captured graph uses its capture stream's workspace,
+ *     so two replays of graphs captured on one stream must not overlap.
  */
 #ifndef RQ_H
 #define RQ_H
@@ -69,14 +84,15 @@ enum rq_status {
  *   and accuracy warning (int8 w8g64 tier); rwkv-quant news article, section
  *   "Dois presets e seis tamanhos" (8-bit symmetric projections, group 16).
  *     codes : int8 [n][k]                          (W8)
- *             uint8 [n][k/2], u = q + 8, even k in the low nibble   (W4)
+ *             uint8 [n][k/2], u = q + 8 in 4-bit words (W4): see "int4
+ *             code words" below
  *     scales: fp16 [n][k/group]
  * RQ_W4_ASYM_SB256 (group must be 32; k % 256 == 0)
  *   Asymmetric 4-bit codes in superblocks of 256 = 8 groups of 32 (news
  *   article, "Dois presets e seis tamanhos": 4-bit asymmetric superblocks,
  *   group 32).  Per group j: S_j = d * sc_j, M_j = dmin * mc_j,
  *   W_hat = S_j * q - M_j with q in 0..15.
- *     codes : uint8 [n][k/2] (q nibbles, even k low)
+ *     codes : uint8 [n][k/2] (q in 4-bit words: see "int4 code words")
  *     scales: fp16 d    [n][k/256]
  *     mins  : fp16 dmin [n][k/256]
  *     sub   : uint8 [n][k/256][12]: 96-bit little-endian stream, sc_j at bit
@@ -92,6 +108,13 @@ enum rq_status {
  *   Unquantized fp16 weights, used for the output head, which the toolkit
  *   keeps in FP16 (Key Design) and the model card keeps full precision.
  *     codes : fp16 [n][k];  scales, mins, sub: unused
+ *
+ * int4 code words (RQ_W4_SYM, RQ_W4_ASYM_SB256).  The pages fix no nibble
+ * order; each run of 8 consecutive k of a row is one little-endian 32-bit
+ * word whose bits 4i..4i+3 hold k = 2i and bits 16+4i..16+4i+3 hold
+ * k = 2i + 1 (i = 0..3), i.e. bytes [u0|u2<<4, u4|u6<<4, u1|u3<<4, u5|u7<<4].
+ * Even k fill the low half-word and odd k the high one, so a pair (2i,
+ * 2i + 1) decodes with one mask into the two halves of a packed fp16 pair.
  *
  * For quantizers, a zero scale (all-zero group, or a scale that rounds to
  * zero) gives all-zero codes.

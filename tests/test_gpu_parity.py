@@ -214,6 +214,8 @@ def test_power_of_two_scaling_and_determinism(fmt, group):
     # shapes whose launch splits K across workgroups and/or groups 2-4 row
     # tiles per workgroup (sharing one activation slice), with ragged tiles
     (quant.W4_SYM, 64, 8192, 2048, 8),      # 2 tiles per workgroup, K unsplit
+    (quant.W4_SYM, 64, 2048, 2048, 32),     # unsplit with a 136 KB activation slice in LDS
+    (quant.W8_SYM, 32, 2048, 2048, 24),     # the same for int8
     (quant.W4_SYM, 64, 2048, 8192, 32),     # K in 8 slices, 4 tiles per workgroup
     (quant.W4_SYM, 64, 1000, 4096, 32),     # ragged row tiles, split K
     (quant.W4_SYM, 32, 2048, 8192, 1),      # K in 2 slices
