@@ -534,7 +534,31 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     subb = nvalid ? (uint32_t)n * nsb * 12u : 0u;
   }
 
-  // 1. this wave's codes and scales, all at once.  Chunks outside the slice
+  // 1. the workgroup's activation slice: rows < M, 64 blocks of 8 halves per
+  //    copy instruction, copy instructions dealt round-robin to the waves.
+  //    These LDS DMA reads go out first and as inline asm: the compiler,
+  //    which cannot tell which LDS bytes a DMA writes, would otherwise wait
+  //    for every load in flight (the code loads included) before the first
+  //    LDS read.  They write no register.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
+  {
+    const int blocks = (cend - cbeg) * (F::CK / 8);
+    const int per_row = (blocks + 63) / 64;
+    const uint16_t* xs = A.x + (size_t)cbeg * F::CK;
+    for (int q = wave; q < M * per_row; q += NW) {
+      const int m = q / per_row;
+      const int b0 = (q - m * per_row) * 64;
+      const int b = b0 + lane;
+      if (b < blocks) {
+        const uint16_t* g = xs + (size_t)m * p.ldx + (size_t)b * 8;
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :: "v"(g), "s"(lds_base + (uint32_t)((m * ldl + b0 * 8) * 2)) : "memory", "m0");
+      }
+    }
+    for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // 2. this wave's codes and scales, all at once.  Chunks outside the slice
   //    (or of a tile past the matrix) read zero codes; their scales are zeroed
   //    after loading (the scale span is read in one piece and may run into
   //    the next slice or row)
@@ -577,25 +601,17 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     }
   }
 
-  // 2. the workgroup's activation slice: rows < M, 64 blocks of 8 halves per
-  //    copy instruction, copy instructions dealt round-robin to the waves
-  {
-    const int blocks = (cend - cbeg) * (F::CK / 8);
-    const int per_row = (blocks + 63) / 64;
-    const uint16_t* xs = A.x + (size_t)cbeg * F::CK;
-    for (int q = wave; q < M * per_row; q += NW) {
-      const int m = q / per_row;
-      const int b0 = (q - m * per_row) * 64;
-      const int b = b0 + lane;
-      if (b < blocks)
-        __builtin_amdgcn_global_load_lds((const void*)(xs + (size_t)m * p.ldx + (size_t)b * 8),
-                                         (__attribute__((address_space(3))) void*)((uint8_t*)lds4 + ((size_t)m * ldl + b0 * 8) * 2),
-                                         16, 0, 0);
-    }
-    for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and codes) have landed
-    __syncthreads();
-  }
+  // keep everything that uses the loaded scales below this point: hoisted
+  // between the loads, it would wait for the scale load before the first
+  // code load is issued
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. wait for this wave's copies only: with at most CPW loads still in
+  //    flight, every DMA issued before the CPW code loads has landed (a
+  //    wave's vector loads complete in issue order).  Then a plain barrier;
+  //    the code loads stay in flight, and each chunk below waits only for
+  //    its own load.
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(CPW) : "memory");
 
   int xrow[MT];
 #pragma unroll
@@ -608,7 +624,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   for (int t = 0; t < MT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
   const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // 3. compute, chunk by chunk
+  // 4. compute, chunk by chunk
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const bool valid = tvalid && c0 + i < cend;
@@ -708,7 +724,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     }
   }
 
-  // 4. reduce the waves of each row tile in wave order
+  // 5. reduce the waves of each row tile in wave order
   float (*red)[MT][4][64] = (float (*)[MT][4][64])lds4;
   __syncthreads();  // everyone is done with the activations
 #pragma unroll
