@@ -195,8 +195,12 @@ def quantize_sb256(w):
     wd = w.astype(np.float64).reshape(n, nsb, SB_NGROUPS, SB_GROUP)
     hi = np.max(wd, axis=3)
     lo = _group_low(wd)
-    s = (hi - lo) / 15.0                       # fp64 group scale
-    neglo = -lo                                # fp64 group offset (>= 0)
+    # fp64 group scale and offset.  Both are magnitudes (the offset is stored
+    # as an unsigned code that is subtracted), so a zero is +0: a range or an
+    # offset of zero must not become -0 and store 0x8000 as d or dmin.
+    s = (hi - lo) / 15.0
+    s = np.where(s == 0.0, 0.0, s)
+    neglo = 0.0 - lo
     d16 = codecs.f16_encode(np.max(s, axis=2) / 63.0)
     m16 = codecs.f16_encode(np.max(neglo, axis=2) / 63.0)
     if not (np.all(np.isfinite(d16)) and np.all(np.isfinite(m16))):

@@ -1,0 +1,238 @@
+"""Parity at the workloads' full sizes, in the launch shapes bench.py times.
+
+Weights are generated on the host from the seeded generators, quantized on
+the GPU with rq_quantize_rtn, and used by the same entry points as the
+benchmark (rq_fused_rkv, rq_gemm_small_m, rq_gemv_*, rq_quantize_act,
+rq_gemm_fp8/int8).  The oracle quantizes only a sample of rows (each row's
+codes depend on that row alone), checks their bytes against the GPU's, and
+computes the outputs of those rows for every activation row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_rwkv_amd.rq as rq
+from gemm_rwkv_amd import synth
+from gpu_helpers import dev_f16, dev_f32, host, say
+from oracle import quant, ref
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 48  # rows checked per matrix
+
+
+def _rows(n, seed):
+    g = np.random.default_rng(seed)
+    pick = g.choice(n, size=min(SAMPLE, n), replace=False)
+    return np.sort(np.concatenate([pick, [0, n - 1]]) if n > 2 else pick).astype(np.int64)
+
+
+def _gpu_weights(w, fmt, group):
+    return rq.quantize(dev_f32(w), fmt, group)
+
+
+def _check_rows_sym(qw, w, rows, fmt, group):
+    """Bytes of the sampled rows against the oracle; returns their parts."""
+    n, k = w.shape
+    bits = 4 if fmt == quant.W4_SYM else 8
+    parts = quant.quantize_sym(w[rows], bits, group)
+    cb = k // 2 if bits == 4 else k
+    codes = host(qw.codes, np.uint8)[: n * cb].reshape(n, cb)[rows]
+    scales = host(qw.scales, np.uint16)[: n * (k // group)].reshape(n, k // group)[rows]
+    assert np.array_equal(codes, parts["codes"].reshape(len(rows), -1).view(np.uint8)), "codes differ"
+    assert np.array_equal(scales, parts["scales"].view(np.uint16)), "scales differ"
+    return parts
+
+
+def _check_rows_sb(qw, w, rows):
+    n, k = w.shape
+    nsb = k // 256
+    parts = quant.quantize_sb256(w[rows])
+    got = {
+        "qs": host(qw.codes, np.uint8)[: n * k // 2].reshape(n, k // 2)[rows],
+        "d": host(qw.scales, np.uint16)[: n * nsb].reshape(n, nsb)[rows],
+        "dmin": host(qw.mins, np.uint16)[: n * nsb].reshape(n, nsb)[rows],
+        "sub": host(qw.sub, np.uint8)[: n * nsb * 12].reshape(n, nsb, 12)[rows],
+    }
+    assert np.array_equal(got["qs"], parts["qs"])
+    assert np.array_equal(got["d"], parts["d"].view(np.uint16))
+    assert np.array_equal(got["dmin"], parts["dmin"].view(np.uint16))
+    assert np.array_equal(got["sub"], parts["sub"])
+    return parts
+
+
+def _compare_rows(y, rows, x, fmt, parts, group, what):
+    y_ref, b = ref.weight_only_ref(x, fmt, parts, group)
+    ok, info = ref.compare(y[:, rows], y_ref, b)
+    assert ok, (what, info)
+
+
+# --------------------------------------------------------------------------
+# width 2048 (1.5B) layer, int4 g64, M in {1, 8, 32}: the benchmark's decode
+# --------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def layer_2048():
+    c = 2048
+    mats = {}
+    for mat, n, k in synth.layer_shapes(c):
+        w = synth.weight(1, 0, mat, n, k)
+        mats[mat] = (w, _gpu_weights(w, quant.W4_SYM, 64))
+    yield c, mats
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [1, 8, 32])
+def test_decode_layer_2048(layer_2048, m):
+    c, mats = layer_2048
+    x = synth.act_channel_1202(m, c)
+    x4 = synth.act_normal(m, 4 * c, 1)
+    xd, x4d = dev_f16(x), dev_f16(x4)
+    say("decode layer 2048 m", m)
+    ys = {mat: torch.empty(m * n * 2, dtype=torch.uint8, device="cuda") for mat, n, _ in synth.layer_shapes(c)}
+    q = {mat: mats[mat][1] for mat in mats}
+    rq.rq_fused_rkv(xd, xd, xd, m, c, q[synth.MAT_R], q[synth.MAT_K], q[synth.MAT_V],
+                    ys[synth.MAT_R], ys[synth.MAT_K], ys[synth.MAT_V], c)
+    rq.rq_gemm_small_m(xd, m, c, q[synth.MAT_O], ys[synth.MAT_O], c)
+    rq.rq_gemm_small_m(xd, m, c, q[synth.MAT_KEY], ys[synth.MAT_KEY], 4 * c)
+    rq.rq_gemm_small_m(x4d, m, 4 * c, q[synth.MAT_VALUE], ys[synth.MAT_VALUE], c)
+    torch.cuda.synchronize()
+    for mat, n, k in synth.layer_shapes(c):
+        w = mats[mat][0]
+        rows = _rows(n, 100 + mat)
+        parts = _check_rows_sym(q[mat], w, rows, quant.W4_SYM, 64)
+        y = host(ys[mat], np.float16).reshape(m, n)
+        _compare_rows(y, rows, x4 if k == 4 * c else x, quant.W4_SYM, parts, 64, synth.MAT_NAMES[mat])
+
+
+# --------------------------------------------------------------------------
+# width 2560 (2.9B): O, cmix key, cmix value as SB256, x with 8 massive channels
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_sb256_2560(m):
+    c = 2560
+    for mat, n, k in [(synth.MAT_O, c, c), (synth.MAT_KEY, 4 * c, c), (synth.MAT_VALUE, c, 4 * c)]:
+        w = synth.weight(2, 0, mat, n, k)
+        qw = _gpu_weights(w, quant.W4_ASYM_SB256, 32)
+        x = synth.act_massive(m, k)
+        y = torch.empty(m * n * 2, dtype=torch.uint8, device="cuda")
+        say("sb256 2560", synth.MAT_NAMES[mat], "m", m)
+        if m == 1:
+            rq.rq_gemv_w4sb256(dev_f16(x), qw, y)
+        else:
+            rq.rq_gemm_small_m(dev_f16(x), m, k, qw, y, n)
+        torch.cuda.synchronize()
+        rows = _rows(n, 200 + mat)
+        parts = _check_rows_sb(qw, w, rows)
+        _compare_rows(host(y, np.float16).reshape(m, n), rows, x, quant.W4_ASYM_SB256, parts, 32,
+                      synth.MAT_NAMES[mat])
+
+
+# --------------------------------------------------------------------------
+# width 4096 (7.2B) prefill set: fp8 and int8 per channel, M in {64, 256, 1024}
+# --------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def prefill_4096():
+    c = 4096
+    ws = {mat: synth.weight(3, 0, mat, n, k) for mat, n, k in synth.layer_shapes(c)}
+    q = {}
+    for kind, fmt in (("fp8", quant.FP8_E4M3_CH), ("int8", quant.I8_CH)):
+        q[kind] = {mat: _gpu_weights(w, fmt, 0) for mat, w in ws.items()}
+    yield c, ws, q
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+@pytest.mark.parametrize("m", [64, 256, 1024])
+def test_prefill_4096(prefill_4096, kind, m):
+    c, ws, q = prefill_4096
+    fmt = quant.FP8_E4M3_CH if kind == "fp8" else quant.I8_CH
+    for mat, n, k in synth.layer_shapes(c):
+        x = synth.act_normal(m, k, 3, salt=mat)
+        xq = torch.empty(m * k, dtype=torch.uint8, device="cuda")
+        sx = torch.empty(m, dtype=torch.float32, device="cuda")
+        say("prefill 4096", kind, synth.MAT_NAMES[mat], "m", m)
+        rq.rq_quantize_act(dev_f16(x), m, k, k, fmt, xq, sx)
+        y = torch.empty(m * n * 2, dtype=torch.uint8, device="cuda")
+        f = rq.rq_gemm_fp8 if kind == "fp8" else rq.rq_gemm_int8
+        f(xq, sx, m, q[kind][mat], y, n)
+        torch.cuda.synchronize()
+        # activation rows: sampled bytes; weight rows: sampled bytes
+        arows = _rows(m, 300 + mat)
+        px = quant.quantize_rows(x[arows], kind)
+        assert np.array_equal(host(xq, np.uint8).reshape(m, k)[arows], px["codes"].reshape(len(arows), k).view(np.uint8))
+        assert np.array_equal(host(sx, np.float32)[arows], px["scales"])
+        rows = _rows(n, 400 + mat)
+        pw = quant.quantize_rows(ws[mat][rows], kind)
+        qw = q[kind][mat]
+        assert np.array_equal(host(qw.codes, np.uint8)[: n * k].reshape(n, k)[rows],
+                              pw["codes"].reshape(len(rows), k).view(np.uint8))
+        assert np.array_equal(host(qw.scales, np.float32)[:n][rows], pw["scales"])
+        y_ref, b = ref.w8a8_ref(px["codes"], px["scales"], kind, fmt, pw)
+        got = host(y, np.float16).reshape(m, n)[np.ix_(arows, rows)]
+        ok, info = ref.compare(got, y_ref, b)
+        assert ok, (kind, synth.MAT_NAMES[mat], m, info)
+
+
+# --------------------------------------------------------------------------
+# width 4096 (13.3B) decode step: one layer's six matrices (every layer has
+# these shapes) at M in {1, 2, 4, 8, 16, 32}, and the fp16 head
+# --------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def layer_4096():
+    c = 4096
+    mats = {}
+    for mat, n, k in synth.layer_shapes(c):
+        w = synth.weight(4, 60, mat, n, k)
+        mats[mat] = (w, _gpu_weights(w, quant.W4_SYM, 64))
+    yield c, mats
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
+def test_decode_layer_4096(layer_4096, m):
+    c, mats = layer_4096
+    x = synth.act_normal(m, c, 4)
+    x4 = synth.act_normal(m, 4 * c, 4, salt=1)
+    xd, x4d = dev_f16(x), dev_f16(x4)
+    q = {mat: mats[mat][1] for mat in mats}
+    ys = {mat: torch.empty(m * n * 2, dtype=torch.uint8, device="cuda") for mat, n, _ in synth.layer_shapes(c)}
+    say("decode layer 4096 m", m)
+    rq.rq_fused_rkv(xd, xd, xd, m, c, q[synth.MAT_R], q[synth.MAT_K], q[synth.MAT_V],
+                    ys[synth.MAT_R], ys[synth.MAT_K], ys[synth.MAT_V], c)
+    rq.rq_gemm_small_m(xd, m, c, q[synth.MAT_O], ys[synth.MAT_O], c)
+    rq.rq_gemm_small_m(xd, m, c, q[synth.MAT_KEY], ys[synth.MAT_KEY], 4 * c)
+    rq.rq_gemm_small_m(x4d, m, 4 * c, q[synth.MAT_VALUE], ys[synth.MAT_VALUE], c)
+    torch.cuda.synchronize()
+    for mat, n, k in synth.layer_shapes(c):
+        rows = _rows(n, 500 + mat + m)
+        parts = _check_rows_sym(q[mat], mats[mat][0], rows, quant.W4_SYM, 64)
+        _compare_rows(host(ys[mat], np.float16).reshape(m, n), rows, x4 if k == 4 * c else x,
+                      quant.W4_SYM, parts, 64, synth.MAT_NAMES[mat])
+
+
+@pytest.mark.parametrize("m", [1, 32])
+def test_head_4096x65536(m):
+    n, k = 65536, 4096
+    w = synth.weight(4, 61, synth.MAT_HEAD, n, k)
+    qw = _gpu_weights(w, quant.F16, 0)
+    x = synth.act_normal(m, k, 4, salt=2)
+    y = torch.empty(m * n * 2, dtype=torch.uint8, device="cuda")
+    say("head m", m)
+    if m == 1:
+        rq.rq_gemv_f16(dev_f16(x), qw, y)
+    else:
+        rq.rq_gemm_small_m(dev_f16(x), m, k, qw, y, n)
+    torch.cuda.synchronize()
+    rows = _rows(n, 600)
+    parts = {"codes": w[rows].astype(np.float16)}
+    assert np.array_equal(host(qw.codes, np.uint16)[: n * k].reshape(n, k)[rows], parts["codes"].view(np.uint16))
+    _compare_rows(host(y, np.float16).reshape(m, n), rows, x, quant.F16, parts, 0, "head")

@@ -89,6 +89,26 @@ def test_quantize_subnormal_superblock_scales():
     _compare_buffers(qw, quant.W4_ASYM_SB256, parts)
 
 
+def test_quantize_signed_zero_superblocks():
+    # superblocks without negative weights, or of signed zeros: d and dmin
+    # are stored as +0 on both sides
+    g = np.random.default_rng(4)
+    w = np.zeros((4, 512), np.float32)
+    w[0] = np.abs(g.standard_normal(512)).astype(np.float32) + 0.25
+    w[1] = -0.0
+    w[2, :256] = -0.0
+    w[2, 256:] = g.standard_normal(256).astype(np.float32)
+    w[3, :32] = 0.0
+    w[3, 32:] = np.abs(g.standard_normal(480)).astype(np.float32)
+    parts = quant.quantize_sb256(w)
+    qw = _quantize_gpu(w, quant.W4_ASYM_SB256, 32)
+    _compare_buffers(qw, quant.W4_ASYM_SB256, parts)
+    # and the symmetric formats on signed zeros
+    for fmt, group in ((quant.W4_SYM, 32), (quant.W8_SYM, 64)):
+        parts = quant.quantize(w, fmt, group)
+        _compare_buffers(_quantize_gpu(w, fmt, group), fmt, parts)
+
+
 def test_quantize_errors():
     w = _weights(8, 128, seed=1)
     w[3, 5] = np.nan

@@ -288,6 +288,24 @@ def check_sb_roundtrip(seed, n=16, k=512):
     assert np.array_equal(quant.dequant_sb256(r["qs"], r["d"], r["dmin"], r["sub"]), w64)
 
 
+def test_sb256_zero_offsets_and_ranges_are_positive_zero():
+    # a superblock with no negative weight has every group offset 0 and a
+    # superblock of signed zeros has every range 0: d and dmin are magnitudes,
+    # so they store +0 (0x0000), and all sub-codes and codes are 0
+    w = np.zeros((3, 256), np.float32)
+    g = np.random.default_rng(4)
+    w[0] = np.abs(g.standard_normal(256)).astype(np.float32) + 0.25   # all positive
+    w[1] = -0.0                                                       # signed zeros
+    w[2, :32] = 0.0                                                   # one constant group
+    w[2, 32:] = np.abs(g.standard_normal(224)).astype(np.float32)
+    r = quant.quantize_sb256(w)
+    assert codecs.f16_bits(r["dmin"][0, 0]) == 0x0000
+    assert codecs.f16_bits(r["d"][1, 0]) == 0x0000 and codecs.f16_bits(r["dmin"][1, 0]) == 0x0000
+    assert codecs.f16_bits(r["dmin"][2, 0]) == 0x0000
+    assert not r["mc"].any()
+    assert not r["q"][1].any() and not r["sc"][1].any()
+
+
 def test_sb256_roundtrip():
     check_sb_roundtrip(seed=4)
 
