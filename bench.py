@@ -205,6 +205,58 @@ class Prefill:
         ]
 
 
+class Sweep:
+    """The 13.3B decode step: 61 width-4096 layers of int4 g64 projections
+    (fused R/K/V, O, cmix key, cmix value) and the fp16 65536x4096 head, all
+    resident (7.06 GB), one graph per batch size; the activations are reused
+    across layers (the step's data dependencies are not modelled)."""
+
+    LAYERS, C, VOCAB = 61, 4096, 65536
+
+    def __init__(self, gen, dev):
+        c = self.C
+        self.layers = []
+        for _ in range(self.LAYERS):
+            s = {}
+            for mat, n, k in synth.layer_shapes(c):
+                wf = torch.randn(n, k, generator=gen, device=dev, dtype=torch.float32) * (1.0 / k ** 0.5)
+                s[mat] = rq.quantize(wf, rq.RQ_W4_SYM, 64)
+                del wf
+            self.layers.append(s)
+        wf = torch.randn(self.VOCAB, c, generator=gen, device=dev, dtype=torch.float32) * (1.0 / c ** 0.5)
+        self.head = rq.quantize(wf, rq.RQ_F16)
+        del wf
+        torch.cuda.empty_cache()
+        self.weight_bytes = sum(q.nbytes() for s in self.layers for q in s.values()) + self.head.nbytes()
+        self.x = {}
+        self.y = {}
+
+    def step(self, m):
+        c = self.C
+        if m not in self.x:
+            self.x[m] = (f16_dev(synth.act_normal(m, c, 4), "cuda"), f16_dev(synth.act_normal(m, 4 * c, 4, salt=1), "cuda"))
+            self.y[m] = {nm: torch.empty(m * n, dtype=torch.int16, device="cuda")
+                         for nm, n in (("r", c), ("k", c), ("v", c), ("o", c), ("key", 4 * c), ("val", c),
+                                       ("head", self.VOCAB))}
+        x, x4 = self.x[m]
+        y = self.y[m]
+        for s in self.layers:
+            rq.rq_fused_rkv(x, x, x, m, c, s[synth.MAT_R], s[synth.MAT_K], s[synth.MAT_V], y["r"], y["k"], y["v"], c)
+            rq.rq_gemm_small_m(x, m, c, s[synth.MAT_O], y["o"], c)
+            rq.rq_gemm_small_m(x, m, c, s[synth.MAT_KEY], y["key"], 4 * c)
+            rq.rq_gemm_small_m(x4, m, 4 * c, s[synth.MAT_VALUE], y["val"], c)
+        rq.rq_gemm_small_m(x, m, c, self.head, y["head"], self.VOCAB)
+
+    def run(self, steps, warmup):
+        out = {}
+        for m in (1, 2, 4, 8, 16, 32):
+            g = capture(lambda m=m: self.step(m))
+            ms = time_graph(g, steps, warmup)
+            out[str(m)] = {"ms": round(ms, 4), "GB_s": round(self.weight_bytes / (ms * 1e-3) / 1e9, 1)}
+            del g
+        return out
+
+
 def class_graph(launch, sets):
     """One graph: the kernel class launched once per rotated weight copy."""
     return capture(lambda: [launch(s) for s in sets])
@@ -453,6 +505,7 @@ def main():
                     help="for counter runs: a calibration copy, then only the named kernel class "
                          "(default: the dominant one) replayed --steps times")
     ap.add_argument("--class-reps", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 13.3B decode-step sweep")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per kernel and launch shape: dispatches and mean duration, from a "
                          "rocprofv3 --kernel-trace CSV")
@@ -533,6 +586,19 @@ def main():
                           "pass_ms": round(float(per[-1]), 4)},
         "roofline": roofline(dom, traffic),
     }
+    if not args.no_sweep:
+        del graphs, rows
+        torch.cuda.empty_cache()
+        sw = Sweep(gen, dev)
+        res = sw.run(max(3, args.steps // 2), 2)
+        out["sweep_13b"] = {"workload": "61 x (fused R/K/V, O, cmix key, cmix value) int4 g64 at width 4096 "
+                                        "+ fp16 head 65536x4096, one graph of 245 launches per M",
+                            "weight_bytes": sw.weight_bytes, "per_m": res,
+                            "m1_hbm_peak_frac": round(res["1"]["GB_s"] / HBM_PEAK_GBS, 4)}
+        if args.phases:
+            for m, r in res.items():
+                print("sweep 13.3B M=%-2s %8.3f ms  %7.1f GB/s" % (m, r["ms"], r["GB_s"]), file=sys.stderr)
+        del sw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(C1)
     print(json.dumps(out))
