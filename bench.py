@@ -257,6 +257,121 @@ class Sweep:
         return out
 
 
+def measure_rows(gen, dev, reps=20):
+    """One measurement per row of the path that the step does not time: the
+    quantizers, the SB256 products (width 2560, M = 1, 4, 16), the int8 GEMM
+    (width 4096 prefill set, M = 256), the width-768 fused R/K/V call and the
+    fp16 head at M = 1.  Each is the mean of `reps` back-to-back launches in
+    a graph over distinct weight copies where the weights are large."""
+    out = {}
+
+    def graph_us(fn, n):
+        g = capture(fn)
+        return time_graph(g, reps) * 1e3 / n
+
+    # quantizers: fp32 bytes read per second
+    for name, fmt, group, (n, k) in (("rtn w4g64 8192x2048", rq.RQ_W4_SYM, 64, (8192, 2048)),
+                                     ("rtn sb256 10240x2560", rq.RQ_W4_ASYM_SB256, 32, (10240, 2560)),
+                                     ("rtn fp8 per-channel 16384x4096", rq.RQ_FP8_E4M3_CH, 0, (16384, 4096))):
+        wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
+        q = rq.QWeight.empty(fmt, group, n, k, device=dev)
+        rq.rq_quantize_rtn(wf, q)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            rq.rq_quantize_rtn(wf, q)  # synchronizes (reads back its status word)
+        us = (time.perf_counter() - t0) * 1e6 / 5
+        out[name] = {"us": round(us, 2), "GB_s_fp32_in": round(n * k * 4 / us / 1e3, 1)}
+        del wf, q
+    # SB256 products, width 2560, 32 copies of the set
+    c = 2560
+    sets = []
+    for _ in range(32):
+        sset = {}
+        for mat, n, k in ((synth.MAT_O, c, c), (synth.MAT_KEY, 4 * c, c), (synth.MAT_VALUE, c, 4 * c)):
+            wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
+            sset[mat] = rq.quantize(wf, rq.RQ_W4_ASYM_SB256, 32)
+            del wf
+        sets.append(sset)
+    for m in (1, 4, 16):
+        x = f16_dev(synth.act_massive(m, c), dev)
+        x4 = f16_dev(synth.act_massive(m, 4 * c), dev)
+        y = torch.empty(m * 4 * c, dtype=torch.int16, device=dev)
+
+        def sb_pass(m=m, x=x, x4=x4, y=y):
+            for sset in sets:
+                rq.rq_gemm_small_m(x, m, c, sset[synth.MAT_O], y, c)
+                rq.rq_gemm_small_m(x, m, c, sset[synth.MAT_KEY], y, 4 * c)
+                rq.rq_gemm_small_m(x4, m, 4 * c, sset[synth.MAT_VALUE], y, c)
+        us = graph_us(sb_pass, len(sets))
+        wb = sum(q.nbytes() for q in sets[0].values())
+        out["sb256 2560 set M=%d" % m] = {"us_per_set": round(us, 2), "GB_s": round(wb / us / 1e3, 1),
+                                           "hbm_peak_frac": round(wb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del sets
+    # int8 GEMM, width-4096 prefill set at M = 256, 6 copies
+    c, m = 4096, 256
+    isets = []
+    for _ in range(6):
+        iset = {}
+        for mat, n, k in synth.layer_shapes(c):
+            wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
+            iset[mat] = rq.quantize(wf, rq.RQ_I8_CH)
+            del wf
+        isets.append(iset)
+    xa = f16_dev(synth.act_normal(m, c, 3), dev)
+    xa4 = f16_dev(synth.act_normal(m, 4 * c, 3, salt=1), dev)
+    xq = torch.empty(m * c, dtype=torch.uint8, device=dev)
+    xq4 = torch.empty(m * 4 * c, dtype=torch.uint8, device=dev)
+    sx = torch.empty(m, dtype=torch.float32, device=dev)
+    sx4 = torch.empty(m, dtype=torch.float32, device=dev)
+    yp = torch.empty(m * 4 * c, dtype=torch.int16, device=dev)
+    rq.rq_quantize_act(xa, m, c, c, rq.RQ_I8_CH, xq, sx)
+    rq.rq_quantize_act(xa4, m, 4 * c, 4 * c, rq.RQ_I8_CH, xq4, sx4)
+
+    def i8_pass():
+        for iset in isets:
+            for mat in (synth.MAT_R, synth.MAT_K, synth.MAT_V, synth.MAT_O, synth.MAT_KEY):
+                rq.rq_gemm_int8(xq, sx, m, iset[mat], yp, iset[mat].n)
+            rq.rq_gemm_int8(xq4, sx4, m, iset[synth.MAT_VALUE], yp, c)
+    us = graph_us(i8_pass, len(isets))
+    flops = sum(2.0 * m * n * k for _, n, k in synth.layer_shapes(c))
+    out["int8 gemm 4096 set M=256"] = {"us_per_set": round(us, 2), "TOPS": round(flops / us / 1e6, 1),
+                                       "frac_of_peak": round(flops / us / 1e6 / FP8_PEAK_TFLOPS, 4)}
+    del isets
+    # width-768 fused R/K/V, w8g64, M = 1: 200 calls on distinct weight copies
+    # (365 MB) per graph, so the figure is the per-call device time
+    ws, x = synth.fused_rkv_768()
+    q0 = [rq.quantize(torch.from_numpy(w).to(dev), rq.RQ_W8_SYM, 64) for w in ws]
+    copies = []
+    for _ in range(200):
+        cq = []
+        for q in q0:
+            c_ = rq.QWeight.empty(q.format, q.group, q.n, q.k, device=dev)
+            c_.codes.copy_(q.codes)
+            c_.scales.copy_(q.scales)
+            cq.append(c_)
+        copies.append(cq)
+    xd = f16_dev(x, dev)
+    ys = [torch.empty(768, dtype=torch.int16, device=dev) for _ in range(3)]
+    us = graph_us(lambda: [rq.rq_fused_rkv(xd, xd, xd, 1, 768, *cq, *ys, 768) for cq in copies], len(copies))
+    wb = sum(q.nbytes() for q in q0)
+    out["fused rkv 768 w8g64 M=1"] = {"us": round(us, 2), "GB_s": round(wb / us / 1e3, 1)}
+    del copies
+    # fp16 head 65536 x 4096 at M = 1, two copies (1.07 GB) per graph
+    heads = []
+    for _ in range(2):
+        wf = torch.randn(65536, 4096, generator=gen, device=dev) * (1.0 / 64.0)
+        heads.append(rq.quantize(wf, rq.RQ_F16))
+        del wf
+    xh = f16_dev(synth.act_normal(1, 4096, 4), dev)
+    yh = torch.empty(65536, dtype=torch.int16, device=dev)
+    us = graph_us(lambda: [rq.rq_gemv_f16(xh, h, yh) for h in heads], len(heads))
+    hb = heads[0].nbytes()
+    out["head f16 65536x4096 M=1"] = {"us": round(us, 2), "GB_s": round(hb / us / 1e3, 1),
+                                      "hbm_peak_frac": round(hb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def class_graph(launch, sets):
     """One graph: the kernel class launched once per rotated weight copy."""
     return capture(lambda: [launch(s) for s in sets])
@@ -506,6 +621,7 @@ def main():
                          "(default: the dominant one) replayed --steps times")
     ap.add_argument("--class-reps", type=int, default=20)
     ap.add_argument("--no-sweep", action="store_true", help="skip the 13.3B decode-step sweep")
+    ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per kernel and launch shape: dispatches and mean duration, from a "
                          "rocprofv3 --kernel-trace CSV")
@@ -599,6 +715,12 @@ def main():
             for m, r in res.items():
                 print("sweep 13.3B M=%-2s %8.3f ms  %7.1f GB/s" % (m, r["ms"], r["GB_s"]), file=sys.stderr)
         del sw
+    if not args.no_rows:
+        torch.cuda.empty_cache()
+        out["rows"] = measure_rows(gen, dev)
+        if args.phases:
+            for name, r in out["rows"].items():
+                print("%-34s %s" % (name, r), file=sys.stderr)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(C1)
     print(json.dumps(out))

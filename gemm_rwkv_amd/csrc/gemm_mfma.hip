@@ -187,6 +187,148 @@ __global__ void __launch_bounds__(64 * KW) gemm_w8a8_kernel(const uint8_t* __res
   }
 }
 
+// Shared-ring variant for large grids: a 128 x 128 output tile per
+// workgroup, each of the four waves computing one 64 x 64 quadrant over all
+// of K.  The waves copy every k block cooperatively (each issues a quarter of
+// its whole-line LDS DMA reads, same swizzle as above) into a 4-stage ring
+// shared by the workgroup, so three blocks (96 KB) are in flight while one is
+// multiplied, and each block crosses L2 once per workgroup instead of once
+// per wave.  One barrier per block: after it every wave's part of block j
+// has landed and every wave is done with block j - 1, whose stage then
+// receives block j + 3.
+template <bool FP8>
+__global__ void __launch_bounds__(256) gemm_w8a8_ring_kernel(const uint8_t* __restrict__ xq,
+                                                             const float* __restrict__ sx, int M,
+                                                             const uint8_t* __restrict__ wq,
+                                                             const float* __restrict__ sw, int N, int K,
+                                                             uint16_t* __restrict__ y, int ldy,
+                                                             int32_t* __restrict__ acc_out) {
+  constexpr int BT = 128;                  // tile rows of x and of w
+  constexpr int SA = BT * 128;             // bytes of one operand's k block
+  constexpr int STAGE = 2 * SA;
+  constexpr int NB = 4;
+  constexpr int PER = 8;                   // DMA instructions per wave per block
+  typedef typename std::conditional<FP8, float4v, int4v>::type AccT;
+  extern __shared__ uint4 lds4[];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int q = lane >> 4;
+  const int m0 = blockIdx.y * BT;
+  const int n0 = blockIdx.x * BT;
+  const int nkb = K >> 7;
+  const int qm = wave >> 1, qn = wave & 1;  // this wave's quadrant
+
+  // this wave's DMA instructions: rows 8i .. 8i + 7 of x (i = 4w .. 4w + 3)
+  // and of w (same i)
+  const int drow = lane >> 3, dslot = lane & 7;
+  const uint8_t* asrc[4];
+  const uint8_t* bsrc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 8 * (4 * wave + u) + drow;
+    const int seg = (dslot ^ ((r >> 1) & 7)) << 4;
+    asrc[u] = xq + (size_t)min(m0 + r, M - 1) * K + seg;
+    bsrc[u] = wq + (size_t)min(n0 + r, N - 1) * K + seg;
+  }
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
+  auto dma = [&](int st, int kb) {
+    const uint32_t base = ring + st * STAGE + wave * 4 * 1024;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint8_t* g = asrc[u] + (size_t)kb * 128;
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(g), "s"(base + u * 1024) : "memory", "m0");
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint8_t* g = bsrc[u] + (size_t)kb * 128;
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(g), "s"(base + SA + u * 1024) : "memory", "m0");
+    }
+  };
+
+  const int swz = (r16 >> 1) & 7;
+  const int o0 = r16 * 128 + (((2 * q) ^ swz) << 4);
+  const int o1 = r16 * 128 + (((2 * q + 1) ^ swz) << 4);
+  const uint8_t* abase = (const uint8_t*)lds4 + qm * 64 * 128;
+  const uint8_t* bbase = (const uint8_t*)lds4 + SA + qn * 64 * 128;
+
+  AccT acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = AccT{0, 0, 0, 0};
+
+  auto compute = [&](int st) {
+    uint4 fa[4][2], fb[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      fa[a][0] = *(const uint4*)(abase + st * STAGE + a * 2048 + o0);
+      fa[a][1] = *(const uint4*)(abase + st * STAGE + a * 2048 + o1);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      fb[b][0] = *(const uint4*)(bbase + st * STAGE + b * 2048 + o0);
+      fb[b][1] = *(const uint4*)(bbase + st * STAGE + b * 2048 + o1);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint4 al = fa[a][0], ah = fa[a][1];
+        const uint4 bl = fb[b][0], bh = fb[b][1];
+        if constexpr (FP8) {
+          const int8v av = {(int)al.x, (int)al.y, (int)al.z, (int)al.w, (int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
+          const int8v bv = {(int)bl.x, (int)bl.y, (int)bl.z, (int)bl.w, (int)bh.x, (int)bh.y, (int)bh.z, (int)bh.w};
+          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[a][b], 0, 0, 0, 0, 0, 0);
+        } else {
+          const int4v a0 = {(int)al.x, (int)al.y, (int)al.z, (int)al.w};
+          const int4v b0 = {(int)bl.x, (int)bl.y, (int)bl.z, (int)bl.w};
+          const int4v a1 = {(int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
+          const int4v b1 = {(int)bh.x, (int)bh.y, (int)bh.z, (int)bh.w};
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[a][b], 0, 0, 0);
+        }
+      }
+  };
+
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (j < nkb) dma(j, j);
+  for (int j = 0; j < nkb; ++j) {
+    // this wave's DMAs of blocks after j that are already issued may stay in flight
+    const int ahead = min(NB - 2, nkb - 1 - j);
+    if (ahead >= 2)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PER) : "memory");
+    else if (ahead == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's part of block j is in; block j - 1 is done
+    if (j + NB - 1 < nkb) dma((j + NB - 1) % NB, j + NB - 1);
+    compute(j % NB);
+  }
+
+  // epilogue: lane holds D[m = 4q + r][n = r16] of each 16 x 16 block
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int n = n0 + qn * 64 + b * 16 + r16;
+    if (n >= N) continue;
+    const float swn = y ? sw[n] : 0.f;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + qm * 64 + a * 16 + 4 * q + r;
+        if (m >= M) continue;
+        if (acc_out) acc_out[(size_t)m * N + n] = (int32_t)acc[a][b][r];
+        if (y) y[(size_t)m * ldy + n] = f32_to_f16_bits((float)acc[a][b][r] * sx[m] * swn);
+      }
+  }
+}
+
 // Tile shape: the largest of 64x64, 32x64, 32x32, 16x32 that still gives at
 // least one workgroup per compute unit (256), else the smallest.
 // blockIdx.x runs over n, so with N / BN a multiple of 8 the workgroups that
@@ -194,6 +336,19 @@ __global__ void __launch_bounds__(64 * KW) gemm_w8a8_kernel(const uint8_t* __res
 template <bool FP8>
 static hipError_t launch_w8a8_t(const void* xq, const float* sx, int m, const void* wq, const float* sw,
                                 int n, int k, uint16_t* y, int ldy, int32_t* acc_out, hipStream_t st) {
+  // 128 x 128 tiles on a shared ring when they still make one workgroup per
+  // compute unit
+  if ((long)((m + 127) / 128) * (long)((n + 127) / 128) >= 256) {
+    constexpr size_t lds = (size_t)4 * 2 * 128 * 128;
+    static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w8a8_ring_kernel<FP8>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)lds) == hipSuccess;
+    (void)attr_set;
+    const dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));
+    hipLaunchKernelGGL((gemm_w8a8_ring_kernel<FP8>), grid, dim3(256), lds, st, (const uint8_t*)xq, sx, m,
+                       (const uint8_t*)wq, sw, n, k, y, ldy, acc_out);
+    return hipGetLastError();
+  }
   struct Shape {
     int tm, tn;
   };

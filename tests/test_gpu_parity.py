@@ -382,7 +382,10 @@ def _w8a8(fmt, kind, n, k, m, seed, ldy=None):
 @pytest.mark.parametrize("n,k,m", [(64, 256, 64), (100, 512, 37), (16, 128, 1), (257, 1024, 130),
                                    # large enough grids for each workgroup tile (64x64, 32x64,
                                    # 32x32), ragged in m and n, odd numbers of k blocks
-                                   (4100, 384, 250), (4100, 256, 120), (4000, 640, 100)])
+                                   (4100, 384, 250), (4100, 256, 120), (4000, 640, 100),
+                                   # 128x128 tiles on the shared 4-stage ring: ragged m and
+                                   # n, 3 k blocks; 2 k blocks; a single k block
+                                   (16300, 384, 250), (4100, 256, 1000), (4096, 128, 1024)])
 def test_w8a8_parity(kind, n, k, m):
     fmt = quant.FP8_E4M3_CH if kind == "fp8" else quant.I8_CH
     out, y_ref, b, xq, parts, qw = _w8a8(fmt, kind, n, k, m, seed=n + k + m, ldy=n + 8)
