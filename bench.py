@@ -543,7 +543,7 @@ def print_traffic(csvs, name, steps):
         print("%s_calibration: %s read %.0f KiB for the %d-byte copy (factor %.4f); %d dispatches after it: %s"
               % (label, ctr, calib / 1024, CALIB_BYTES, CALIB_BYTES / calib, ndisp, ", ".join(kernels)))
     print("launches: %d" % launches)
-    print("sources_sha256: %s" % sources_hash())
+    print("sources_sha256: %s" % sources_hash(name))
 
 
 def stored_traffic(name):
@@ -559,7 +559,7 @@ def stored_traffic(name):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("class") != name or fields.get("sources_sha256") != sources_hash():
+    if fields.get("class") != name or fields.get("sources_sha256") != sources_hash(name):
         return None
     try:
         return float(fields["bytes_per_launch"])
@@ -567,11 +567,20 @@ def stored_traffic(name):
         return None
 
 
-def sources_hash():
+def sources_hash(name):
+    """SHA-256 over the sources the kernel class `name` is built from: its own
+    kernel file plus the shared headers and the C-ABI layer that plans and
+    launches it.  A change to an unrelated kernel file leaves it unchanged."""
     import hashlib
+    if "gemm" in name:
+        own = "gemm_mfma.hip"
+    elif "quant" in name:
+        own = "quant.hip"
+    else:
+        own = "gemv.hip"
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_rwkv_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in sorted([own, "api.hip", "device_common.h", "kernels.h"]):
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(fn.encode() + b"\0" + f.read())
     return h.hexdigest()
