@@ -776,6 +776,15 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
   if (m < p.m && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
 }
 
+// Chunks per wave for a slice of `cps` chunks: a wave keeps CPW code loads in
+// flight and a workgroup is best at four to eight waves per row tile, so the
+// count grows with the slice (16 only for one activation tile and formats
+// whose per-chunk operands fit the registers without spilling).
+static int pick_cpw(int cps, bool allow16) {
+  if (cps >= 128 && allow16) return 16;
+  return cps >= 32 ? 8 : 4;
+}
+
 // Launch shape for gemv5_kernel, or false when none fits (activation slice
 // too large for LDS even at the finest split, or no workspace for a split).
 // Preference: the fewest slices that give at least one workgroup per compute
@@ -787,11 +796,14 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
   const int nchunks = b.k / F::CK;
   const int mt = b.m <= 16 ? 1 : 2;
   bool found = false;
+  // row tiles share a workgroup (and its activation slice) only where that
+  // slice is larger than the tile's codes, 16 rows x 64 bytes per chunk
+  const bool share_x = (b.m + 1) * F::CK * 2 > 16 * 64;
   // unsplit with a large activation slice, if that occupies at least half
   // of the compute units
   {
     const size_t xb = (size_t)(b.m + 1) * (nchunks * F::CK + 8) * 2;
-    const int cpw = nchunks <= 64 ? 4 : 8;
+    const int cpw = pick_cpw(nchunks, mt == 1 && FMT != GF_SB);
     const int wpt = (nchunks + cpw - 1) / cpw;
     int tiles = 0;
     for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
@@ -802,7 +814,12 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
         for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
         return g;
       };
-      while (rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) >= 128) rt *= 2;
+      // down to 256 workgroups; to 128 while each still fetches more than
+      // five times its codes' bytes of activations
+      auto x_heavy = [&](int r) { return xb > (size_t)5 * r * 16 * 64 * nchunks; };
+      while (share_x && rt < 4 && 2 * rt * wpt <= 16 &&
+             (groups(2 * rt) >= 256 || (groups(2 * rt) >= 128 && x_heavy(rt))))
+        rt *= 2;
       sp.split = 1;
       sp.cps = nchunks;
       sp.wpt = wpt;
@@ -823,7 +840,8 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
     if ((split - 1) * cps >= nchunks) continue;  // an empty slice
     const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
     if (xb > (size_t)kXBudget) continue;
-    const int cpw = cps <= 64 ? 4 : 8;
+    // from M = 3 on, a split slice does better with more waves of fewer chunks
+    const int cpw = b.m <= 2 ? pick_cpw(cps, FMT != GF_SB) : (cps <= 64 ? 4 : 8);
     const int wpt = (cps + cpw - 1) / cpw;
     if (wpt > 16) continue;
     int rt = 1;
@@ -832,8 +850,7 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
       for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
       return g;
     };
-    if (b.m > 1)
-      while (rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) * split >= 256) rt *= 2;
+    while (share_x && rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) * split >= 256) rt *= 2;
     if (split > 1 && (size_t)groups(rt) * rt * split * mt * 1024 > kGemvWsPartialBytes) break;
     sp.split = split;
     sp.cps = cps;
@@ -875,12 +892,20 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   } while (0)
   if (mt == 2) {
     if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
+  } else if constexpr (FMT == GF_SB) {
+    if (b.m == 1) {
+      if (cpw == 4) RQ_L5(1, 4, 1); else RQ_L5(1, 8, 1);
+    } else if (b.m == 2) {
+      if (cpw == 4) RQ_L5(1, 4, 2); else RQ_L5(1, 8, 2);
+    } else {
+      if (cpw == 4) RQ_L5(1, 4, 4); else RQ_L5(1, 8, 4);
+    }
   } else if (b.m == 1) {
-    if (cpw == 4) RQ_L5(1, 4, 1); else RQ_L5(1, 8, 1);
+    if (cpw == 4) RQ_L5(1, 4, 1); else if (cpw == 8) RQ_L5(1, 8, 1); else RQ_L5(1, 16, 1);
   } else if (b.m == 2) {
-    if (cpw == 4) RQ_L5(1, 4, 2); else RQ_L5(1, 8, 2);
+    if (cpw == 4) RQ_L5(1, 4, 2); else if (cpw == 8) RQ_L5(1, 8, 2); else RQ_L5(1, 16, 2);
   } else {
-    if (cpw == 4) RQ_L5(1, 4, 4); else RQ_L5(1, 8, 4);
+    if (cpw == 4) RQ_L5(1, 4, 4); else if (cpw == 8) RQ_L5(1, 8, 4); else RQ_L5(1, 16, 4);
   }
 #undef RQ_L5
   err = hipGetLastError();
