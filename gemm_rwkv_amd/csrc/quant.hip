@@ -158,6 +158,18 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float (&o)[4]
   o[3] = f16_bits_to_f32((uint16_t)(v.y >> 16));
 }
 
+// One code against the stored per-row scale s (a decoded fp32, here in fp64):
+// the fp64 quotient rounded onto the fp8 e4m3fn grid (saturating) or to a
+// clamped int8.  A zero scale gives code 0.
+template <bool FP8>
+__device__ __forceinline__ uint32_t row_code(float e, double s) {
+  if (s == 0.0) return 0u;
+  if (FP8) return f64_to_e4m3((double)e / s);
+  double q = __builtin_rint((double)e / s);
+  q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
+  return (uint32_t)((int)q & 0xff);
+}
+
 template <typename T, bool FP8>
 __global__ void __launch_bounds__(256) quant_rows_kernel(const T* __restrict__ in, int64_t k, int64_t ld,
                                                          uint32_t* __restrict__ codes,
@@ -192,20 +204,65 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const T* __restrict__ i
     load4<T>(r + 4 * i, e);
     uint32_t packed = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t c;
-      if (s == 0.0) {
-        c = 0;
-      } else if (FP8) {
-        c = f64_to_e4m3((double)e[j] / s);
-      } else {
-        double q = __builtin_rint((double)e[j] / s);
-        q = q > 127.0 ? 127.0 : (q < -127.0 ? -127.0 : q);
-        c = (uint32_t)((int)q & 0xff);
-      }
-      packed |= c << (8 * j);
-    }
+    for (int j = 0; j < 4; ++j) packed |= row_code<FP8>(e[j], s) << (8 * j);
     out[i] = packed;
+  }
+  if (threadIdx.x == 0) scales[row] = __builtin_bit_cast(float, sb);
+}
+
+// Per-token quantization of fp16 activations in one pass: a workgroup per
+// row, each thread loads its NL blocks of 8 halves at once and keeps them in
+// registers through the row's absmax reduction and the coding.  Same codes
+// and scales as quant_rows_kernel; rows of up to 2048 blocks (K <= 16384).
+template <bool FP8, int NL>
+__global__ void __launch_bounds__(1024) quant_act_kernel(const uint16_t* __restrict__ x, int k, int64_t ldx,
+                                                         uint2* __restrict__ codes,
+                                                         float* __restrict__ scales,
+                                                         int* __restrict__ flags) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const uint16_t* r = x + row * ldx;
+  const int blocks = k >> 3;
+  uint4 v[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int b = threadIdx.x + i * blockDim.x;
+    v[i] = b < blocks ? *(const uint4*)(r + 8 * b) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float a = 0.f;
+  bool fin = true;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e = f16_bits_to_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1))));
+      fin = fin && finite_f32(e);
+      a = fmaxf(a, fabsf(e));
+    }
+  }
+  if (!fin) raise_flag(flags, 0);
+  a = group_max<64>(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) a = fmaxf(a, red[w]);
+  const uint32_t sb = f64_to_f32_bits((double)a / (FP8 ? 448.0 : 127.0));
+  if (sb == 0x7f800000u) raise_flag(flags, 1);
+  const double s = (double)__builtin_bit_cast(float, sb);
+  uint2* out = codes + row * blocks;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int b = threadIdx.x + i * blockDim.x;
+    if (b >= blocks) continue;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= row_code<FP8>(f16_bits_to_f32((uint16_t)(w[j >> 1] >> (16 * (j & 1)))), s) << (8 * j);
+      hi |= row_code<FP8>(f16_bits_to_f32((uint16_t)(w[2 + (j >> 1)] >> (16 * (j & 1)))), s) << (8 * j);
+    }
+    out[b] = make_uint2(lo, hi);
   }
   if (threadIdx.x == 0) scales[row] = __builtin_bit_cast(float, sb);
 }
@@ -275,6 +332,24 @@ hipError_t launch_quant_rows_f32(const float* w, int64_t n, int64_t k, bool fp8,
 hipError_t launch_quant_rows_f16(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, bool fp8,
                                  void* codes, float* scales, int* flags, hipStream_t st) {
   if (m == 0) return hipSuccess;
+  const int64_t blocks = k / 8;
+  if (k % 8 == 0 && blocks <= 2048) {
+    const unsigned threads = blocks <= 256 ? 256u : (blocks <= 512 ? 512u : 1024u);
+    const dim3 grid((unsigned)m), block(threads);
+    uint2* c2 = (uint2*)codes;
+    if (blocks <= 1024) {
+      if (fp8)
+        hipLaunchKernelGGL((quant_act_kernel<true, 1>), grid, block, 0, st, x, (int)k, ldx, c2, scales, flags);
+      else
+        hipLaunchKernelGGL((quant_act_kernel<false, 1>), grid, block, 0, st, x, (int)k, ldx, c2, scales, flags);
+    } else {
+      if (fp8)
+        hipLaunchKernelGGL((quant_act_kernel<true, 2>), grid, block, 0, st, x, (int)k, ldx, c2, scales, flags);
+      else
+        hipLaunchKernelGGL((quant_act_kernel<false, 2>), grid, block, 0, st, x, (int)k, ldx, c2, scales, flags);
+    }
+    return hipGetLastError();
+  }
   if (fp8)
     hipLaunchKernelGGL((quant_rows_kernel<uint16_t, true>), dim3((unsigned)m), dim3(256), 0, st, x, k,
                        ldx, (uint32_t*)codes, scales, flags);

@@ -123,7 +123,11 @@ def test_quantize_errors():
 
 def test_quantize_act_bytes_exact():
     g = np.random.default_rng(9)
-    for m, k, ldx in [(1, 768, 768), (5, 4096, 4104), (64, 16384, 16384), (3, 16, 16)]:
+    # one-pass kernel: 256, 512 and 1024 threads per row, one or two blocks of
+    # 8 per thread (ragged last pass at K = 12304); the looping kernel beyond
+    # 2048 blocks (K = 16400)
+    for m, k, ldx in [(1, 768, 768), (5, 4096, 4104), (64, 16384, 16384), (3, 16, 16), (7, 8192, 8200),
+                      (4, 12304, 12304), (3, 16400, 16408), (2, 2064, 2064)]:
         x = (g.standard_normal((m, ldx)) * 10.0 ** g.uniform(-3, 2, (m, 1))).astype(np.float16)
         x[0, :4] = [0, -0.0, 65504, -1e-7]
         for fmt, kind in ((quant.FP8_E4M3_CH, "fp8"), (quant.I8_CH, "int8")):
