@@ -47,11 +47,13 @@ void fill_matrix(rq::GemvMatrix& g, const rq_qweight* w, const uint16_t* x, uint
   g.tiles = (int)((w->n + 15) / 16);
 }
 
-// Workspace of the K-split weight-streaming products (fp32 partial tiles),
-// one per (device, stream) so that products on different streams never share
-// it.  It is allocated on the first product on that stream.  During graph
-// capture nothing is allocated: a stream without a workspace runs unsplit
-// launch shapes (same results).
+// Workspace of the K-split products (fp32 or int32 partial tiles), one per
+// (device, stream) so that products on different streams never share it; on
+// one stream the kernels that use it run one after another.  It is allocated
+// on the first product on that stream.  During graph capture nothing is
+// allocated: a stream without a workspace runs unsplit launch shapes (same
+// results for the weight-streaming products; the dense GEMMs then sum K in
+// one workgroup, equal within rounding).
 struct Workspace {
   int dev;
   hipStream_t stream;
@@ -60,24 +62,21 @@ struct Workspace {
 std::mutex g_ws_mu;
 std::vector<Workspace> g_ws;
 
-void gemv_workspace(hipStream_t st, rq::GemvBatch& b) {
-  b.ws = nullptr;
+void* stream_workspace(hipStream_t st) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  for (const Workspace& w : g_ws) {
-    if (w.dev == dev && w.stream == st) {
-      b.ws = (float*)w.mem;
-      return;
-    }
-  }
+  for (const Workspace& w : g_ws)
+    if (w.dev == dev && w.stream == st) return w.mem;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
   void* mem = nullptr;
-  if (hipMalloc(&mem, rq::kGemvWsPartialBytes) != hipSuccess) return;
+  if (hipMalloc(&mem, rq::kGemvWsPartialBytes) != hipSuccess) return nullptr;
   g_ws.push_back(Workspace{dev, st, mem});
-  b.ws = (float*)mem;
+  return mem;
 }
+
+void gemv_workspace(hipStream_t st, rq::GemvBatch& b) { b.ws = (float*)stream_workspace(st); }
 
 // Shared path of the gemv entry points and rq_gemm_small_m.
 int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
@@ -133,7 +132,7 @@ int w8a8(const void* xq, const float* sx, int64_t m, const rq_qweight* w, uint16
   if (m == 0 || w->n == 0) return RQ_OK;
   return hip_status(rq::launch_gemm_w8a8(xq, sx, (int)m, w->codes, (const float*)w->scales, (int)w->n,
                                          (int)w->k, want_format == RQ_FP8_E4M3_CH, y, (int)ldy, acc,
-                                         S(stream)));
+                                         stream_workspace(S(stream)), rq::kGemvWsPartialBytes, S(stream)));
 }
 
 }  // namespace

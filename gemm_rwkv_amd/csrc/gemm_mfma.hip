@@ -188,26 +188,32 @@ __global__ void __launch_bounds__(64 * KW) gemm_w8a8_kernel(const uint8_t* __res
 }
 
 // Shared-ring variant for large grids: a 128 x 128 output tile per
-// workgroup, each of the four waves computing one 64 x 64 quadrant over all
-// of K.  The waves copy every k block cooperatively (each issues a quarter of
-// its whole-line LDS DMA reads, same swizzle as above) into a 4-stage ring
-// shared by the workgroup, so three blocks (96 KB) are in flight while one is
-// multiplied, and each block crosses L2 once per workgroup instead of once
-// per wave.  One barrier per block: after it every wave's part of block j
-// has landed and every wave is done with block j - 1, whose stage then
-// receives block j + 3.
-template <bool FP8>
-__global__ void __launch_bounds__(256) gemm_w8a8_ring_kernel(const uint8_t* __restrict__ xq,
-                                                             const float* __restrict__ sx, int M,
-                                                             const uint8_t* __restrict__ wq,
-                                                             const float* __restrict__ sw, int N, int K,
-                                                             uint16_t* __restrict__ y, int ldy,
-                                                             int32_t* __restrict__ acc_out) {
+// workgroup of NW waves, each computing a 64 x (128 / (NW / 2)) part of it over
+// the workgroup's k blocks.  The waves copy every k block cooperatively (each
+// issues 32 / NW of its whole-line LDS DMA reads, same swizzle as above) into
+// a 4-stage ring shared by the workgroup, so three blocks (96 KB) are in
+// flight while one is multiplied, and each block crosses L2 once per
+// workgroup instead of once per wave.  One barrier per block: after it every
+// wave's part of block j has landed and every wave is done with block j - 1,
+// whose stage then receives block j + 3.
+//
+// Split along K (part != null): workgroup z of gridDim.z takes k blocks
+// [z kbs, (z + 1) kbs) and stores its raw fp32 (int32) tile to part[z][m][n];
+// gemm_splitk_reduce_kernel then sums the slices in order and scales.
+template <bool FP8, int NW>
+__global__ void __launch_bounds__(64 * NW) gemm_w8a8_ring_kernel(const uint8_t* __restrict__ xq,
+                                                                 const float* __restrict__ sx, int M,
+                                                                 const uint8_t* __restrict__ wq,
+                                                                 const float* __restrict__ sw, int N, int K,
+                                                                 uint16_t* __restrict__ y, int ldy,
+                                                                 int32_t* __restrict__ acc_out, int kbs,
+                                                                 void* __restrict__ part) {
   constexpr int BT = 128;                  // tile rows of x and of w
   constexpr int SA = BT * 128;             // bytes of one operand's k block
   constexpr int STAGE = 2 * SA;
   constexpr int NB = 4;
-  constexpr int PER = 8;                   // DMA instructions per wave per block
+  constexpr int PER = 32 / NW;             // DMA instructions per wave per block
+  constexpr int TB = 8 / NW * 2;           // 16-column blocks of a wave's part (4 or 2)
   typedef typename std::conditional<FP8, float4v, int4v>::type AccT;
   extern __shared__ uint4 lds4[];
 
@@ -217,35 +223,30 @@ __global__ void __launch_bounds__(256) gemm_w8a8_ring_kernel(const uint8_t* __re
   const int q = lane >> 4;
   const int m0 = blockIdx.y * BT;
   const int n0 = blockIdx.x * BT;
-  const int nkb = K >> 7;
-  const int qm = wave >> 1, qn = wave & 1;  // this wave's quadrant
+  const int kb0 = blockIdx.z * kbs;
+  const int nkb = min(K >> 7, kb0 + kbs) - kb0;
+  const int qm = wave / (NW / 2), qn = wave % (NW / 2);  // 64-row half, column part
 
-  // this wave's DMA instructions: rows 8i .. 8i + 7 of x (i = 4w .. 4w + 3)
-  // and of w (same i)
+  // this wave's DMA instructions: instruction g = wave * PER + u of the 32 a
+  // block takes rows 8 (g % 16) .. + 7 of x (g < 16) or of w (g >= 16)
   const int drow = lane >> 3, dslot = lane & 7;
-  const uint8_t* asrc[4];
-  const uint8_t* bsrc[4];
+  const uint8_t* src[PER];
+  uint32_t dst[PER];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 8 * (4 * wave + u) + drow;
+  for (int u = 0; u < PER; ++u) {
+    const int g = wave * PER + u;
+    const int r = 8 * (g & 15) + drow;
     const int seg = (dslot ^ ((r >> 1) & 7)) << 4;
-    asrc[u] = xq + (size_t)min(m0 + r, M - 1) * K + seg;
-    bsrc[u] = wq + (size_t)min(n0 + r, N - 1) * K + seg;
+    src[u] = g < 16 ? xq + (size_t)min(m0 + r, M - 1) * K + seg : wq + (size_t)min(n0 + r, N - 1) * K + seg;
+    dst[u] = (g < 16 ? 0 : SA) + (g & 15) * 1024;
   }
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
   auto dma = [&](int st, int kb) {
-    const uint32_t base = ring + st * STAGE + wave * 4 * 1024;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint8_t* g = asrc[u] + (size_t)kb * 128;
+    for (int u = 0; u < PER; ++u) {
+      const uint8_t* g = src[u] + (size_t)(kb0 + kb) * 128;
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :: "v"(g), "s"(base + u * 1024) : "memory", "m0");
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint8_t* g = bsrc[u] + (size_t)kb * 128;
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                   :: "v"(g), "s"(base + SA + u * 1024) : "memory", "m0");
+                   :: "v"(g), "s"(ring + st * STAGE + dst[u]) : "memory", "m0");
     }
   };
 
@@ -253,30 +254,30 @@ __global__ void __launch_bounds__(256) gemm_w8a8_ring_kernel(const uint8_t* __re
   const int o0 = r16 * 128 + (((2 * q) ^ swz) << 4);
   const int o1 = r16 * 128 + (((2 * q + 1) ^ swz) << 4);
   const uint8_t* abase = (const uint8_t*)lds4 + qm * 64 * 128;
-  const uint8_t* bbase = (const uint8_t*)lds4 + SA + qn * 64 * 128;
+  const uint8_t* bbase = (const uint8_t*)lds4 + SA + qn * (16 * TB) * 128;
 
-  AccT acc[4][4];
+  AccT acc[4][TB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = AccT{0, 0, 0, 0};
+    for (int b = 0; b < TB; ++b) acc[a][b] = AccT{0, 0, 0, 0};
 
   auto compute = [&](int st) {
-    uint4 fa[4][2], fb[4][2];
+    uint4 fa[4][2], fb[TB][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       fa[a][0] = *(const uint4*)(abase + st * STAGE + a * 2048 + o0);
       fa[a][1] = *(const uint4*)(abase + st * STAGE + a * 2048 + o1);
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < TB; ++b) {
       fb[b][0] = *(const uint4*)(bbase + st * STAGE + b * 2048 + o0);
       fb[b][1] = *(const uint4*)(bbase + st * STAGE + b * 2048 + o1);
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+      for (int b = 0; b < TB; ++b) {
         const uint4 al = fa[a][0], ah = fa[a][1];
         const uint4 bl = fb[b][0], bh = fb[b][1];
         if constexpr (FP8) {
@@ -313,19 +314,53 @@ __global__ void __launch_bounds__(256) gemm_w8a8_ring_kernel(const uint8_t* __re
 
   // epilogue: lane holds D[m = 4q + r][n = r16] of each 16 x 16 block
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int n = n0 + qn * 64 + b * 16 + r16;
+  for (int b = 0; b < TB; ++b) {
+    const int n = n0 + qn * (16 * TB) + b * 16 + r16;
     if (n >= N) continue;
-    const float swn = y ? sw[n] : 0.f;
+    const float swn = (y && !part) ? sw[n] : 0.f;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + qm * 64 + a * 16 + 4 * q + r;
         if (m >= M) continue;
+        if (part) {
+          const size_t o = ((size_t)blockIdx.z * M + m) * N + n;
+          if constexpr (FP8)
+            ((float*)part)[o] = acc[a][b][r];
+          else
+            ((int32_t*)part)[o] = (int32_t)acc[a][b][r];
+          continue;
+        }
         if (acc_out) acc_out[(size_t)m * N + n] = (int32_t)acc[a][b][r];
         if (y) y[(size_t)m * ldy + n] = f32_to_f16_bits((float)acc[a][b][r] * sx[m] * swn);
       }
+  }
+}
+
+// Split K, second step: the slices' tiles summed in slice order (fp32 for
+// fp8, exact int32 for int8), then scaled, one thread per output.
+template <bool FP8>
+__global__ void __launch_bounds__(256) gemm_splitk_reduce_kernel(const void* __restrict__ part, int split,
+                                                                 const float* __restrict__ sx, int M,
+                                                                 const float* __restrict__ sw, int N,
+                                                                 uint16_t* __restrict__ y, int ldy,
+                                                                 int32_t* __restrict__ acc_out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t mn = (size_t)M * N;
+  if (i >= mn) return;
+  const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
+  if constexpr (FP8) {
+    const float* p = (const float*)part + i;
+    float v = p[0];
+    for (int z = 1; z < split; ++z) v += p[(size_t)z * mn];
+    y[(size_t)m * ldy + n] = f32_to_f16_bits(v * sx[m] * sw[n]);
+  } else {
+    const int32_t* p = (const int32_t*)part + i;
+    int32_t v = p[0];
+    for (int z = 1; z < split; ++z) v += p[(size_t)z * mn];
+    if (acc_out) acc_out[(size_t)m * N + n] = v;
+    if (y) y[(size_t)m * ldy + n] = f32_to_f16_bits((float)v * sx[m] * sw[n]);
   }
 }
 
@@ -334,20 +369,49 @@ __global__ void __launch_bounds__(256) gemm_w8a8_ring_kernel(const uint8_t* __re
 // blockIdx.x runs over n, so with N / BN a multiple of 8 the workgroups that
 // share a weight tile land on the same XCD (dispatch is round-robin over 8).
 template <bool FP8>
+static void launch_ring(const void* xq, const float* sx, int m, const void* wq, const float* sw, int n, int k,
+                        uint16_t* y, int ldy, int32_t* acc_out, int split, void* part, hipStream_t st) {
+  constexpr int NW = 8;
+  constexpr size_t lds = (size_t)4 * 2 * 128 * 128;
+  static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w8a8_ring_kernel<FP8, NW>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)lds) == hipSuccess;
+  (void)attr_set;
+  const int nkb = k >> 7;
+  const int kbs = (nkb + split - 1) / split;
+  const dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128), (unsigned)split);
+  hipLaunchKernelGGL((gemm_w8a8_ring_kernel<FP8, NW>), grid, dim3(64 * NW), lds, st, (const uint8_t*)xq, sx, m,
+                     (const uint8_t*)wq, sw, n, k, y, ldy, acc_out, kbs, part);
+}
+
+template <bool FP8>
 static hipError_t launch_w8a8_t(const void* xq, const float* sx, int m, const void* wq, const float* sw,
-                                int n, int k, uint16_t* y, int ldy, int32_t* acc_out, hipStream_t st) {
+                                int n, int k, uint16_t* y, int ldy, int32_t* acc_out, void* ws,
+                                size_t ws_bytes, hipStream_t st) {
   // 128 x 128 tiles on a shared ring when they still make one workgroup per
   // compute unit
-  if ((long)((m + 127) / 128) * (long)((n + 127) / 128) >= 256) {
-    constexpr size_t lds = (size_t)4 * 2 * 128 * 128;
-    static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w8a8_ring_kernel<FP8>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)lds) == hipSuccess;
-    (void)attr_set;
-    const dim3 grid((unsigned)((n + 127) / 128), (unsigned)((m + 127) / 128));
-    hipLaunchKernelGGL((gemm_w8a8_ring_kernel<FP8>), grid, dim3(256), lds, st, (const uint8_t*)xq, sx, m,
-                       (const uint8_t*)wq, sw, n, k, y, ldy, acc_out);
+  const long tiles128 = (long)((m + 127) / 128) * (long)((n + 127) / 128);
+  if (tiles128 >= 256) {
+    launch_ring<FP8>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, 1, nullptr, st);
     return hipGetLastError();
+  }
+  // fewer: split K over 2^s slices of at least 32 k blocks each until there
+  // are 256 workgroups, when the tiles are full in m and the partial tiles
+  // fit the workspace (shorter slices lose more to filling the ring and to
+  // the partial tiles than the larger tiles save)
+  {
+    const int nkb = k >> 7;
+    int split = 1;
+    while (tiles128 * split < 256 && nkb / (2 * split) >= 32) split *= 2;
+    if (m >= 128 && split > 1 && ws && (size_t)split * m * n * 4 <= ws_bytes) {
+      launch_ring<FP8>(xq, sx, m, wq, sw, n, k, nullptr, 0, nullptr, split, ws, st);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      const size_t outs = (size_t)m * n;
+      hipLaunchKernelGGL(gemm_splitk_reduce_kernel<FP8>, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st,
+                         (const void*)ws, split, sx, m, sw, n, y, ldy, acc_out);
+      return hipGetLastError();
+    }
   }
   struct Shape {
     int tm, tn;
@@ -388,11 +452,11 @@ static hipError_t launch_w8a8_t(const void* xq, const float* sx, int m, const vo
 }
 
 hipError_t launch_gemm_w8a8(const void* xq, const float* sx, int m, const void* wq, const float* sw,
-                            int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out,
-                            hipStream_t st) {
+                            int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out, void* ws,
+                            size_t ws_bytes, hipStream_t st) {
   if (m == 0 || n == 0) return hipSuccess;
-  if (fp8) return launch_w8a8_t<true>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, st);
-  return launch_w8a8_t<false>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, st);
+  if (fp8) return launch_w8a8_t<true>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, ws, ws_bytes, st);
+  return launch_w8a8_t<false>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, ws, ws_bytes, st);
 }
 
 }  // namespace rq

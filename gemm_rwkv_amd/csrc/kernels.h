@@ -48,8 +48,10 @@ constexpr size_t kGemvWsPartialBytes = 64u << 20;
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 
 // ---- MFMA GEMMs on per-row quantized operands (gemm_mfma.hip) ---------------
+// ws (may be null) is the stream's workspace of ws_bytes: shapes with fewer
+// than 256 output tiles of 128 x 128 split K and keep partial tiles there.
 hipError_t launch_gemm_w8a8(const void* xq, const float* sx, int m, const void* wq, const float* sw,
-                            int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out,
-                            hipStream_t st);
+                            int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out, void* ws,
+                            size_t ws_bytes, hipStream_t st);
 
 }  // namespace rq

@@ -389,7 +389,10 @@ def _w8a8(fmt, kind, n, k, m, seed, ldy=None):
                                    (4100, 384, 250), (4100, 256, 120), (4000, 640, 100),
                                    # 128x128 tiles on the shared 4-stage ring: ragged m and
                                    # n, 3 k blocks; 2 k blocks; a single k block
-                                   (16300, 384, 250), (4100, 256, 1000), (4096, 128, 1024)])
+                                   (16300, 384, 250), (4100, 256, 1000), (4096, 128, 1024),
+                                   # fewer than 256 such tiles: K split over 2 slices (65 k
+                                   # blocks: 33 + 32), 4 slices, 2 slices, ragged m and n
+                                   (260, 8320, 200), (300, 16384, 129), (600, 8192, 130)])
 def test_w8a8_parity(kind, n, k, m):
     fmt = quant.FP8_E4M3_CH if kind == "fp8" else quant.I8_CH
     out, y_ref, b, xq, parts, qw = _w8a8(fmt, kind, n, k, m, seed=n + k + m, ldy=n + 8)
