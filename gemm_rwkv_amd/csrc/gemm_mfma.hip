@@ -350,15 +350,22 @@ __global__ void __launch_bounds__(256) gemm_splitk_reduce_kernel(const void* __r
   const size_t mn = (size_t)M * N;
   if (i >= mn) return;
   const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
+  // every slice's load is issued before the first add (split <= 16)
+  uint32_t vals[16];
+  const uint32_t* p = (const uint32_t*)part + i;
+#pragma unroll
+  for (int z = 0; z < 16; ++z) vals[z] = z < split ? p[(size_t)z * mn] : 0u;
   if constexpr (FP8) {
-    const float* p = (const float*)part + i;
-    float v = p[0];
-    for (int z = 1; z < split; ++z) v += p[(size_t)z * mn];
+    float v = __builtin_bit_cast(float, vals[0]);
+#pragma unroll
+    for (int z = 1; z < 16; ++z)
+      if (z < split) v += __builtin_bit_cast(float, vals[z]);
     y[(size_t)m * ldy + n] = f32_to_f16_bits(v * sx[m] * sw[n]);
   } else {
-    const int32_t* p = (const int32_t*)part + i;
-    int32_t v = p[0];
-    for (int z = 1; z < split; ++z) v += p[(size_t)z * mn];
+    int32_t v = (int32_t)vals[0];
+#pragma unroll
+    for (int z = 1; z < 16; ++z)
+      if (z < split) v += (int32_t)vals[z];
     if (acc_out) acc_out[(size_t)m * N + n] = v;
     if (y) y[(size_t)m * ldy + n] = f32_to_f16_bits((float)v * sx[m] * sw[n]);
   }
@@ -402,7 +409,7 @@ static hipError_t launch_w8a8_t(const void* xq, const float* sx, int m, const vo
   {
     const int nkb = k >> 7;
     int split = 1;
-    while (tiles128 * split < 256 && nkb / (2 * split) >= 32) split *= 2;
+    while (tiles128 * split < 256 && nkb / (2 * split) >= 32 && split < 16) split *= 2;
     if (m >= 128 && split > 1 && ws && (size_t)split * m * n * 4 <= ws_bytes) {
       launch_ring<FP8>(xq, sx, m, wq, sw, n, k, nullptr, 0, nullptr, split, ws, st);
       hipError_t err = hipGetLastError();

@@ -758,13 +758,24 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
   constexpr int E = MT * 4 * 64;
   const int ent = sp.rt * E;
   const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
-  const int gi = blockIdx.x * 256 + threadIdx.x;
-  const int gall = gi / ent;
+  // ent is a multiple of 256, so a block lies inside one tile group
+  const int gall = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 256) / ent);
   if (gall >= gtot) return;
-  const int idx = gi - gall * ent;
-  const float* base = p.ws + (size_t)gall * sp.split * ent + idx;
-  float v = base[0];
-  for (int s2 = 1; s2 < sp.split; ++s2) v += base[(size_t)s2 * ent];
+  const int idx = (int)(blockIdx.x * 256 + threadIdx.x) - gall * ent;
+  // every slice's load is issued before the first add (slices past the split
+  // read zero through an out-of-range offset); the adds run in slice order
+  constexpr uint32_t kOOB = 0x7ffff000u;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.ws + (size_t)gall * sp.split * ent), (short)0, (int)(sp.split * ent * 4), 0x00020000);
+  float vals[16];
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2)
+    vals[s2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rw, (uint32_t)idx * 4u, s2 < sp.split ? (uint32_t)(s2 * ent) * 4u : kOOB, 0));
+  float v = vals[0];
+#pragma unroll
+  for (int s2 = 1; s2 < 16; ++s2)
+    if (s2 < sp.split) v += vals[s2];
   const int g0 = sp.groups[0], g1 = sp.groups[1];
   const bool in1 = gall >= g0, in2 = gall >= g0 + g1;
   const int grp = gall - (in2 ? g0 + g1 : (in1 ? g0 : 0));
