@@ -39,6 +39,7 @@ from gemm_rwkv_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+F16_PEAK_TFLOPS = 2500.0
 METRIC = "weight-stream GB/s (% HBM peak) W4g64 GEMV M=1..32; TFLOPS fp8 GEMM M=256"
 ROTATE_BYTES = 1 << 30
 C1, MS = 2048, (1, 8, 32)   # decode layer width, batches
@@ -338,6 +339,31 @@ def measure_rows(gen, dev, reps=20):
     out["int8 gemm 4096 set M=256"] = {"us_per_set": round(us, 2), "TOPS": round(flops / us / 1e6, 1),
                                        "frac_of_peak": round(flops / us / 1e6 / FP8_PEAK_TFLOPS, 4)}
     del isets
+    # int4 g64 prefill GEMM (rq_gemm_w4), width-4096 set at M = 64, 256, 1024,
+    # 6 copies (640 MB), fp16 activations
+    wsets = []
+    for _ in range(6):
+        wset = {}
+        for mat, n, k in synth.layer_shapes(c):
+            wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
+            wset[mat] = rq.quantize(wf, rq.RQ_W4_SYM, 64)
+            del wf
+        wsets.append(wset)
+    for m in (64, 256, 1024):
+        xa = f16_dev(synth.act_normal(m, c, 3), dev)
+        xa4 = f16_dev(synth.act_normal(m, 4 * c, 3, salt=1), dev)
+        yp = torch.empty(m * 4 * c, dtype=torch.int16, device=dev)
+
+        def w4_pass(m=m, xa=xa, xa4=xa4, yp=yp):
+            for wset in wsets:
+                for mat in (synth.MAT_R, synth.MAT_K, synth.MAT_V, synth.MAT_O, synth.MAT_KEY):
+                    rq.rq_gemm_w4(xa, m, c, wset[mat], yp, wset[mat].n)
+                rq.rq_gemm_w4(xa4, m, 4 * c, wset[synth.MAT_VALUE], yp, c)
+        us = graph_us(w4_pass, len(wsets))
+        flops = sum(2.0 * m * n * k for _, n, k in synth.layer_shapes(c))
+        out["int4 g64 gemm 4096 set M=%d" % m] = {"us_per_set": round(us, 2), "TFLOPS": round(flops / us / 1e6, 1),
+                                                  "frac_of_fp16_peak": round(flops / us / 1e6 / F16_PEAK_TFLOPS, 4)}
+    del wsets
     # width-768 fused R/K/V, w8g64, M = 1: 200 calls on distinct weight copies
     # (365 MB) per graph, so the figure is the per-call device time
     ws, x = synth.fused_rkv_768()

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librq.so")
 
-SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm_mfma.hip", "validate.cpp"]
+SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm_mfma.hip", "gemm_w4.hip", "validate.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

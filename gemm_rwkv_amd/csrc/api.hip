@@ -107,6 +107,34 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   return hip_status(rq::launch_gemv(b, gf, w->group, S(stream)));
 }
 
+// rq_gemm_w4: symmetric int4 codes, any m.
+int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
+            void* stream) {
+  int st = rqv::check_weight(w);
+  if (st != RQ_OK) return st;
+  if (w->format != RQ_W4_SYM) return RQ_ERR_FORMAT;
+  if (w->k % 128 != 0) return RQ_ERR_SHAPE;
+  if (m < 0 || m >= rqv::kMaxDim) return RQ_ERR_SHAPE;
+  if ((st = rqv::check_act(x, m, w->k, ldx)) != RQ_OK) return st;
+  if ((st = rqv::check_out(y, m, w->n, ldy)) != RQ_OK) return st;
+  Span ins[5];
+  rqv::weight_spans(w, ins);
+  ins[4] = rqv::act_span(x, m, w->k, ldx, 2);
+  if ((st = check_alias_out(rqv::act_span(y, m, w->n, ldy, 2), ins, 5)) != RQ_OK) return st;
+  if (m == 0 || w->n == 0) return RQ_OK;
+  rq::W4Gemm p;
+  p.x = x;
+  p.codes = (const uint8_t*)w->codes;
+  p.scales = (const uint16_t*)w->scales;
+  p.y = y;
+  p.m = (int)m;
+  p.n = (int)w->n;
+  p.k = (int)w->k;
+  p.ldx = (int)ldx;
+  p.ldy = (int)ldy;
+  return hip_status(rq::launch_gemm_w4(p, w->group, S(stream)));
+}
+
 int w8a8(const void* xq, const float* sx, int64_t m, const rq_qweight* w, uint16_t* y, int64_t ldy,
          int32_t* acc, void* stream, int want_format) {
   int st = rqv::check_weight(w);
@@ -291,6 +319,11 @@ int rq_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int fo
   if (m == 0) return RQ_OK;
   return hip_status(
       rq::launch_quant_rows_f16(x, m, k, ldx, format == RQ_FP8_E4M3_CH, xq, sx, nullptr, S(stream)));
+}
+
+int rq_gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
+               void* stream) {
+  return gemm_w4(x, m, ldx, w, y, ldy, stream);
 }
 
 int rq_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, const rq_qweight* w, uint16_t* y,

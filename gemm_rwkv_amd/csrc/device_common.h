@@ -117,6 +117,38 @@ __device__ __forceinline__ bool finite_f32(float f) {
   return (__builtin_bit_cast(uint32_t, f) & 0x7f800000u) != 0x7f800000u;
 }
 
+// ---- int4 code decoding (weight-streaming products and the int4 GEMM) ----
+
+// packed fp16 pair a - b
+__device__ __forceinline__ uint32_t hsub2(uint32_t a, uint32_t b) {
+  half2v r = __builtin_bit_cast(half2v, a) - __builtin_bit_cast(half2v, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// (v & m) | o in one instruction (v_bitop3_b32, truth table 0xEA)
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t o) {
+  return __builtin_amdgcn_bitop3_b32(v, m, o, 0xEA);
+}
+
+// One int4 code word (8 consecutive k: even k in nibbles 0..3 of the low
+// half-word, odd k in those of the high half-word) -> fp16 (u - bias) for
+// k = 0..7 in natural order.  Nibbles 0 and 2 of both halves land in the
+// mantissa of 1024 (ulp 1), nibbles 1 and 3 in that of 64 (ulp 1/16), so each
+// pair (2i, 2i + 1) is one AND-OR and one packed subtract of the bias:
+// 1032 / 72 for offset-binary symmetric codes (u = q + 8), 1024 / 64 for the
+// unsigned superblock codes.
+template <bool SIGNED>
+__device__ __forceinline__ half8 dec4n(uint32_t v) {
+  const uint32_t blo = SIGNED ? 0x64086408u : 0x64006400u;  // 1032 : 1024
+  const uint32_t bhi = SIGNED ? 0x54805480u : 0x54005400u;  // 72 : 64
+  const uint32_t v8 = v >> 8;
+  const uint32_t h0 = hsub2(and_or(v, 0x000f000fu, 0x64006400u), blo);
+  const uint32_t h1 = hsub2(and_or(v, 0x00f000f0u, 0x54005400u), bhi);
+  const uint32_t h2 = hsub2(and_or(v8, 0x000f000fu, 0x64006400u), blo);
+  const uint32_t h3 = hsub2(and_or(v8, 0x00f000f0u, 0x54005400u), bhi);
+  return __builtin_bit_cast(half8, make_uint4(h0, h1, h2, h3));
+}
+
 // Butterfly reductions over aligned groups of `width` lanes (power of two).
 template <int width>
 __device__ __forceinline__ float group_max(float v) {

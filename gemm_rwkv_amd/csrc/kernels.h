@@ -47,6 +47,18 @@ constexpr size_t kGemvWsPartialBytes = 64u << 20;
 
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 
+// ---- prefill products on int4 codes, any m (gemm_w4.hip) --------------------
+struct W4Gemm {
+  const uint16_t* x;       // fp16 [m][ldx]
+  const uint8_t* codes;    // [n][k/2]
+  const uint16_t* scales;  // fp16 [n][k/group]
+  uint16_t* y;             // fp16 [m][ldy]
+  int m, n, k, ldx, ldy;
+};
+
+// symmetric int4, group 16, 32 or 64; k % 128 == 0
+hipError_t launch_gemm_w4(const W4Gemm& p, int group, hipStream_t st);
+
 // ---- MFMA GEMMs on per-row quantized operands (gemm_mfma.hip) ---------------
 // ws (may be null) is the stream's workspace of ws_bytes: shapes with fewer
 // than 256 output tiles of 128 x 128 split K and keep partial tiles there.

@@ -36,6 +36,7 @@ EXPORTS = (
     "rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16", "rq_gemv_w8g32",
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
+    "rq_gemm_w4",
 )
 
 
@@ -69,6 +70,7 @@ def lib():
             "rq_qweight_bytes": ([i32, i32, i64, i64] + [ctypes.POINTER(ctypes.c_size_t)] * 4, i32),
             "rq_quantize_rtn": ([vp, qp, vp], i32),
             "rq_gemm_small_m": ([vp, i64, i64, qp, vp, i64, vp], i32),
+            "rq_gemm_w4": ([vp, i64, i64, qp, vp, i64, vp], i32),
             "rq_fused_rkv": ([vp, vp, vp, i64, i64, qp, qp, qp, vp, vp, vp, i64, vp], i32),
             "rq_quantize_act": ([vp, i64, i64, i64, i32, vp, vp, vp], i32),
             "rq_gemm_fp8": ([vp, vp, i64, qp, vp, i64, vp], i32),
@@ -210,6 +212,13 @@ def rq_gemm_small_m(x, m, ldx, w, y, ldy, stream=None):
     d = w.desc()
     st = lib().rq_gemm_small_m(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, _stream(stream))
     _check(st, "rq_gemm_small_m")
+    return y
+
+
+def rq_gemm_w4(x, m, ldx, w, y, ldy, stream=None):
+    d = w.desc()
+    st = lib().rq_gemm_w4(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, _stream(stream))
+    _check(st, "rq_gemm_w4")
     return y
 
 

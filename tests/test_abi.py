@@ -142,6 +142,24 @@ def test_small_m_and_fused_validation():
     rq.rq_fused_rkv(x, x, x, 0, 128, w, w2, w3, *ys, 32)  # m == 0, shared x: valid no-op
 
 
+def test_gemm_w4_validation():
+    w = _w(rq.RQ_W4_SYM, 64, 32, 256, A, B)
+    x, y = C, C + 0x100000
+    assert _status(rq.rq_gemm_w4, x, 4, 256, _w(rq.RQ_W8_SYM, 64, 32, 256, A, B), y, 32) == rq.RQ_ERR_FORMAT
+    assert _status(rq.rq_gemm_w4, x, 4, 256, _w(rq.RQ_FP8_E4M3_CH, 0, 32, 256, A, B), y, 32) == rq.RQ_ERR_FORMAT
+    assert _status(rq.rq_gemm_w4, x, 4, 192, _w(rq.RQ_W4_SYM, 64, 32, 192, A, B), y, 32) == rq.RQ_ERR_SHAPE
+    assert _status(rq.rq_gemm_w4, x, -1, 256, w, y, 32) == rq.RQ_ERR_SHAPE
+    assert _status(rq.rq_gemm_w4, x, 4, 248, w, y, 32) == rq.RQ_ERR_SHAPE     # ldx < k
+    assert _status(rq.rq_gemm_w4, x, 4, 260, w, y, 32) == rq.RQ_ERR_ALIGN     # ldx % 8
+    assert _status(rq.rq_gemm_w4, x, 4, 256, w, y, 31) == rq.RQ_ERR_SHAPE     # ldy < n
+    assert _status(rq.rq_gemm_w4, 0, 4, 256, w, y, 32) == rq.RQ_ERR_NULL
+    assert _status(rq.rq_gemm_w4, x + 8, 4, 256, w, y, 32) == rq.RQ_ERR_ALIGN
+    assert _status(rq.rq_gemm_w4, x, 4, 256, w, A + 0x10, 32) == rq.RQ_ERR_ALIAS
+    assert _status(rq.rq_gemm_w4, x, 4, 256, w, x, 32) == rq.RQ_ERR_ALIAS
+    rq.rq_gemm_w4(x, 0, 256, w, y, 32)                   # m == 0: no-op
+    rq.rq_gemm_w4(x, 4, 256, _w(rq.RQ_W4_SYM, 64, 0, 256, A, B), y, 32)  # n == 0: no-op
+
+
 def test_quantize_and_gemm_validation():
     qw = _w(rq.RQ_W4_SYM, 64, 16, 128)
     assert _status(rq.rq_quantize_rtn, 0, qw) == rq.RQ_ERR_NULL

@@ -181,6 +181,38 @@ def test_prefill_4096(prefill_4096, kind, m):
 
 
 # --------------------------------------------------------------------------
+# width 4096 (7.2B) prefill set on int4 g64 codes (rq_gemm_w4), M in
+# {64, 256, 1024}
+# --------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def prefill_w4_4096():
+    c = 4096
+    mats = {}
+    for mat, n, k in synth.layer_shapes(c):
+        w = synth.weight(3, 10, mat, n, k)
+        mats[mat] = (w, _gpu_weights(w, quant.W4_SYM, 64))
+    yield c, mats
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [64, 256, 1024])
+def test_prefill_w4_4096(prefill_w4_4096, m):
+    c, mats = prefill_w4_4096
+    for mat, n, k in synth.layer_shapes(c):
+        x = synth.act_normal(m, k, 3, salt=20 + mat)
+        y = torch.empty(m * n * 2, dtype=torch.uint8, device="cuda")
+        say("prefill w4 4096", synth.MAT_NAMES[mat], "m", m)
+        rq.rq_gemm_w4(dev_f16(x), m, k, mats[mat][1], y, n)
+        torch.cuda.synchronize()
+        rows = _rows(n, 700 + mat + m)
+        parts = _check_rows_sym(mats[mat][1], mats[mat][0], rows, quant.W4_SYM, 64)
+        _compare_rows(host(y, np.float16).reshape(m, n), rows, x, quant.W4_SYM, parts, 64,
+                      synth.MAT_NAMES[mat])
+
+
+# --------------------------------------------------------------------------
 # width 4096 (13.3B) decode step: one layer's six matrices (every layer has
 # these shapes) at M in {1, 2, 4, 8, 16, 32}, and the fp16 head
 # --------------------------------------------------------------------------
