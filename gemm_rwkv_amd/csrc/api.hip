@@ -132,7 +132,8 @@ int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   p.k = (int)w->k;
   p.ldx = (int)ldx;
   p.ldy = (int)ldy;
-  return hip_status(rq::launch_gemm_w4(p, w->group, S(stream)));
+  return hip_status(rq::launch_gemm_w4(p, w->group, (float*)stream_workspace(S(stream)),
+                                       rq::kGemvWsPartialBytes, S(stream)));
 }
 
 int w8a8(const void* xq, const float* sx, int64_t m, const rq_qweight* w, uint16_t* y, int64_t ldy,

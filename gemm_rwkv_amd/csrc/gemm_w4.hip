@@ -8,9 +8,12 @@
 // written out.  The one rounding beyond fp32 summation is that of q * s to
 // fp16 (q has 3 significant bits, s 11), at most 2^-12 of each weight.
 //
-// A workgroup of four waves computes a BM x BN output tile (BM, BN in
-// {64, 128}); each wave computes a (BM / 2) x (BN / 2) quarter as 16 x 16
-// v_mfma_f32_16x16x32_f16 tiles over all of K.  K runs in blocks of 128.  For
+// A workgroup of four waves computes a BM x BN output tile; the waves form a
+// WM x (4 / WM) grid and each computes its (BM / WM) x (BN * WM / 4) part as
+// 16 x 16 v_mfma_f32_16x16x32_f16 tiles over the workgroup's k blocks.  With
+// WM = 1 no two waves decode the same codes.  Split along K (part != null),
+// workgroup z of gridDim.z takes k blocks [z kbs, (z + 1) kbs) and stores its
+// fp32 tile to part[z][m][n]; gemm_w4_reduce_kernel adds the slices in order.  K runs in blocks of 128.  For
 // each block the x rows (BM x 256 bytes, whole 128-byte lines) and the code
 // rows (BN x 64 bytes) are copied by LDS DMA into a 3-stage ring shared by
 // the workgroup, so two blocks are in flight while one is multiplied; one
@@ -38,9 +41,10 @@
 
 namespace rq {
 
-template <int G, int BM, int BN>
-__global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p) {
-  constexpr int TM = BM / 32, TN = BN / 32;   // 16 x 16 tiles of a wave in m and n
+template <int G, int BM, int BN, int WM>
+__global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p, int kbs, float* __restrict__ part) {
+  constexpr int WN = 4 / WM;
+  constexpr int TM = BM / (16 * WM), TN = BN / (16 * WN);  // 16 x 16 tiles of a wave in m and n
   constexpr int D = 64 / G;                   // scale dwords per row and block
   constexpr int SX = BM * 256, SC = BN * 64, SS = BN * 4 * D, STAGE = SX + SC + SS;
   constexpr int NB = 3;
@@ -55,11 +59,12 @@ __global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p) {
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int q = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int m0 = blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
   const int M = p.m, N = p.n, K = p.k;
-  const int nkb = K >> 7;
+  const int kb0 = blockIdx.z * kbs;
+  const int nkb = min(K >> 7, kb0 + kbs) - kb0;  // this workgroup's k blocks
 
   // DMA sources.  x instruction g (0 .. BM/4 - 1) copies rows 4g .. 4g + 3:
   // lane -> row 4g + lane / 16, slot lane % 16.  Code instruction g
@@ -73,14 +78,14 @@ __global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p) {
   for (int u = 0; u < XPW; ++u) {
     const int r = 4 * (wave * XPW + u) + (lane >> 4);
     const int seg = (lane & 15) ^ (r & 15);
-    xsrc[u] = p.x + (size_t)min(m0 + r, M - 1) * p.ldx + seg * 8;
+    xsrc[u] = p.x + (size_t)min(m0 + r, M - 1) * p.ldx + (size_t)kb0 * 128 + seg * 8;
   }
   const size_t crow = (size_t)(K >> 1);
 #pragma unroll
   for (int u = 0; u < CPW; ++u) {
     const int r = 16 * (wave * CPW + u) + (lane >> 2);
     const int seg = (lane & 3) ^ ((r >> 2) & 3);
-    csrc[u] = p.codes + (size_t)min(n0 + r, N - 1) * crow + seg * 16;
+    csrc[u] = p.codes + (size_t)min(n0 + r, N - 1) * crow + (size_t)kb0 * 64 + seg * 16;
   }
   const size_t srow = (size_t)(K / G) * 2;  // scale bytes per row
 #pragma unroll
@@ -88,7 +93,8 @@ __global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p) {
     const int i = u * 64 + lane;             // dword of this wave's share
     const int t = wave * SDW + i;
     sact[u] = i < SDW;
-    ssrc[u] = (const uint8_t*)p.scales + (size_t)min(n0 + t / D, N - 1) * srow + (t % D) * 4;
+    ssrc[u] = (const uint8_t*)p.scales + (size_t)min(n0 + t / D, N - 1) * srow + (size_t)kb0 * (4 * D) +
+              (t % D) * 4;
   }
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
 
@@ -129,7 +135,7 @@ __global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p) {
     half8 s01[TN], s23[TN];  // the lane's scale for steps 0-1 and 2-3, broadcast
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
-      const int row = wn * (BN / 2) + 16 * b + r16;
+      const int row = wn * (BN / WN) + 16 * b + r16;
       cw[b] = *(const uint4*)(cs + row * 64 + ((q ^ ((row >> 2) & 3)) << 4));
       // group of k = 32 q + 8 s within the block: g64 -> q / 2, g32 -> q, g16 -> 2 q + s / 2
       _Float16 lo, hi;
@@ -154,7 +160,7 @@ __global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p) {
       }
 #pragma unroll
       for (int a = 0; a < TM; ++a) {
-        const int row = wm * (BM / 2) + 16 * a + r16;
+        const int row = wm * (BM / WM) + 16 * a + r16;
         const half8 af = *(const half8*)(xs + row * 256 + (((4 * q + s) ^ (row & 15)) << 4));
 #pragma unroll
         for (int b = 0; b < TN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b], acc[a][b], 0, 0, 0);
@@ -180,46 +186,108 @@ __global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p) {
   // epilogue: lane holds D[m = 4q + r][n = r16] of each 16 x 16 tile
 #pragma unroll
   for (int b = 0; b < TN; ++b) {
-    const int n = n0 + wn * (BN / 2) + 16 * b + r16;
+    const int n = n0 + wn * (BN / WN) + 16 * b + r16;
     if (n >= N) continue;
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * (BM / 2) + 16 * a + 4 * q + r;
-        if (m < M) p.y[(size_t)m * p.ldy + n] = f32_to_f16_bits(acc[a][b][r]);
+        const int m = m0 + wm * (BM / WM) + 16 * a + 4 * q + r;
+        if (m >= M) continue;
+        if (part)
+          part[((size_t)blockIdx.z * M + m) * N + n] = acc[a][b][r];
+        else
+          p.y[(size_t)m * p.ldy + n] = f32_to_f16_bits(acc[a][b][r]);
       }
   }
 }
 
-template <int G, int BM, int BN>
-static hipError_t launch_w4_t(const W4Gemm& p, hipStream_t st) {
+// Split K, second step: y = fp16 of the slices' fp32 tiles added in slice
+// order, one thread per output; every slice's load is issued before the
+// first add (split <= 16).
+__global__ void __launch_bounds__(256) gemm_w4_reduce_kernel(const float* __restrict__ part, int split,
+                                                             const W4Gemm p) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t mn = (size_t)p.m * p.n;
+  if (i >= mn) return;
+  const int m = (int)(i / p.n), n = (int)(i - (size_t)m * p.n);
+  float vals[16];
+#pragma unroll
+  for (int z = 0; z < 16; ++z) vals[z] = z < split ? part[(size_t)z * mn + i] : 0.f;
+  float v = vals[0];
+#pragma unroll
+  for (int z = 1; z < 16; ++z)
+    if (z < split) v += vals[z];
+  p.y[(size_t)m * p.ldy + n] = f32_to_f16_bits(v);
+}
+
+template <int G, int BM, int BN, int WM>
+static hipError_t launch_w4_t(const W4Gemm& p, int split, float* part, hipStream_t st) {
   constexpr size_t lds = (size_t)3 * (BM * 256 + BN * 64 + BN * 256 / G);
-  static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w4_kernel<G, BM, BN>,
+  static_assert(lds <= 160 * 1024, "ring fits LDS");
+  static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w4_kernel<G, BM, BN, WM>,
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    (int)lds) == hipSuccess;
   (void)attr_set;
-  const dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM));
-  hipLaunchKernelGGL((gemm_w4_kernel<G, BM, BN>), grid, dim3(256), lds, st, p);
+  const int nkb = p.k >> 7;
+  const int kbs = (nkb + split - 1) / split;
+  const dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM), (unsigned)split);
+  hipLaunchKernelGGL((gemm_w4_kernel<G, BM, BN, WM>), grid, dim3(256), lds, st, p, kbs, split > 1 ? part : nullptr);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || split == 1) return err;
+  const size_t outs = (size_t)p.m * p.n;
+  hipLaunchKernelGGL(gemm_w4_reduce_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st,
+                     (const float*)part, split, p);
   return hipGetLastError();
 }
 
-// Tile: 128 x 128 when m > 64 and that gives one workgroup per compute unit
-// (256), else 64 x 128 when that does, else 64 x 64.
-template <int G>
-static hipError_t launch_w4_g(const W4Gemm& p, hipStream_t st) {
-  const long mt128 = (p.m + 127) / 128, mt64 = (p.m + 63) / 64;
-  const long nt128 = (p.n + 127) / 128;
-  if (p.m > 64 && mt128 * nt128 >= 256) return launch_w4_t<G, 128, 128>(p, st);
-  if (mt64 * nt128 >= 256) return launch_w4_t<G, 64, 128>(p, st);
-  return launch_w4_t<G, 64, 64>(p, st);
+// Launch plan, from measurements of the width-4096 shapes at m = 64, 256 and
+// 1024.  Tiles in order of activation + code traffic per output,
+// K (2 / BN + 1 / (2 BM)) bytes: 128 x 256, 64 x 256, 128 x 128, 64 x 128,
+// 64 x 64 (128-row tiles only for m > 64).  Up to 32 k blocks (K <= 4096),
+// the first tile that makes 256 workgroups unsplit; otherwise, and for longer
+// K, the first that makes 256 with K split in 2, 4 or 8 slices of at least 8
+// k blocks (partial tiles in the workspace); failing both, 64 x 64 split as
+// far as that allows.
+struct W4Plan {
+  int bm, bn, wm, split;
+};
+
+static W4Plan plan_w4(const W4Gemm& p, size_t ws_bytes) {
+  static const W4Plan tiles[] = {{128, 256, 1, 1}, {64, 256, 1, 1}, {128, 128, 2, 1}, {64, 128, 2, 1}, {64, 64, 2, 1}};
+  const int nkb = p.k >> 7;
+  auto wgs = [&](const W4Plan& t) { return (long)((p.m + t.bm - 1) / t.bm) * (long)((p.n + t.bn - 1) / t.bn); };
+  auto split_ok = [&](int split) {
+    return nkb / split >= 8 && (size_t)split * p.m * p.n * 4 <= ws_bytes;
+  };
+  if (nkb <= 32)
+    for (const W4Plan& t : tiles)
+      if (!(t.bm == 128 && p.m <= 64) && wgs(t) >= 256) return t;
+  for (const W4Plan& t : tiles) {
+    if (t.bm == 128 && p.m <= 64) continue;
+    for (int split = 2; split <= 8; split *= 2)
+      if (split_ok(split) && wgs(t) * split >= 256) return W4Plan{t.bm, t.bn, t.wm, split};
+  }
+  int split = 1;
+  while (split < 8 && split_ok(2 * split) && wgs(tiles[4]) * split < 256) split *= 2;
+  return W4Plan{64, 64, 2, split};
 }
 
-hipError_t launch_gemm_w4(const W4Gemm& p, int group, hipStream_t st) {
+template <int G>
+static hipError_t launch_w4_g(const W4Gemm& p, const W4Plan& pl, float* ws, hipStream_t st) {
+  if (pl.bm == 128 && pl.bn == 256) return launch_w4_t<G, 128, 256, 1>(p, pl.split, ws, st);
+  if (pl.bm == 64 && pl.bn == 256) return launch_w4_t<G, 64, 256, 1>(p, pl.split, ws, st);
+  if (pl.bm == 128 && pl.bn == 128) return launch_w4_t<G, 128, 128, 2>(p, pl.split, ws, st);
+  if (pl.bm == 64 && pl.bn == 128) return launch_w4_t<G, 64, 128, 2>(p, pl.split, ws, st);
+  return launch_w4_t<G, 64, 64, 2>(p, pl.split, ws, st);
+}
+
+hipError_t launch_gemm_w4(const W4Gemm& p, int group, float* ws, size_t ws_bytes, hipStream_t st) {
   if (p.m == 0 || p.n == 0) return hipSuccess;
-  if (group == 64) return launch_w4_g<64>(p, st);
-  if (group == 32) return launch_w4_g<32>(p, st);
-  if (group == 16) return launch_w4_g<16>(p, st);
+  const W4Plan pl = plan_w4(p, ws ? ws_bytes : 0);
+  if (group == 64) return launch_w4_g<64>(p, pl, ws, st);
+  if (group == 32) return launch_w4_g<32>(p, pl, ws, st);
+  if (group == 16) return launch_w4_g<16>(p, pl, ws, st);
   return hipErrorInvalidValue;
 }
 

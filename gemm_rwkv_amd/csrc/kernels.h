@@ -56,8 +56,9 @@ struct W4Gemm {
   int m, n, k, ldx, ldy;
 };
 
-// symmetric int4, group 16, 32 or 64; k % 128 == 0
-hipError_t launch_gemm_w4(const W4Gemm& p, int group, hipStream_t st);
+// symmetric int4, group 16, 32 or 64; k % 128 == 0.  ws (may be null) is the
+// stream's workspace of ws_bytes, for fp32 partial tiles when K is split.
+hipError_t launch_gemm_w4(const W4Gemm& p, int group, float* ws, size_t ws_bytes, hipStream_t st);
 
 // ---- MFMA GEMMs on per-row quantized operands (gemm_mfma.hip) ---------------
 // ws (may be null) is the stream's workspace of ws_bytes: shapes with fewer

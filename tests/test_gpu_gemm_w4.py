@@ -31,8 +31,15 @@ def _run(qw, x, m, ldx, n, ldy=None):
     (100, 128, 37), (257, 384, 130), (300, 1152, 100), (64, 256, 1),
     # 64 x 128 tiles (m <= 64, 257 column tiles), ragged n
     (32770, 128, 50),
-    # 128 x 128 tiles (256 of them), ragged m and n, two blocks
-    (16300, 256, 250)])
+    # 64 x 256 tiles (256 of them), ragged m and n, two blocks
+    (16300, 256, 250),
+    # 64 x 64 tiles (4 x 65) over 32 k blocks, ragged m and n
+    (4100, 4096, 200),
+    # 128 x 256 tiles (8 x 33), ragged m and n
+    (8200, 128, 1000),
+    # K split: 64 x 64 tiles in 2 slices of 8 blocks; 128 x 256 tiles in 8
+    # slices of 8 blocks; ragged m and n
+    (300, 2048, 70), (4000, 8192, 250)])
 def test_gemm_w4_parity(group, n, k, m):
     g = np.random.default_rng(n + k + m + group)
     w = (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
