@@ -8,18 +8,19 @@
 // written out.  The one rounding beyond fp32 summation is that of q * s to
 // fp16 (q has 3 significant bits, s 11), at most 2^-12 of each weight.
 //
-// A workgroup of four waves computes a BM x BN output tile; the waves form a
-// WM x (4 / WM) grid and each computes its (BM / WM) x (BN * WM / 4) part as
-// 16 x 16 v_mfma_f32_16x16x32_f16 tiles over the workgroup's k blocks.  With
-// WM = 1 no two waves decode the same codes.  Split along K (part != null),
-// workgroup z of gridDim.z takes k blocks [z kbs, (z + 1) kbs) and stores its
-// fp32 tile to part[z][m][n]; gemm_w4_reduce_kernel adds the slices in order.  K runs in blocks of 128.  For
-// each block the x rows (BM x 256 bytes, whole 128-byte lines) and the code
-// rows (BN x 64 bytes) are copied by LDS DMA into a 3-stage ring shared by
-// the workgroup, so two blocks are in flight while one is multiplied; one
-// barrier per block.  The x segments of a row are stored at slot
-// segment ^ (row % 16) and the code segments at segment ^ ((row / 4) % 4), so
-// the 16 rows a fragment read touches fall in distinct LDS banks.
+// A workgroup of NW waves (4 or 8) computes a BM x BN output tile; the waves
+// form a WM x (NW / WM) grid and each computes its (BM / WM) x (BN WM / NW)
+// part as 16 x 16 v_mfma_f32_16x16x32_f16 tiles over the workgroup's k
+// blocks.  With WM = 1 no two waves decode the same codes.  K runs in blocks
+// of 128.  For each block the x rows (BM x 256 bytes, whole 128-byte lines)
+// and the code rows (BN x 64 bytes) are copied by LDS DMA into a 3-stage ring
+// shared by the workgroup, so two blocks are in flight while one is
+// multiplied; one barrier per block.  The x segments of a row are stored at
+// slot segment ^ (row % 16) and the code segments at
+// segment ^ ((row / 4) % 4), so the 16 rows a fragment read touches fall in
+// distinct LDS banks.  Split along K (part != null), workgroup z of gridDim.z
+// takes k blocks [z kbs, (z + 1) kbs) and stores its fp32 tile to
+// part[z][m][n]; gemm_w4_reduce_kernel adds the slices in order.
 //
 // k mapping: lane l (row l % 16 of a tile, quarter q = l / 16) reads one
 // 16-byte code segment per n tile and block, segment q of the row's 64 bytes.
@@ -41,16 +42,17 @@
 
 namespace rq {
 
-template <int G, int BM, int BN, int WM>
-__global__ void __launch_bounds__(256) gemm_w4_kernel(const W4Gemm p, int kbs, float* __restrict__ part) {
-  constexpr int WN = 4 / WM;
+template <int G, int BM, int BN, int WM, int NW>
+__global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kbs, float* __restrict__ part) {
+  constexpr int WN = NW / WM;
   constexpr int TM = BM / (16 * WM), TN = BN / (16 * WN);  // 16 x 16 tiles of a wave in m and n
   constexpr int D = 64 / G;                   // scale dwords per row and block
   constexpr int SX = BM * 256, SC = BN * 64, SS = BN * 4 * D, STAGE = SX + SC + SS;
   constexpr int NB = 3;
-  constexpr int XPW = BM / 16;                // x DMA instructions per wave per block
-  constexpr int CPW = BN / 64;                // code DMA instructions per wave per block
-  constexpr int SDW = BN * D / 4;             // scale dwords per wave per block
+  constexpr int XPW = BM / (4 * NW);          // x DMA instructions per wave per block
+  constexpr int CPW = BN / (16 * NW);         // code DMA instructions per wave per block
+  static_assert(XPW * 4 * NW == BM && CPW * 16 * NW == BN && TM >= 1 && TN >= 1, "tile splits evenly");
+  constexpr int SDW = BN * D / NW;            // scale dwords per wave per block
   constexpr int SPW = (SDW + 63) / 64;        // scale DMA instructions per wave per block
   constexpr int OPS = XPW + CPW + SPW;        // vector memory instructions per wave per block
   extern __shared__ uint4 lds4[];
@@ -221,18 +223,19 @@ __global__ void __launch_bounds__(256) gemm_w4_reduce_kernel(const float* __rest
   p.y[(size_t)m * p.ldy + n] = f32_to_f16_bits(v);
 }
 
-template <int G, int BM, int BN, int WM>
+template <int G, int BM, int BN, int WM, int NW>
 static hipError_t launch_w4_t(const W4Gemm& p, int split, float* part, hipStream_t st) {
   constexpr size_t lds = (size_t)3 * (BM * 256 + BN * 64 + BN * 256 / G);
   static_assert(lds <= 160 * 1024, "ring fits LDS");
-  static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w4_kernel<G, BM, BN, WM>,
+  static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w4_kernel<G, BM, BN, WM, NW>,
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    (int)lds) == hipSuccess;
   (void)attr_set;
   const int nkb = p.k >> 7;
   const int kbs = (nkb + split - 1) / split;
   const dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM), (unsigned)split);
-  hipLaunchKernelGGL((gemm_w4_kernel<G, BM, BN, WM>), grid, dim3(256), lds, st, p, kbs, split > 1 ? part : nullptr);
+  hipLaunchKernelGGL((gemm_w4_kernel<G, BM, BN, WM, NW>), grid, dim3(64 * NW), lds, st, p, kbs,
+                     split > 1 ? part : nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || split == 1) return err;
   const size_t outs = (size_t)p.m * p.n;
@@ -242,19 +245,22 @@ static hipError_t launch_w4_t(const W4Gemm& p, int split, float* part, hipStream
 }
 
 // Launch plan, from measurements of the width-4096 shapes at m = 64, 256 and
-// 1024.  Tiles in order of activation + code traffic per output,
-// K (2 / BN + 1 / (2 BM)) bytes: 128 x 256, 64 x 256, 128 x 128, 64 x 128,
-// 64 x 64 (128-row tiles only for m > 64).  Up to 32 k blocks (K <= 4096),
+// 1024 (activation + code traffic per output is K (2 / BN + 1 / (2 BM))
+// bytes; eight waves let one wave's decoding overlap another's MFMAs).
+// Tiles in order: 128 x 256 and 128 x 128 with eight waves (2 x 4), 64 x 256
+// with four (1 x 4), 64 x 128 with eight (1 x 8), 64 x 64 with four (2 x 2);
+// 128-row tiles only for m > 64.  Up to 32 k blocks (K <= 4096),
 // the first tile that makes 256 workgroups unsplit; otherwise, and for longer
 // K, the first that makes 256 with K split in 2, 4 or 8 slices of at least 8
 // k blocks (partial tiles in the workspace); failing both, 64 x 64 split as
 // far as that allows.
 struct W4Plan {
-  int bm, bn, wm, split;
+  int bm, bn, wm, split, nw;
 };
 
 static W4Plan plan_w4(const W4Gemm& p, size_t ws_bytes) {
-  static const W4Plan tiles[] = {{128, 256, 1, 1}, {64, 256, 1, 1}, {128, 128, 2, 1}, {64, 128, 2, 1}, {64, 64, 2, 1}};
+  static const W4Plan tiles[] = {{128, 256, 2, 1, 8}, {128, 128, 2, 1, 8}, {64, 256, 1, 1, 4}, {64, 128, 1, 1, 8},
+                                 {64, 64, 2, 1, 4}};
   const int nkb = p.k >> 7;
   auto wgs = [&](const W4Plan& t) { return (long)((p.m + t.bm - 1) / t.bm) * (long)((p.n + t.bn - 1) / t.bn); };
   auto split_ok = [&](int split) {
@@ -266,20 +272,24 @@ static W4Plan plan_w4(const W4Gemm& p, size_t ws_bytes) {
   for (const W4Plan& t : tiles) {
     if (t.bm == 128 && p.m <= 64) continue;
     for (int split = 2; split <= 8; split *= 2)
-      if (split_ok(split) && wgs(t) * split >= 256) return W4Plan{t.bm, t.bn, t.wm, split};
+      if (split_ok(split) && wgs(t) * split >= 256) return W4Plan{t.bm, t.bn, t.wm, split, t.nw};
   }
   int split = 1;
   while (split < 8 && split_ok(2 * split) && wgs(tiles[4]) * split < 256) split *= 2;
-  return W4Plan{64, 64, 2, split};
+  return W4Plan{64, 64, 2, split, 4};
 }
 
 template <int G>
 static hipError_t launch_w4_g(const W4Gemm& p, const W4Plan& pl, float* ws, hipStream_t st) {
-  if (pl.bm == 128 && pl.bn == 256) return launch_w4_t<G, 128, 256, 1>(p, pl.split, ws, st);
-  if (pl.bm == 64 && pl.bn == 256) return launch_w4_t<G, 64, 256, 1>(p, pl.split, ws, st);
-  if (pl.bm == 128 && pl.bn == 128) return launch_w4_t<G, 128, 128, 2>(p, pl.split, ws, st);
-  if (pl.bm == 64 && pl.bn == 128) return launch_w4_t<G, 64, 128, 2>(p, pl.split, ws, st);
-  return launch_w4_t<G, 64, 64, 2>(p, pl.split, ws, st);
+#define RQ_W4(BM, BN, WM, NW)                                                  \
+  if (pl.bm == BM && pl.bn == BN && pl.wm == WM && pl.nw == NW)                 \
+    return launch_w4_t<G, BM, BN, WM, NW>(p, pl.split, ws, st);
+  RQ_W4(128, 256, 2, 8)
+  RQ_W4(128, 128, 2, 8)
+  RQ_W4(64, 256, 1, 4)
+  RQ_W4(64, 128, 1, 8)
+#undef RQ_W4
+  return launch_w4_t<G, 64, 64, 2, 4>(p, pl.split, ws, st);
 }
 
 hipError_t launch_gemm_w4(const W4Gemm& p, int group, float* ws, size_t ws_bytes, hipStream_t st) {

@@ -29,13 +29,14 @@ def _run(qw, x, m, ldx, n, ldy=None):
     # 64 x 64 tiles: one k block, ragged m and n; three blocks (the whole
     # ring once); nine blocks; a single row
     (100, 128, 37), (257, 384, 130), (300, 1152, 100), (64, 256, 1),
-    # 64 x 128 tiles (m <= 64, 257 column tiles), ragged n
-    (32770, 128, 50),
-    # 64 x 256 tiles (256 of them), ragged m and n, two blocks
+    # m <= 64: 64 x 128 tiles of eight waves (257 column tiles); 64 x 256
+    # tiles of four waves (257 column tiles); ragged n
+    (32770, 128, 50), (65540, 128, 60),
+    # 128 x 128 tiles of eight waves (2 x 128), ragged m and n, two blocks
     (16300, 256, 250),
     # 64 x 64 tiles (4 x 65) over 32 k blocks, ragged m and n
     (4100, 4096, 200),
-    # 128 x 256 tiles (8 x 33), ragged m and n
+    # 128 x 256 tiles of eight waves (8 x 33), ragged m and n
     (8200, 128, 1000),
     # K split: 64 x 64 tiles in 2 slices of 8 blocks; 128 x 256 tiles in 8
     # slices of 8 blocks; ragged m and n
