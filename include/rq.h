@@ -17,15 +17,17 @@
  *     rq_qweight_bytes, which live in host memory.  The caller allocates and
  *     frees every buffer it passes; the library keeps no pointer to them
  *     after returning.
- *   - Workspace: the weight-streaming products (rq_gemv_*, rq_gemm_small_m,
- *     rq_fused_rkv) may cut K across workgroups and add the partial sums in
- *     a second kernel.  Those partials live in a 64 MiB device buffer that
- *     the library allocates on the first such call on each (device, stream)
- *     pair and keeps until the process ends, so calls on different streams
- *     never share one.  While a stream is being captured into a graph
- *     nothing is allocated: a stream that has no workspace yet runs unsplit
- *     launch shapes, with the same results (warm up on the capture stream
- *     to capture the split shapes).
+ *   - Workspace: the products (rq_gemv_*, rq_gemm_small_m, rq_fused_rkv,
+ *     rq_gemm_w4, rq_gemm_fp8, rq_gemm_int8, rq_gemm_int8_acc) may cut K
+ *     across workgroups and add the partial sums in a second kernel.  Those
+ *     partials live in a 64 MiB device buffer that the library allocates on
+ *     the first such call on each (device, stream) pair and keeps until the
+ *     process ends, so calls on different streams never share one.  While a
+ *     stream is being captured into a graph nothing is allocated: a stream
+ *     that has no workspace yet runs unsplit launch shapes (warm up on the
+ *     capture stream to capture the split shapes).  The weight-streaming
+ *     products give the same results either way; the dense GEMMs agree
+ *     within the fp32 summation tolerance.
  *   - fp16 values are IEEE binary16 bit patterns (uint16_t).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it; product calls return without synchronizing.
