@@ -258,6 +258,36 @@ class Sweep:
         return out
 
 
+def _w4_gemm_rows(gen, dev, c, fmt, group, ms, label, graph_us):
+    """rq_gemm_w4 on 6 copies of the width-c set: us per set and TFLOP/s."""
+    out = {}
+    wsets = []
+    for _ in range(6):
+        wset = {}
+        for mat, n, k in synth.layer_shapes(c):
+            wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
+            wset[mat] = rq.quantize(wf, fmt, group)
+            del wf
+        wsets.append(wset)
+    for m in ms:
+        xa = f16_dev(synth.act_normal(m, c, 3), dev)
+        xa4 = f16_dev(synth.act_normal(m, 4 * c, 3, salt=1), dev)
+        yp = torch.empty(m * 4 * c, dtype=torch.int16, device=dev)
+
+        def w4_pass(m=m, xa=xa, xa4=xa4, yp=yp):
+            for wset in wsets:
+                for mat in (synth.MAT_R, synth.MAT_K, synth.MAT_V, synth.MAT_O, synth.MAT_KEY):
+                    rq.rq_gemm_w4(xa, m, c, wset[mat], yp, wset[mat].n)
+                rq.rq_gemm_w4(xa4, m, 4 * c, wset[synth.MAT_VALUE], yp, c)
+        us = graph_us(w4_pass, len(wsets))
+        flops = sum(2.0 * m * n * k for _, n, k in synth.layer_shapes(c))
+        out["%s gemm %d set M=%d" % (label, c, m)] = {
+            "us_per_set": round(us, 2), "TFLOPS": round(flops / us / 1e6, 1),
+            "frac_of_fp16_peak": round(flops / us / 1e6 / F16_PEAK_TFLOPS, 4)}
+    del wsets
+    return out
+
+
 def measure_rows(gen, dev, reps=20):
     """One measurement per row of the path that the step does not time: the
     quantizers, the SB256 products (width 2560, M = 1, 4, 16), the int8 GEMM
@@ -339,31 +369,12 @@ def measure_rows(gen, dev, reps=20):
     out["int8 gemm 4096 set M=256"] = {"us_per_set": round(us, 2), "TOPS": round(flops / us / 1e6, 1),
                                        "frac_of_peak": round(flops / us / 1e6 / FP8_PEAK_TFLOPS, 4)}
     del isets
-    # int4 g64 prefill GEMM (rq_gemm_w4), width-4096 set at M = 64, 256, 1024,
-    # 6 copies (640 MB), fp16 activations
-    wsets = []
-    for _ in range(6):
-        wset = {}
-        for mat, n, k in synth.layer_shapes(c):
-            wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
-            wset[mat] = rq.quantize(wf, rq.RQ_W4_SYM, 64)
-            del wf
-        wsets.append(wset)
-    for m in (64, 256, 1024):
-        xa = f16_dev(synth.act_normal(m, c, 3), dev)
-        xa4 = f16_dev(synth.act_normal(m, 4 * c, 3, salt=1), dev)
-        yp = torch.empty(m * 4 * c, dtype=torch.int16, device=dev)
-
-        def w4_pass(m=m, xa=xa, xa4=xa4, yp=yp):
-            for wset in wsets:
-                for mat in (synth.MAT_R, synth.MAT_K, synth.MAT_V, synth.MAT_O, synth.MAT_KEY):
-                    rq.rq_gemm_w4(xa, m, c, wset[mat], yp, wset[mat].n)
-                rq.rq_gemm_w4(xa4, m, 4 * c, wset[synth.MAT_VALUE], yp, c)
-        us = graph_us(w4_pass, len(wsets))
-        flops = sum(2.0 * m * n * k for _, n, k in synth.layer_shapes(c))
-        out["int4 g64 gemm 4096 set M=%d" % m] = {"us_per_set": round(us, 2), "TFLOPS": round(flops / us / 1e6, 1),
-                                                  "frac_of_fp16_peak": round(flops / us / 1e6 / F16_PEAK_TFLOPS, 4)}
-    del wsets
+    # int4 prefill GEMM (rq_gemm_w4), width-4096 set, 6 copies, fp16
+    # activations: symmetric g64 at M = 64, 256, 1024 (640 MB), superblocks
+    # at M = 256 (340 MB)
+    for fmt, group, ms, label in ((rq.RQ_W4_SYM, 64, (64, 256, 1024), "int4 g64"),
+                                  (rq.RQ_W4_ASYM_SB256, 32, (256,), "int4 sb256")):
+        out.update(_w4_gemm_rows(gen, dev, c, fmt, group, ms, label, graph_us))
     # width-768 fused R/K/V, w8g64, M = 1: 200 calls on distinct weight copies
     # (365 MB) per graph, so the figure is the per-call device time
     ws, x = synth.fused_rkv_768()

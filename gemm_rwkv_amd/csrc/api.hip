@@ -107,12 +107,12 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   return hip_status(rq::launch_gemv(b, gf, w->group, S(stream)));
 }
 
-// rq_gemm_w4: symmetric int4 codes, any m.
+// rq_gemm_w4: int4 codes (symmetric groups or asymmetric superblocks), any m.
 int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
             void* stream) {
   int st = rqv::check_weight(w);
   if (st != RQ_OK) return st;
-  if (w->format != RQ_W4_SYM) return RQ_ERR_FORMAT;
+  if (w->format != RQ_W4_SYM && w->format != RQ_W4_ASYM_SB256) return RQ_ERR_FORMAT;
   if (w->k % 128 != 0) return RQ_ERR_SHAPE;
   if (m < 0 || m >= rqv::kMaxDim) return RQ_ERR_SHAPE;
   if ((st = rqv::check_act(x, m, w->k, ldx)) != RQ_OK) return st;
@@ -126,13 +126,15 @@ int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   p.x = x;
   p.codes = (const uint8_t*)w->codes;
   p.scales = (const uint16_t*)w->scales;
+  p.mins = (const uint16_t*)w->mins;
+  p.sub = (const uint8_t*)w->sub;
   p.y = y;
   p.m = (int)m;
   p.n = (int)w->n;
   p.k = (int)w->k;
   p.ldx = (int)ldx;
   p.ldy = (int)ldy;
-  return hip_status(rq::launch_gemm_w4(p, w->group, (float*)stream_workspace(S(stream)),
+  return hip_status(rq::launch_gemm_w4(p, w->format == RQ_W4_ASYM_SB256, w->group, (float*)stream_workspace(S(stream)),
                                        rq::kGemvWsPartialBytes, S(stream)));
 }
 

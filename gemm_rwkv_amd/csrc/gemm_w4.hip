@@ -1,12 +1,16 @@
 // Prefill products on int4 codes, any number of activation rows (the prefill
 // chunks of 64 to 1024 tokens):
-//   y[m][n] = fp16( sum_k x[m][k] * w[n][k] ),  w = fp16(q * s),
-// on symmetric int4 group codes (groups of 16, 32 or 64), accumulated in fp32.
+//   y[m][n] = fp16( sum_k x[m][k] * w[n][k] ),  accumulated in fp32, with
+//   w = fp16(q * s) on symmetric int4 group codes (groups of 16, 32 or 64),
+//   w = fma16(u, fp16(S_j), fp16(-M_j)) on asymmetric 256-superblocks.
 // This is the tensor-core GEMM member of the int4 product family ("RWKV-7 G1
 // 1.5B -- int4 GPTQ for rwkv-sglang" model card, summary), here on gfx950
 // MFMA; the weights are read as codes and dequantized in registers, never
-// written out.  The one rounding beyond fp32 summation is that of q * s to
-// fp16 (q has 3 significant bits, s 11), at most 2^-12 of each weight.
+// written out.  Beyond fp32 summation: symmetric, q * s is rounded once to
+// fp16 (q has 3 significant bits, s 11), at most 2^-12 of each weight;
+// superblocks, S_j and M_j (exact in fp32) are each rounded to fp16 and the
+// fp16 fma rounds once more, so each weight is off by at most about
+// 2^-12 (15 S_j + 2 M_j).
 //
 // A workgroup of NW waves (4 or 8) computes a BM x BN output tile; the waves
 // form a WM x (NW / WM) grid and each computes its (BM / WM) x (BN WM / NW)
@@ -29,7 +33,8 @@
 // scaled in packed fp16 by that group's scale.  The A operand of step s is
 // the 16 bytes of x holding the same eight k, so every product pairs matching
 // k whatever order the MFMA sums in.  The block's scales (64 / G dwords per
-// row) are copied into the same ring stage by LDS DMA.
+// row; for superblocks d, dmin and the 12 sub-code bytes of the block's
+// superblock) are copied into the same ring stage by LDS DMA.
 //
 // Every copy and its wait are inline asm: the compiler cannot tell which LDS
 // bytes a DMA writes and would otherwise wait for every load in flight before
@@ -42,18 +47,23 @@
 
 namespace rq {
 
-template <int G, int BM, int BN, int WM, int NW>
+template <bool SB, int G, int BM, int BN, int WM, int NW>
 __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kbs, float* __restrict__ part) {
   constexpr int WN = NW / WM;
   constexpr int TM = BM / (16 * WM), TN = BN / (16 * WN);  // 16 x 16 tiles of a wave in m and n
-  constexpr int D = 64 / G;                   // scale dwords per row and block
-  constexpr int SX = BM * 256, SC = BN * 64, SS = BN * 4 * D, STAGE = SX + SC + SS;
+  constexpr int D = SB ? 1 : 64 / G;          // symmetric: scale dwords per row and block
+  // scale area per stage: symmetric, D dwords per row; superblocks, d and dmin
+  // in a 4-byte slot each and the 12 sub-code bytes in a 16-byte slot per row
+  constexpr int SS = SB ? BN * 24 : BN * 4 * D;
+  constexpr int SX = BM * 256, SC = BN * 64, STAGE = SX + SC + SS;
   constexpr int NB = 3;
   constexpr int XPW = BM / (4 * NW);          // x DMA instructions per wave per block
   constexpr int CPW = BN / (16 * NW);         // code DMA instructions per wave per block
   static_assert(XPW * 4 * NW == BM && CPW * 16 * NW == BN && TM >= 1 && TN >= 1, "tile splits evenly");
-  constexpr int SDW = BN * D / NW;            // scale dwords per wave per block
-  constexpr int SPW = (SDW + 63) / 64;        // scale DMA instructions per wave per block
+  constexpr int SDW = BN * D / NW;            // symmetric: scale dwords per wave per block
+  constexpr int RPW = BN / NW;                // superblocks: rows per wave
+  static_assert(!SB || RPW <= 64, "one superblock copy per wave and kind");
+  constexpr int SPW = SB ? 3 : (SDW + 63) / 64;  // scale DMA instructions per wave per block
   constexpr int OPS = XPW + CPW + SPW;        // vector memory instructions per wave per block
   extern __shared__ uint4 lds4[];
 
@@ -89,14 +99,26 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
     const int seg = (lane & 3) ^ ((r >> 2) & 3);
     csrc[u] = p.codes + (size_t)min(n0 + r, N - 1) * crow + (size_t)kb0 * 64 + seg * 16;
   }
-  const size_t srow = (size_t)(K / G) * 2;  // scale bytes per row
+  if constexpr (SB) {
+    // lane -> row wave * RPW + lane: d, dmin (2 bytes each) and sub (12 bytes)
+    // of the row's superblock; the block's superblock is added per copy
+    const size_t nsb = (size_t)(K / 256);
+    const size_t rsb = (size_t)min(n0 + wave * RPW + lane, N - 1) * nsb;
 #pragma unroll
-  for (int u = 0; u < SPW; ++u) {
-    const int i = u * 64 + lane;             // dword of this wave's share
-    const int t = wave * SDW + i;
-    sact[u] = i < SDW;
-    ssrc[u] = (const uint8_t*)p.scales + (size_t)min(n0 + t / D, N - 1) * srow + (size_t)kb0 * (4 * D) +
-              (t % D) * 4;
+    for (int u = 0; u < 3; ++u) sact[u] = lane < RPW;
+    ssrc[0] = (const uint8_t*)p.scales + rsb * 2;
+    ssrc[1] = (const uint8_t*)p.mins + rsb * 2;
+    ssrc[2] = p.sub + rsb * 12;
+  } else {
+    const size_t srow = (size_t)(K / G) * 2;  // scale bytes per row
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+      const int i = u * 64 + lane;           // dword of this wave's share
+      const int t = wave * SDW + i;
+      sact[u] = i < SDW;
+      ssrc[u] = (const uint8_t*)p.scales + (size_t)min(n0 + t / D, N - 1) * srow + (size_t)kb0 * (4 * D) +
+                (t % D) * 4;
+    }
   }
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
 
@@ -114,12 +136,29 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                    :: "v"(g), "s"(base + SX + (wave * CPW + u) * 1024) : "memory", "m0");
     }
+    if constexpr (SB) {
+      // 2-byte copies land zero-extended in 4-byte slots, 12-byte copies in
+      // 16-byte slots (one per lane)
+      const size_t sb = (size_t)((kb0 + kb) >> 1);
+      if (sact[0]) {
+        const uint8_t* gd = ssrc[0] + sb * 2;
+        const uint8_t* gm = ssrc[1] + sb * 2;
+        const uint8_t* gs = ssrc[2] + sb * 12;
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off"
+                     :: "v"(gd), "s"(base + SX + SC + wave * RPW * 4) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off"
+                     :: "v"(gm), "s"(base + SX + SC + BN * 4 + wave * RPW * 4) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, off"
+                     :: "v"(gs), "s"(base + SX + SC + BN * 8 + wave * RPW * 16) : "memory", "m0");
+      }
+    } else {
 #pragma unroll
-    for (int u = 0; u < SPW; ++u) {
-      const uint8_t* g = ssrc[u] + (size_t)kb * (4 * D);
-      if (sact[u])
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                     :: "v"(g), "s"(base + SX + SC + (wave * SDW + u * 64) * 4) : "memory", "m0");
+      for (int u = 0; u < SPW; ++u) {
+        const uint8_t* g = ssrc[u] + (size_t)kb * (4 * D);
+        if (sact[u])
+          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                       :: "v"(g), "s"(base + SX + SC + (wave * SDW + u * 64) * 4) : "memory", "m0");
+      }
     }
   };
 
@@ -129,28 +168,45 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st) {
+  auto compute = [&](int j, int st) {
     const uint8_t* xs = (const uint8_t*)lds4 + st * STAGE;
     const uint8_t* cs = xs + SX;
     const uint8_t* ss = xs + SX + SC;
     uint4 cw[TN];
     half8 s01[TN], s23[TN];  // the lane's scale for steps 0-1 and 2-3, broadcast
+    half8 mneg[TN];          // superblocks: -M_j, broadcast
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
       const int row = wn * (BN / WN) + 16 * b + r16;
       cw[b] = *(const uint4*)(cs + row * 64 + ((q ^ ((row >> 2) & 3)) << 4));
-      // group of k = 32 q + 8 s within the block: g64 -> q / 2, g32 -> q, g16 -> 2 q + s / 2
-      _Float16 lo, hi;
-      if constexpr (G == 16) {
-        const half2v v = *(const half2v*)(ss + row * 16 + q * 4);
-        lo = v[0];
-        hi = v[1];
+      if constexpr (SB) {
+        // group j = (block % 2) * 4 + q of the superblock: S_j = d sc_j and
+        // M_j = dmin mc_j (exact in fp32), each rounded once to fp16
+        const float d = f16_bits_to_f32(*(const uint16_t*)(ss + row * 4));
+        const float dm = f16_bits_to_f32(*(const uint16_t*)(ss + BN * 4 + row * 4));
+        const uint4 sub = *(const uint4*)(ss + BN * 8 + row * 16);
+        const uint64_t lo48 = (uint64_t)sub.x | ((uint64_t)(sub.y & 0xffffu) << 32);
+        const uint64_t hi48 = (uint64_t)(sub.y >> 16) | ((uint64_t)sub.z << 16);
+        const int g = ((kb0 + j) & 1) * 4 + q;
+        const _Float16 sh = (_Float16)(d * (float)((uint32_t)(lo48 >> (6 * g)) & 63u));
+        const _Float16 mh = (_Float16)(-(dm * (float)((uint32_t)(hi48 >> (6 * g)) & 63u)));
+        s01[b] = half8{sh, sh, sh, sh, sh, sh, sh, sh};
+        s23[b] = s01[b];
+        mneg[b] = half8{mh, mh, mh, mh, mh, mh, mh, mh};
       } else {
-        lo = *(const _Float16*)(ss + row * 4 * D + (G == 64 ? (q >> 1) : q) * 2);
-        hi = lo;
+        // group of k = 32 q + 8 s within the block: g64 -> q / 2, g32 -> q, g16 -> 2 q + s / 2
+        _Float16 lo, hi;
+        if constexpr (G == 16) {
+          const half2v v = *(const half2v*)(ss + row * 16 + q * 4);
+          lo = v[0];
+          hi = v[1];
+        } else {
+          lo = *(const _Float16*)(ss + row * 4 * D + (G == 64 ? (q >> 1) : q) * 2);
+          hi = lo;
+        }
+        s01[b] = half8{lo, lo, lo, lo, lo, lo, lo, lo};
+        s23[b] = half8{hi, hi, hi, hi, hi, hi, hi, hi};
       }
-      s01[b] = half8{lo, lo, lo, lo, lo, lo, lo, lo};
-      s23[b] = half8{hi, hi, hi, hi, hi, hi, hi, hi};
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -158,7 +214,10 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         const uint32_t w = s == 0 ? cw[b].x : (s == 1 ? cw[b].y : (s == 2 ? cw[b].z : cw[b].w));
-        bf[b] = dec4n<true>(w) * (s < 2 ? s01[b] : s23[b]);
+        if constexpr (SB)
+          bf[b] = dec4n<false>(w) * s01[b] + mneg[b];
+        else
+          bf[b] = dec4n<true>(w) * (s < 2 ? s01[b] : s23[b]);
       }
 #pragma unroll
       for (int a = 0; a < TM; ++a) {
@@ -182,7 +241,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 2 < nkb) issue(j + 2, (j + 2) % NB);
-    compute(j % NB);
+    compute(j, j % NB);
   }
 
   // epilogue: lane holds D[m = 4q + r][n = r16] of each 16 x 16 tile
@@ -223,18 +282,18 @@ __global__ void __launch_bounds__(256) gemm_w4_reduce_kernel(const float* __rest
   p.y[(size_t)m * p.ldy + n] = f32_to_f16_bits(v);
 }
 
-template <int G, int BM, int BN, int WM, int NW>
+template <bool SB, int G, int BM, int BN, int WM, int NW>
 static hipError_t launch_w4_t(const W4Gemm& p, int split, float* part, hipStream_t st) {
-  constexpr size_t lds = (size_t)3 * (BM * 256 + BN * 64 + BN * 256 / G);
+  constexpr size_t lds = (size_t)3 * (BM * 256 + BN * 64 + (SB ? BN * 24 : BN * 256 / G));
   static_assert(lds <= 160 * 1024, "ring fits LDS");
-  static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w4_kernel<G, BM, BN, WM, NW>,
+  static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w4_kernel<SB, G, BM, BN, WM, NW>,
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    (int)lds) == hipSuccess;
   (void)attr_set;
   const int nkb = p.k >> 7;
   const int kbs = (nkb + split - 1) / split;
   const dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM), (unsigned)split);
-  hipLaunchKernelGGL((gemm_w4_kernel<G, BM, BN, WM, NW>), grid, dim3(64 * NW), lds, st, p, kbs,
+  hipLaunchKernelGGL((gemm_w4_kernel<SB, G, BM, BN, WM, NW>), grid, dim3(64 * NW), lds, st, p, kbs,
                      split > 1 ? part : nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || split == 1) return err;
@@ -249,7 +308,8 @@ static hipError_t launch_w4_t(const W4Gemm& p, int split, float* part, hipStream
 // bytes; eight waves let one wave's decoding overlap another's MFMAs).
 // Tiles in order: 128 x 256 and 128 x 128 with eight waves (2 x 4), 64 x 256
 // with four (1 x 4), 64 x 128 with eight (1 x 8), 64 x 64 with four (2 x 2);
-// 128-row tiles only for m > 64.  Up to 32 k blocks (K <= 4096),
+// 128-row tiles only for m > 64, and no 128 x 256 for superblocks (its ring
+// would not fit LDS).  Up to 32 k blocks (K <= 4096),
 // the first tile that makes 256 workgroups unsplit; otherwise, and for longer
 // K, the first that makes 256 with K split in 2, 4 or 8 slices of at least 8
 // k blocks (partial tiles in the workspace); failing both, 64 x 64 split as
@@ -258,7 +318,7 @@ struct W4Plan {
   int bm, bn, wm, split, nw;
 };
 
-static W4Plan plan_w4(const W4Gemm& p, size_t ws_bytes) {
+static W4Plan plan_w4(const W4Gemm& p, bool sb, size_t ws_bytes) {
   static const W4Plan tiles[] = {{128, 256, 2, 1, 8}, {128, 128, 2, 1, 8}, {64, 256, 1, 1, 4}, {64, 128, 1, 1, 8},
                                  {64, 64, 2, 1, 4}};
   const int nkb = p.k >> 7;
@@ -266,11 +326,13 @@ static W4Plan plan_w4(const W4Gemm& p, size_t ws_bytes) {
   auto split_ok = [&](int split) {
     return nkb / split >= 8 && (size_t)split * p.m * p.n * 4 <= ws_bytes;
   };
+  // 128-row tiles only for m > 64; superblocks' ring of 128 x 256 exceeds LDS
+  auto usable = [&](const W4Plan& t) { return !(t.bm == 128 && p.m <= 64) && !(sb && t.bm == 128 && t.bn == 256); };
   if (nkb <= 32)
     for (const W4Plan& t : tiles)
-      if (!(t.bm == 128 && p.m <= 64) && wgs(t) >= 256) return t;
+      if (usable(t) && wgs(t) >= 256) return t;
   for (const W4Plan& t : tiles) {
-    if (t.bm == 128 && p.m <= 64) continue;
+    if (!usable(t)) continue;
     for (int split = 2; split <= 8; split *= 2)
       if (split_ok(split) && wgs(t) * split >= 256) return W4Plan{t.bm, t.bn, t.wm, split, t.nw};
   }
@@ -279,25 +341,28 @@ static W4Plan plan_w4(const W4Gemm& p, size_t ws_bytes) {
   return W4Plan{64, 64, 2, split, 4};
 }
 
-template <int G>
+template <bool SB, int G>
 static hipError_t launch_w4_g(const W4Gemm& p, const W4Plan& pl, float* ws, hipStream_t st) {
 #define RQ_W4(BM, BN, WM, NW)                                                  \
   if (pl.bm == BM && pl.bn == BN && pl.wm == WM && pl.nw == NW)                 \
-    return launch_w4_t<G, BM, BN, WM, NW>(p, pl.split, ws, st);
-  RQ_W4(128, 256, 2, 8)
+    return launch_w4_t<SB, G, BM, BN, WM, NW>(p, pl.split, ws, st);
+  if constexpr (!SB) {
+    RQ_W4(128, 256, 2, 8)
+  }
   RQ_W4(128, 128, 2, 8)
   RQ_W4(64, 256, 1, 4)
   RQ_W4(64, 128, 1, 8)
 #undef RQ_W4
-  return launch_w4_t<G, 64, 64, 2, 4>(p, pl.split, ws, st);
+  return launch_w4_t<SB, G, 64, 64, 2, 4>(p, pl.split, ws, st);
 }
 
-hipError_t launch_gemm_w4(const W4Gemm& p, int group, float* ws, size_t ws_bytes, hipStream_t st) {
+hipError_t launch_gemm_w4(const W4Gemm& p, bool sb, int group, float* ws, size_t ws_bytes, hipStream_t st) {
   if (p.m == 0 || p.n == 0) return hipSuccess;
-  const W4Plan pl = plan_w4(p, ws ? ws_bytes : 0);
-  if (group == 64) return launch_w4_g<64>(p, pl, ws, st);
-  if (group == 32) return launch_w4_g<32>(p, pl, ws, st);
-  if (group == 16) return launch_w4_g<16>(p, pl, ws, st);
+  const W4Plan pl = plan_w4(p, sb, ws ? ws_bytes : 0);
+  if (sb) return launch_w4_g<true, 32>(p, pl, ws, st);
+  if (group == 64) return launch_w4_g<false, 64>(p, pl, ws, st);
+  if (group == 32) return launch_w4_g<false, 32>(p, pl, ws, st);
+  if (group == 16) return launch_w4_g<false, 16>(p, pl, ws, st);
   return hipErrorInvalidValue;
 }
 

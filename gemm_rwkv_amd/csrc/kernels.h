@@ -51,14 +51,17 @@ hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 struct W4Gemm {
   const uint16_t* x;       // fp16 [m][ldx]
   const uint8_t* codes;    // [n][k/2]
-  const uint16_t* scales;  // fp16 [n][k/group]
+  const uint16_t* scales;  // symmetric: fp16 [n][k/group]; superblocks: d [n][k/256]
+  const uint16_t* mins;    // superblocks: dmin [n][k/256]
+  const uint8_t* sub;      // superblocks: [n][k/256][12]
   uint16_t* y;             // fp16 [m][ldy]
   int m, n, k, ldx, ldy;
 };
 
-// symmetric int4, group 16, 32 or 64; k % 128 == 0.  ws (may be null) is the
+// symmetric int4 (group 16, 32 or 64; k % 128 == 0) or, with sb, the
+// asymmetric 256-superblocks (k % 256 == 0).  ws (may be null) is the
 // stream's workspace of ws_bytes, for fp32 partial tiles when K is split.
-hipError_t launch_gemm_w4(const W4Gemm& p, int group, float* ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_gemm_w4(const W4Gemm& p, bool sb, int group, float* ws, size_t ws_bytes, hipStream_t st);
 
 // ---- MFMA GEMMs on per-row quantized operands (gemm_mfma.hip) ---------------
 // ws (may be null) is the stream's workspace of ws_bytes: shapes with fewer

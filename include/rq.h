@@ -190,13 +190,14 @@ int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight 
 
 /* Prefill products on int4 codes for any number of rows m (the tensor-core
  * GEMM member of the int4 family in the model card's summary), on MFMA:
- * y[m][n] = fp16(sum_k x[m][k] * w[n][k]) with w = fp16(q * s), the code
- * times its group's scale rounded once to fp16 (at most 2^-12 of the weight),
- * and fp32 accumulation.  x: fp16 [m][ldx], ldx >= k, ldx % 8 == 0;
- * y: fp16 [m][ldy], ldy >= n.  w: RQ_W4_SYM with group 16, 32 or 64 and
- * k % 128 == 0 (RQ_ERR_FORMAT for other formats, RQ_ERR_SHAPE for k).  The
- * weights are read once per tile row of 64 or 128 activation rows; meant for
- * m from about 64 up (rq_gemm_small_m covers m <= 32).  Any m >= 0. */
+ * y[m][n] = fp16(sum_k x[m][k] * w[n][k]) with fp32 accumulation and the
+ * weight dequantized to fp16 in registers: w = fp16(q * s) for RQ_W4_SYM
+ * (group 16, 32 or 64; k % 128 == 0), at most 2^-12 of the weight off;
+ * w = fma16(u, fp16(S_j), fp16(-M_j)) for RQ_W4_ASYM_SB256.  Other formats:
+ * RQ_ERR_FORMAT.  x: fp16 [m][ldx], ldx >= k, ldx % 8 == 0; y: fp16
+ * [m][ldy], ldy >= n.  The weights are read once per tile row of 64 or 128
+ * activation rows; meant for m from about 64 up (rq_gemm_small_m covers
+ * m <= 32).  Any m >= 0. */
 int rq_gemm_w4(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w, uint16_t *y,
                int64_t ldy, void *stream);
 

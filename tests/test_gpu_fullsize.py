@@ -212,6 +212,25 @@ def test_prefill_w4_4096(prefill_w4_4096, m):
                       synth.MAT_NAMES[mat])
 
 
+@pytest.mark.parametrize("m", [64, 256, 1024])
+def test_prefill_sb256_4096(m):
+    """The width-4096 prefill set on asymmetric superblock codes (rq_gemm_w4)."""
+    c = 4096
+    for mat, n, k in synth.layer_shapes(c):
+        w = synth.weight(3, 20, mat, n, k)
+        qw = _gpu_weights(w, quant.W4_ASYM_SB256, 32)
+        x = synth.act_normal(m, k, 3, salt=40 + mat)
+        y = torch.empty(m * n * 2, dtype=torch.uint8, device="cuda")
+        say("prefill sb256 4096", synth.MAT_NAMES[mat], "m", m)
+        rq.rq_gemm_w4(dev_f16(x), m, k, qw, y, n)
+        torch.cuda.synchronize()
+        rows = _rows(n, 800 + mat + m)
+        parts = _check_rows_sb(qw, w, rows)
+        _compare_rows(host(y, np.float16).reshape(m, n), rows, x, quant.W4_ASYM_SB256, parts, 32,
+                      synth.MAT_NAMES[mat])
+        del qw
+
+
 # --------------------------------------------------------------------------
 # width 4096 (13.3B) decode step: one layer's six matrices (every layer has
 # these shapes) at M in {1, 2, 4, 8, 16, 32}, and the fp16 head

@@ -54,6 +54,47 @@ def test_gemm_w4_parity(group, n, k, m):
     assert ok, info
 
 
+@pytest.mark.parametrize("n,k,m", [
+    # 64 x 64 tiles, one superblock (two k blocks); ragged m and n
+    (100, 256, 37), (257, 768, 130),
+    # 64 x 128 tiles of eight waves (m <= 64); 128 x 128 tiles of eight waves
+    (32770, 256, 50), (16300, 512, 250),
+    # K = 10240 (the width-2560 cmix value input) split in 8 slices of 10
+    # blocks, on 64 x 128 and 64 x 64 tiles; 18 blocks split 9 + 9, so a
+    # slice boundary falls inside a superblock; ragged m and n
+    (2560, 10240, 100), (1000, 10240, 70), (300, 2304, 70)])
+def test_gemm_w4_sb256_parity(n, k, m):
+    g = np.random.default_rng(n + k + m + 7)
+    w = (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
+    parts = quant.quantize(w, quant.W4_ASYM_SB256, 32)
+    qw = qweight_from_oracle(quant.W4_ASYM_SB256, 32, parts, n, k)
+    ldx = k + 8
+    x = g.standard_normal((m, ldx)).astype(np.float16)
+    y = _run(qw, x, m, ldx, n)
+    y_ref, b = ref.weight_only_ref(x[:, :k], quant.W4_ASYM_SB256, parts, 32)
+    ok, info = ref.compare(y, y_ref, b)
+    assert ok, info
+
+
+def test_gemm_w4_sb256_integer_exact():
+    """d = dmin = 1 with sub-codes sc = 1, mc = 8 give S_j = 1 and M_j = 8, so
+    w = u - 8 is exact in fp16 and every sum is an integer: the output equals
+    the integer product exactly."""
+    g = np.random.default_rng(11)
+    n, k, m = 96, 512, 70
+    u = g.integers(0, 16, (n, k))
+    nsb = k // 256
+    parts = {"qs": quant.pack_nibbles(u),
+             "d": np.ones((n, nsb), np.float16), "dmin": np.ones((n, nsb), np.float16),
+             "sub": quant.pack_sub(np.ones((n, nsb, 8), np.uint8), np.full((n, nsb, 8), 8, np.uint8))}
+    qw = qweight_from_oracle(quant.W4_ASYM_SB256, 32, parts, n, k)
+    x = g.integers(-1, 2, (m, k)).astype(np.float16)
+    y = _run(qw, x, m, k, n)
+    exact = x.astype(np.int64) @ (u - 8).astype(np.int64).T
+    assert np.abs(exact).max() <= 2048
+    assert np.array_equal(y.astype(np.float64), exact.astype(np.float64))
+
+
 @pytest.mark.parametrize("group", [64, 16])
 def test_gemm_w4_integer_exact(group):
     """A code of +-7 in every group gives scale 1 exactly, so w = q is exact in
