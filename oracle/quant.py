@@ -201,6 +201,16 @@ def quantize_sb256(w):
     s = (hi - lo) / 15.0
     s = np.where(s == 0.0, 0.0, s)
     neglo = 0.0 - lo
+    return sb256_from_group_params(wd, s, neglo)
+
+
+def sb256_from_group_params(wd, s, neglo):
+    """The superblock step of the SB256 format from each group's fp64 scale s
+    and offset magnitude -lo (both [N][nsb][8]), for weights wd
+    [N][nsb][8][32] (fp64): two-level fp16 d / dmin with 6-bit sub-codes, then
+    the codes against the effective S_j and M_j."""
+    n, nsb = wd.shape[0], wd.shape[1]
+    k = nsb * SB
     d16 = codecs.f16_encode(np.max(s, axis=2) / 63.0)
     m16 = codecs.f16_encode(np.max(neglo, axis=2) / 63.0)
     if not (np.all(np.isfinite(d16)) and np.all(np.isfinite(m16))):
