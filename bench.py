@@ -314,6 +314,22 @@ def measure_rows(gen, dev, reps=20):
         us = (time.perf_counter() - t0) * 1e6 / 5
         out[name] = {"us": round(us, 2), "GB_s_fp32_in": round(n * k * 4 / us / 1e3, 1)}
         del wf, q
+    # activation-weighted search (16 candidates per group), importance from a
+    # massive-channel batch
+    for name, fmt, group, (n, k) in (("aw w4g64 8192x2048", rq.RQ_W4_SYM, 64, (8192, 2048)),
+                                     ("aw sb256 10240x2560", rq.RQ_W4_ASYM_SB256, 32, (10240, 2560))):
+        wf = torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5)
+        xc = torch.from_numpy(synth.act_massive(256, k, cfg=2, salt=1)).to(dev).float()
+        a = (xc * xc).mean(0).contiguous()
+        q = rq.QWeight.empty(fmt, group, n, k, device=dev)
+        rq.rq_quantize_aw(wf, a, q)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            rq.rq_quantize_aw(wf, a, q)
+        us = (time.perf_counter() - t0) * 1e6 / 5
+        out[name] = {"us": round(us, 2), "GB_s_fp32_in": round(n * k * 4 / us / 1e3, 1)}
+        del wf, xc, a, q
     # SB256 products, width 2560, 32 copies of the set
     c = 2560
     sets = []

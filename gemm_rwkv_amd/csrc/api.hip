@@ -192,16 +192,19 @@ int rq_qweight_bytes(int format, int group, int64_t n, int64_t k, size_t* codes,
   return rqv::weight_bytes(format, group, n, k, codes, scales, mins, sub);
 }
 
-int rq_quantize_rtn(const float* w, const rq_qweight* out, void* stream) {
+namespace {
+// Shared path of rq_quantize_rtn and rq_quantize_aw (imp non-null).
+int quantize_impl(const float* w, const float* imp, const rq_qweight* out, void* stream) {
   if (!w) return RQ_ERR_NULL;
   int st = rqv::check_weight(out);
   if (st != RQ_OK) return st;
-  if (!rqv::aligned16(w)) return RQ_ERR_ALIGN;
+  if (!rqv::aligned16(w) || (imp && !rqv::aligned16(imp))) return RQ_ERR_ALIGN;
   Span outs[4];
   rqv::weight_spans(out, outs);
   const Span in = rqv::act_span(w, out->n, out->k, out->k, 4);
+  const Span ins = imp ? rqv::act_span(imp, 1, out->k, out->k, 4) : Span();
   for (int i = 0; i < 4; ++i)
-    if (rqv::overlaps(in, outs[i])) return RQ_ERR_ALIAS;
+    if (rqv::overlaps(in, outs[i]) || rqv::overlaps(ins, outs[i])) return RQ_ERR_ALIAS;
   for (int i = 0; i < 4; ++i)
     for (int j = i + 1; j < 4; ++j)
       if (rqv::overlaps(outs[i], outs[j])) return RQ_ERR_ALIAS;
@@ -216,10 +219,10 @@ int rq_quantize_rtn(const float* w, const rq_qweight* out, void* stream) {
       case RQ_W8_SYM:
       case RQ_W4_SYM:
         e = rq::launch_quant_sym(w, n, k, out->format == RQ_W8_SYM ? 8 : 4, out->group, out->codes,
-                                 (uint16_t*)out->scales, flags, s);
+                                 (uint16_t*)out->scales, flags, imp, s);
         break;
       case RQ_W4_ASYM_SB256:
-        e = rq::launch_quant_sb256(w, n, k, out->codes, out->scales, out->mins, out->sub, flags, s);
+        e = rq::launch_quant_sb256(w, n, k, out->codes, out->scales, out->mins, out->sub, flags, imp, s);
         break;
       case RQ_FP8_E4M3_CH:
       case RQ_I8_CH:
@@ -240,6 +243,18 @@ int rq_quantize_rtn(const float* w, const rq_qweight* out, void* stream) {
   if (host[0]) return RQ_ERR_NONFINITE;
   if (host[1]) return RQ_ERR_RANGE;
   return RQ_OK;
+}
+}  // namespace
+
+int rq_quantize_rtn(const float* w, const rq_qweight* out, void* stream) {
+  return quantize_impl(w, nullptr, out, stream);
+}
+
+int rq_quantize_aw(const float* w, const float* act_sq, const rq_qweight* out, void* stream) {
+  if (!act_sq || !out) return RQ_ERR_NULL;
+  if (out->format != RQ_W8_SYM && out->format != RQ_W4_SYM && out->format != RQ_W4_ASYM_SB256)
+    return RQ_ERR_FORMAT;
+  return quantize_impl(w, act_sq, out, stream);
 }
 
 #define RQ_GEMV_ENTRY(NAME, FORMAT, GROUP)                                                    \

@@ -165,6 +165,13 @@ __device__ __forceinline__ float group_min(float v) {
 }
 
 template <int width>
+__device__ __forceinline__ double group_sum_d(double v) {
+#pragma unroll
+  for (int o = width / 2; o > 0; o >>= 1) v = v + __shfl_xor(v, o, width);
+  return v;
+}
+
+template <int width>
 __device__ __forceinline__ double group_max_d(double v) {
 #pragma unroll
   for (int o = width / 2; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, width));

@@ -7,10 +7,12 @@
 namespace rq {
 
 // ---- quantizers (quant.hip) ------------------------------------------------
+// imp (may be null): fp32 [k] E[x^2] importances; non-null selects the
+// activation-weighted scale search instead of RTN
 hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int group, void* codes,
-                            uint16_t* scales, int* flags, hipStream_t st);
+                            uint16_t* scales, int* flags, const float* imp, hipStream_t st);
 hipError_t launch_quant_sb256(const float* w, int64_t n, int64_t k, void* qs, void* d, void* dmin,
-                              void* sub, int* flags, hipStream_t st);
+                              void* sub, int* flags, const float* imp, hipStream_t st);
 hipError_t launch_quant_rows_f32(const float* w, int64_t n, int64_t k, bool fp8, void* codes,
                                  float* scales, int* flags, hipStream_t st);
 hipError_t launch_quant_rows_f16(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, bool fp8,

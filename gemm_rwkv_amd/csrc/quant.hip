@@ -38,13 +38,48 @@ __device__ __forceinline__ void raise_flag(int* flags, int which) {
 }
 
 // ---------------------------------------------------------------------------
-// symmetric group RTN: one lane per 4 consecutive weights, G/4 lanes a group
+// activation-weighted (AW) scale search (rwkv-quant news article, "Dois
+// presets e seis tamanhos": each group's scale and offset are chosen by a
+// search weighted by E[x^2] of the input channel).  The article gives no grid:
+// here 16 steps shrink the RTN scale (or both ends of a superblock group's
+// range) by the factor 1 - t/32, each scored by sum_k a_k (w_k - w_hat_k)^2,
+// and the smallest t within (1 + 2^-40) of the lowest score is chosen (a
+// choice that does not depend on the order the score is summed in).  Step 0
+// is RTN.
 // ---------------------------------------------------------------------------
-template <int BITS, int G>
+constexpr int kAwSteps = 16;
+
+__device__ __forceinline__ int aw_choose(const double (&err)[kAwSteps]) {
+  double emin = err[0];
+#pragma unroll
+  for (int t = 1; t < kAwSteps; ++t) emin = err[t] < emin ? err[t] : emin;
+  const double thr = emin * (1.0 + 0x1p-40);
+  int pick = kAwSteps - 1;
+#pragma unroll
+  for (int t = kAwSteps - 1; t >= 0; --t)
+    if (err[t] <= thr) pick = t;
+  return pick;
+}
+
+// importances of a lane's four channels; flags a NaN, Inf or negative one
+__device__ __forceinline__ float4 aw_importance(const float* imp, int64_t k, bool active, int* flags) {
+  const float4 a = active ? *(const float4*)(imp + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool ok = finite_f32(a.x) && finite_f32(a.y) && finite_f32(a.z) && finite_f32(a.w) && a.x >= 0.f &&
+                  a.y >= 0.f && a.z >= 0.f && a.w >= 0.f;
+  if (!ok) raise_flag(flags, 0);
+  return a;
+}
+
+// ---------------------------------------------------------------------------
+// symmetric group RTN: one lane per 4 consecutive weights, G/4 lanes a group
+// (AW: the scale comes from the search above; imp is fp32 [K])
+// ---------------------------------------------------------------------------
+template <int BITS, int G, bool AW>
 __global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict__ w, int64_t total4,
                                                         void* __restrict__ codes,
                                                         uint16_t* __restrict__ scales,
-                                                        int* __restrict__ flags) {
+                                                        int* __restrict__ flags, const float* __restrict__ imp,
+                                                        int64_t K) {
   constexpr int LPG = G / 4;
   constexpr int Q = (1 << (BITS - 1)) - 1;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -54,7 +89,30 @@ __global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict
   if (!fin) raise_flag(flags, 0);
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   a = group_max<LPG>(a);
-  const uint16_t sbits = f64_to_f16_bits((double)a / (double)Q);
+  uint16_t sbits;
+  if constexpr (AW) {
+    const float4 av = aw_importance(imp, (t * 4) % K, active, flags);
+    const float e4[4] = {v.x, v.y, v.z, v.w}, a4[4] = {av.x, av.y, av.z, av.w};
+    const double base = (double)a / (double)Q;
+    if (f64_to_f16_bits(base) == 0x7c00u) raise_flag(flags, 1);  // step 0 overflows iff any step does
+    double err[kAwSteps];
+#pragma unroll
+    for (int st = 0; st < kAwSteps; ++st) {
+      const double s = f16_bits_to_f64(f64_to_f16_bits(base * (1.0 - st / 32.0)));
+      double e = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double r = s == 0.0 ? 0.0 : __builtin_rint((double)e4[i] / s);
+        r = r > (double)Q ? (double)Q : (r < -(double)Q ? -(double)Q : r);
+        const double d = (double)e4[i] - r * s;
+        e = e + (double)a4[i] * (d * d);
+      }
+      err[st] = group_sum_d<LPG>(e);
+    }
+    sbits = f64_to_f16_bits(base * (1.0 - aw_choose(err) / 32.0));
+  } else {
+    sbits = f64_to_f16_bits((double)a / (double)Q);
+  }
   if (sbits == 0x7c00u) raise_flag(flags, 1);
   const double s = f16_bits_to_f64(sbits);
   int q[4];
@@ -79,12 +137,14 @@ __global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict
 // ---------------------------------------------------------------------------
 // asymmetric 4-bit superblocks: one wave per 256 weights, 8 lanes per group
 // ---------------------------------------------------------------------------
+template <bool AW>
 __global__ void __launch_bounds__(256) quant_sb256_kernel(const float4* __restrict__ w, int64_t nsb,
                                                           uint32_t* __restrict__ qs,
                                                           uint16_t* __restrict__ dout,
                                                           uint16_t* __restrict__ mout,
                                                           uint32_t* __restrict__ sub,
-                                                          int* __restrict__ flags) {
+                                                          int* __restrict__ flags, const float* __restrict__ imp,
+                                                          int64_t K) {
   const int lane = threadIdx.x & 63;
   const int64_t sbi = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
   if (sbi >= nsb) return;  // uniform per wave
@@ -93,9 +153,40 @@ __global__ void __launch_bounds__(256) quant_sb256_kernel(const float4* __restri
   if (!fin) raise_flag(flags, 0);
   float hi = group_max<8>(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
   float lo = fminf(0.f, group_min<8>(fminf(fminf(v.x, v.y), fminf(v.z, v.w))));
-  double s = ((double)hi - (double)lo) / 15.0;
-  if (s == 0.0) s = 0.0;  // a zero range is +0
-  const double nl = 0.0 - (double)lo;
+  double s, nl;
+  if constexpr (AW) {
+    // the group's range ends scaled toward zero, scored with the unquantized
+    // scale s_t and offset m_t; the chosen pair goes through the superblock step
+    const float4 av = aw_importance(imp, (sbi * 256 + lane * 4) % K, true, flags);
+    const float e4[4] = {v.x, v.y, v.z, v.w}, a4[4] = {av.x, av.y, av.z, av.w};
+    double err[kAwSteps];
+#pragma unroll
+    for (int st = 0; st < kAwSteps; ++st) {
+      const double f = 1.0 - st / 32.0;
+      const double lo_t = (double)lo * f, hi_t = (double)hi * f;
+      double sv = (hi_t - lo_t) / 15.0;
+      if (sv == 0.0) sv = 0.0;
+      const double mv = 0.0 - lo_t;
+      double e = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        double u = sv == 0.0 ? 0.0 : __builtin_rint(((double)e4[i] + mv) / sv);
+        u = u < 0.0 ? 0.0 : (u > 15.0 ? 15.0 : u);
+        const double d = (double)e4[i] - (sv * u - mv);
+        e = e + (double)a4[i] * (d * d);
+      }
+      err[st] = group_sum_d<8>(e);
+    }
+    const double f = 1.0 - aw_choose(err) / 32.0;
+    const double lo_t = (double)lo * f, hi_t = (double)hi * f;
+    s = (hi_t - lo_t) / 15.0;
+    if (s == 0.0) s = 0.0;
+    nl = 0.0 - lo_t;
+  } else {
+    s = ((double)hi - (double)lo) / 15.0;
+    if (s == 0.0) s = 0.0;  // a zero range is +0
+    nl = 0.0 - (double)lo;
+  }
   const double smax = group_max_d<64>(s);
   const double nlmax = group_max_d<64>(nl);
   const uint16_t db = f64_to_f16_bits(smax / 63.0);
@@ -287,16 +378,20 @@ __global__ void __launch_bounds__(256) to_f16_kernel(const float* __restrict__ w
 static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int group, void* codes,
-                            uint16_t* scales, int* flags, hipStream_t st) {
+                            uint16_t* scales, int* flags, const float* imp, hipStream_t st) {
   const int64_t total4 = n * k / 4;
   if (total4 == 0) return hipSuccess;
   const dim3 grid(grid_for(total4)), block(256);
   const float4* w4 = (const float4*)w;
-#define RQ_SYM_CASE(B, G)                                                                   \
-  if (bits == B && group == G) {                                                            \
-    hipLaunchKernelGGL((quant_sym_kernel<B, G>), grid, block, 0, st, w4, total4, codes, scales, \
-                       flags);                                                              \
-    return hipGetLastError();                                                               \
+#define RQ_SYM_CASE(B, G)                                                                          \
+  if (bits == B && group == G) {                                                                   \
+    if (imp)                                                                                       \
+      hipLaunchKernelGGL((quant_sym_kernel<B, G, true>), grid, block, 0, st, w4, total4, codes,    \
+                         scales, flags, imp, k);                                                   \
+    else                                                                                           \
+      hipLaunchKernelGGL((quant_sym_kernel<B, G, false>), grid, block, 0, st, w4, total4, codes,   \
+                         scales, flags, imp, k);                                                   \
+    return hipGetLastError();                                                                      \
   }
   RQ_SYM_CASE(8, 16)
   RQ_SYM_CASE(8, 32)
@@ -309,11 +404,15 @@ hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int 
 }
 
 hipError_t launch_quant_sb256(const float* w, int64_t n, int64_t k, void* qs, void* d, void* dmin,
-                              void* sub, int* flags, hipStream_t st) {
+                              void* sub, int* flags, const float* imp, hipStream_t st) {
   const int64_t nsb = n * k / 256;
   if (nsb == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_sb256_kernel, dim3(grid_for(nsb * 64)), dim3(256), 0, st, (const float4*)w,
-                     nsb, (uint32_t*)qs, (uint16_t*)d, (uint16_t*)dmin, (uint32_t*)sub, flags);
+  if (imp)
+    hipLaunchKernelGGL(quant_sb256_kernel<true>, dim3(grid_for(nsb * 64)), dim3(256), 0, st, (const float4*)w,
+                       nsb, (uint32_t*)qs, (uint16_t*)d, (uint16_t*)dmin, (uint32_t*)sub, flags, imp, k);
+  else
+    hipLaunchKernelGGL(quant_sb256_kernel<false>, dim3(grid_for(nsb * 64)), dim3(256), 0, st, (const float4*)w,
+                       nsb, (uint32_t*)qs, (uint16_t*)d, (uint16_t*)dmin, (uint32_t*)sub, flags, imp, k);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ EXPORTS = (
     "rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16", "rq_gemv_w8g32",
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
-    "rq_gemm_w4",
+    "rq_gemm_w4", "rq_quantize_aw",
 )
 
 
@@ -69,6 +69,7 @@ def lib():
             "rq_status_str": ([i32], ctypes.c_char_p),
             "rq_qweight_bytes": ([i32, i32, i64, i64] + [ctypes.POINTER(ctypes.c_size_t)] * 4, i32),
             "rq_quantize_rtn": ([vp, qp, vp], i32),
+            "rq_quantize_aw": ([vp, vp, qp, vp], i32),
             "rq_gemm_small_m": ([vp, i64, i64, qp, vp, i64, vp], i32),
             "rq_gemm_w4": ([vp, i64, i64, qp, vp, i64, vp], i32),
             "rq_fused_rkv": ([vp, vp, vp, i64, i64, qp, qp, qp, vp, vp, vp, i64, vp], i32),
@@ -169,11 +170,28 @@ def rq_quantize_rtn(w, out, stream=None):
     return out
 
 
+def rq_quantize_aw(w, act_sq, out, stream=None):
+    """Activation-weighted quantization of fp32 device weights w[n][k] with
+    per-channel E[x^2] importances act_sq[k] (fp32, device) into ``out``
+    (synchronizes)."""
+    d = out.desc()
+    st = lib().rq_quantize_aw(_ptr(w), _ptr(act_sq), ctypes.byref(d), _stream(stream))
+    _check(st, "rq_quantize_aw")
+    return out
+
+
 def quantize(w, fmt, group=0, stream=None):
     """Allocate a QWeight for fp32 device weights w and fill it with rq_quantize_rtn."""
     n, k = w.shape
     q = QWeight.empty(fmt, group, n, k, device=w.device)
     return rq_quantize_rtn(w, q, stream)
+
+
+def quantize_aw(w, act_sq, fmt, group=0, stream=None):
+    """Allocate a QWeight for fp32 device weights w and fill it with rq_quantize_aw."""
+    n, k = w.shape
+    q = QWeight.empty(fmt, group, n, k, device=w.device)
+    return rq_quantize_aw(w, act_sq, q, stream)
 
 
 # --------------------------------------------------------------------------

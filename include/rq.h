@@ -166,6 +166,23 @@ int rq_qweight_bytes(int format, int group, int64_t n, int64_t k, size_t *codes_
  * buffers hold unspecified bytes.  RQ_F16 converts to fp16 (RNE). */
 int rq_quantize_rtn(const float *w, const rq_qweight *out, void *stream);
 
+/* Activation-weighted quantization (rwkv-quant news article, section "Dois
+ * presets e seis tamanhos": group scales and offsets chosen by a search
+ * weighted by E[x^2] of each input channel).  act_sq[k] (device fp32,
+ * 16-byte aligned, finite and >= 0) is that mean square per input channel.
+ * For each group, 16 candidates shrink the RTN scale (symmetric formats: the
+ * fp16 scale absmax/Q times 1 - t/32, t = 0..15) or both ends of the RTN
+ * range (RQ_W4_ASYM_SB256: lo and hi times 1 - t/32, scored with the
+ * unquantized scale and offset) and are scored by sum a_k (w_k - w_hat_k)^2
+ * in fp64; the smallest t within a factor 1 + 2^-40 of the lowest score is
+ * kept (step 0 is RTN, so an all-zero act_sq gives rq_quantize_rtn's bytes).
+ * Superblock weights then take the RTN superblock step with the chosen group
+ * parameters.  Formats: RQ_W8_SYM, RQ_W4_SYM, RQ_W4_ASYM_SB256, else
+ * RQ_ERR_FORMAT.  Synchronization, allocation and errors as rq_quantize_rtn;
+ * a NaN, Inf or negative act_sq entry gives RQ_ERR_NONFINITE.  act_sq may
+ * not overlap an output buffer (RQ_ERR_ALIAS). */
+int rq_quantize_aw(const float *w, const float *act_sq, const rq_qweight *out, void *stream);
+
 /* M = 1 products y[n] = sum_k x[k] * W_hat[n][k], fp32 accumulation, fp16
  * output (RNE).  x: fp16 [k]; y: fp16 [n].  Each entry point accepts exactly
  * its format and group (RQ_ERR_FORMAT otherwise):

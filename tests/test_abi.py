@@ -231,3 +231,21 @@ def test_host_convert_e4m3_against_torch():
     # saturation and signed zero (torch does not saturate, so hand values)
     got = rq.rq_host_convert(2, np.array([449.0, 464.0, 1e9, -1e9, -0.0, -1e-30]))
     assert got.tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x80]
+
+
+def test_quantize_aw_validation():
+    qw = _w(rq.RQ_W4_SYM, 64, 16, 128, B, C)
+    imp = A + 0x100000
+    assert _status(rq.rq_quantize_aw, A, 0, qw) == rq.RQ_ERR_NULL
+    assert _status(rq.rq_quantize_aw, 0, imp, qw) == rq.RQ_ERR_NULL
+    assert _status(rq.rq_quantize_aw, A, imp, _w(rq.RQ_FP8_E4M3_CH, 0, 16, 128, B, C)) == rq.RQ_ERR_FORMAT
+    assert _status(rq.rq_quantize_aw, A, imp, _w(rq.RQ_I8_CH, 0, 16, 128, B, C)) == rq.RQ_ERR_FORMAT
+    assert _status(rq.rq_quantize_aw, A, imp, _w(rq.RQ_F16, 0, 16, 128, B)) == rq.RQ_ERR_FORMAT
+    assert _status(rq.rq_quantize_aw, A, imp + 4, qw) == rq.RQ_ERR_ALIGN
+    assert _status(rq.rq_quantize_aw, A + 4, imp, qw) == rq.RQ_ERR_ALIGN
+    assert _status(rq.rq_quantize_aw, A, B + 0x10, qw) == rq.RQ_ERR_ALIAS      # act_sq inside the codes
+    assert _status(rq.rq_quantize_aw, A, C, qw) == rq.RQ_ERR_ALIAS             # act_sq on the scales
+    assert _status(rq.rq_quantize_aw, A, imp, _w(rq.RQ_W4_SYM, 64, 16, 100, B, C)) == rq.RQ_ERR_SHAPE
+    sb = _w(rq.RQ_W4_ASYM_SB256, 32, 4, 384, B, C, C + 0x1000, C + 0x2000)
+    assert _status(rq.rq_quantize_aw, A, imp, sb) == rq.RQ_ERR_SHAPE         # K % 256
+    rq.rq_quantize_aw(A, imp, _w(n=0, codes=B, scales=C))                    # empty: no-op

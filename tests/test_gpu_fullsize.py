@@ -287,3 +287,34 @@ def test_head_4096x65536(m):
     parts = {"codes": w[rows].astype(np.float16)}
     assert np.array_equal(host(qw.codes, np.uint16)[: n * k].reshape(n, k)[rows], parts["codes"].view(np.uint16))
     _compare_rows(host(y, np.float16).reshape(m, n), rows, x, quant.F16, parts, 0, "head")
+
+
+@pytest.mark.parametrize("fmt,group,n,k,mat", [(quant.W4_SYM, 64, 4096, 4096, synth.MAT_O),
+                                               (quant.W4_ASYM_SB256, 32, 2560, 10240, synth.MAT_VALUE),
+                                               (quant.W8_SYM, 32, 10240, 2560, synth.MAT_KEY)])
+def test_quantize_aw_fullsize(fmt, group, n, k, mat):
+    """rq_quantize_aw on whole matrices of the 2.9B and 4096-wide layers with
+    E[x^2] from a massive-channel calibration batch; the sampled rows' bytes
+    equal the oracle's AW search of those rows (each row depends on itself
+    and the shared importance only)."""
+    from oracle import aw
+    w = synth.weight(2, 3, mat, n, k)
+    xc = synth.act_massive(256, k, cfg=2, salt=11).astype(np.float64)
+    a = np.mean(xc * xc, axis=0).astype(np.float32)
+    say("quantize_aw full", fmt, group, n, k)
+    qw = rq.quantize_aw(dev_f32(w), dev_f32(a), fmt, group)
+    torch.cuda.synchronize()
+    rows = _rows(n, 77)
+    parts = aw.quantize_aw(w[rows], a, fmt, group)
+    assert np.any(parts["t"] > 0)
+    got = qw.buffers()
+    if fmt == quant.W4_ASYM_SB256:
+        nsb = k // 256
+        pairs = (("codes", parts["qs"], k // 2), ("scales", parts["d"], nsb * 2),
+                 ("mins", parts["dmin"], nsb * 2), ("sub", parts["sub"], nsb * 12))
+    else:
+        cb = k // 2 if fmt == quant.W4_SYM else k
+        pairs = (("codes", parts["codes"], cb), ("scales", parts["scales"], (k // group) * 2))
+    for name, want, row_bytes in pairs:
+        g = host(got[name], np.uint8).reshape(n, row_bytes)[rows]
+        assert np.array_equal(g, np.ascontiguousarray(want).reshape(len(rows), -1).view(np.uint8)), name
