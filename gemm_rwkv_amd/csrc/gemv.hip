@@ -508,27 +508,80 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
 
   // 1. the workgroup's activation slice: rows < M, 64 blocks of 8 halves per
   //    copy instruction, copy instructions dealt round-robin to the waves.
-  //    These LDS DMA reads go out first and as inline asm: the compiler,
+  //    The copies are LDS DMA reads written as inline asm: the compiler,
   //    which cannot tell which LDS bytes a DMA writes, would otherwise wait
   //    for every load in flight (the code loads included) before the first
-  //    LDS read.  They write no register.
+  //    LDS read.  They write no register.  The issue loop is the copy's cost
+  //    at M = 32 (a workgroup issues M * K / 512 of them), so it walks
+  //    (row, block) with increments and no per-copy division or lane test
+  //    when every copy is whole.  For two activation tiles (M > 16) the code
+  //    loads, which come from HBM and take longer, go out first so that their
+  //    latency covers that loop; for one tile the copies go out first and
+  //    each chunk's compute waits only for its own code load.
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
-  {
+  auto copy_x = [&]() {
     const int blocks = (cend - cbeg) * (F::CK / 8);
-    const int per_row = (blocks + 63) / 64;
-    const uint16_t* xs = A.x + (size_t)cbeg * F::CK;
-    for (int q = wave; q < M * per_row; q += NW) {
-      const int m = q / per_row;
-      const int b0 = (q - m * per_row) * 64;
-      const int b = b0 + lane;
-      if (b < blocks) {
-        const uint16_t* g = xs + (size_t)m * p.ldx + (size_t)b * 8;
+    const int per_row = (blocks + 63) >> 6;
+    if constexpr (MR == 1) {  // one activation row (M = 1): wave w copies blocks w, w + NW, ...
+      const uint8_t* xs = (const uint8_t*)(A.x + (size_t)cbeg * F::CK) + lane * 16;
+      for (int col = wave; col < per_row; col += NW)
+        if (col * 64 + lane < blocks)
+          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                       :: "v"(xs + col * 1024), "s"(lds_base + (uint32_t)col * 1024u) : "memory", "m0");
+      for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
+      return;
+    }
+    int m, col, dm, dc;
+    if ((per_row & (per_row - 1)) == 0) {  // the usual case: shifts, no division
+      const int sh = __builtin_ctz((unsigned)per_row);
+      m = wave >> sh;
+      col = wave & (per_row - 1);
+      dm = NW >> sh;
+      dc = NW & (per_row - 1);
+    } else {
+      m = wave / per_row;
+      col = wave - m * per_row;
+      dm = NW / per_row;
+      dc = NW - dm * per_row;
+    }
+    const uint32_t lrow = (uint32_t)ldl * 2u;     // LDS bytes per row
+    const uint32_t grow = (uint32_t)p.ldx * 2u;   // global bytes per row (M * ldx < 2^31)
+    const uint8_t* xs = (const uint8_t*)(A.x + (size_t)cbeg * F::CK) + lane * 16;
+    uint32_t goff = (uint32_t)m * grow + (uint32_t)col * 1024u;  // byte offsets of this copy
+    uint32_t loff = lds_base + (uint32_t)m * lrow + (uint32_t)col * 1024u;
+    const uint32_t gstep = (uint32_t)dm * grow + (uint32_t)dc * 1024u;
+    const uint32_t lstep = (uint32_t)dm * lrow + (uint32_t)dc * 1024u;
+    const uint32_t gwrap = grow - (uint32_t)per_row * 1024u, lwrap = lrow - (uint32_t)per_row * 1024u;
+#define RQ_COPY_STEP                                   \
+  col += dc;                                           \
+  m += dm;                                             \
+  goff += gstep;                                       \
+  loff += lstep;                                       \
+  if (col >= per_row) {                                \
+    col -= per_row;                                    \
+    ++m;                                               \
+    goff += gwrap;                                     \
+    loff += lwrap;                                     \
+  }
+    if ((blocks & 63) == 0) {
+      while (m < M) {
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :: "v"(g), "s"(lds_base + (uint32_t)((m * ldl + b0 * 8) * 2)) : "memory", "m0");
+                     :: "v"(xs + goff), "s"(loff) : "memory", "m0");
+        RQ_COPY_STEP
+      }
+    } else {
+      while (m < M) {
+        if (col * 64 + lane < blocks)
+          asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                       :: "v"(xs + goff), "s"(loff) : "memory", "m0");
+        RQ_COPY_STEP
       }
     }
+#undef RQ_COPY_STEP
     for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
-  }
+  };
+  constexpr bool kCodesFirst = MT == 2;
+  if constexpr (!kCodesFirst) copy_x();
 
   // 2. this wave's codes and scales, all at once.  Chunks outside the slice
   //    (or of a tile past the matrix) read zero codes; their scales are zeroed
@@ -578,12 +631,17 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   // code load is issued
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. wait for this wave's copies only: with at most CPW loads still in
-  //    flight, every DMA issued before the CPW code loads has landed (a
-  //    wave's vector loads complete in issue order).  Then a plain barrier;
-  //    the code loads stay in flight, and each chunk below waits only for
-  //    its own load.
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(CPW) : "memory");
+  // 3. wait for this wave's copies.  Copies first: with at most CPW loads
+  //    still in flight, every DMA issued before the CPW code loads has landed
+  //    (a wave's vector loads complete in issue order), and each chunk below
+  //    waits only for its own code load.  Codes first: everything.  Then a
+  //    plain barrier.
+  if constexpr (kCodesFirst) {
+    copy_x();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(CPW) : "memory");
+  }
 
   int xrow[MT];
 #pragma unroll
@@ -730,10 +788,14 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
   constexpr int E = MT * 4 * 64;
   const int ent = sp.rt * E;
   const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
-  // ent is a multiple of 256, so a block lies inside one tile group
-  const int gall = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 256) / ent);
-  if (gall >= gtot) return;
-  const int idx = (int)(blockIdx.x * 256 + threadIdx.x) - gall * ent;
+  // block b = j * gtot + gall sums outputs j * 256 ... of tile group gall
+  // (ent is a multiple of 256).  Workgroups are dealt to the eight XCDs
+  // round-robin, so with gtot % 8 == 0 this block runs on the XCD whose L2
+  // holds the partial tiles (written by blocks s * gtot + gall).
+  const int j = __builtin_amdgcn_readfirstlane((int)blockIdx.x / gtot);
+  const int gall = (int)blockIdx.x - j * gtot;
+  if (j * 256 >= ent) return;
+  const int idx = j * 256 + (int)threadIdx.x;
   // every slice's load is issued before the first add (slices past the split
   // read zero through an out-of-range offset); the adds run in slice order
   constexpr uint32_t kOOB = 0x7ffff000u;
@@ -786,7 +848,9 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
   // of the compute units
   {
     const size_t xb = (size_t)(b.m + 1) * (nchunks * F::CK + 8) * 2;
-    const int cpw = pick_cpw(nchunks, mt == 1 && FMT != GF_SB);
+    // two activation tiles over a short K: eight waves of two chunks issue
+    // the activation copies twice as fast as four of four
+    const int cpw = (mt == 2 && nchunks <= 16) ? 2 : pick_cpw(nchunks, mt == 1 && FMT != GF_SB);
     const int wpt = (nchunks + cpw - 1) / cpw;
     int tiles = 0;
     for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
@@ -874,7 +938,7 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
     hipLaunchKernelGGL((gemv5_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b, sp);         \
   } while (0)
   if (mt == 2) {
-    if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
+    if (cpw == 2) RQ_L5(2, 2, 4); else if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
   } else if constexpr (FMT == GF_SB) {
     if (b.m == 1) {
       if (cpw == 4) RQ_L5(1, 4, 1); else RQ_L5(1, 8, 1);
