@@ -79,8 +79,7 @@ def quantize_sym_aw(w, a, bits, group):
     w = np.asarray(w, dtype=np.float32)
     quant._check_finite(w)
     n, k = w.shape
-    if bits not in (4, 8) or group not in (16, 32, 64) or k % group:
-        raise ValueError("unsupported bits/group/shape")
+    quant.check_sym_shape(bits, group, k)
     ad = _check_importance(a, k).reshape(1, k // group, group)
     qmax = quant._qmax(bits)
     wd = w.astype(np.float64).reshape(n, k // group, group)
@@ -101,7 +100,10 @@ def quantize_sym_aw(w, a, bits, group):
     s16 = np.take_along_axis(np.stack(s16), t[None], axis=0)[0]
     s = s16.astype(np.float64)[:, :, None]
     q = _sym_codes(wd, s, qmax).astype(np.int8).reshape(n, k)
-    return {"codes": quant.pack_sym(q, bits), "scales": s16, "q": q, "t": t, "err": err}
+    out = quant.sym_parts(q, s16, bits)
+    out["t"] = t
+    out["err"] = err
+    return out
 
 
 def quantize_sb256_aw(w, a):
@@ -143,10 +145,8 @@ def quantize_sb256_aw(w, a):
 
 def quantize_aw(w, a, fmt, group=0):
     """AW quantization of fp32 W[N][K] with importance a[K] into ``fmt``."""
-    if fmt == quant.W8_SYM:
-        return quantize_sym_aw(w, a, 8, group)
-    if fmt == quant.W4_SYM:
-        return quantize_sym_aw(w, a, 4, group)
+    if fmt in quant.SYM_BITS:
+        return quantize_sym_aw(w, a, quant.SYM_BITS[fmt], group)
     if fmt == quant.W4_ASYM_SB256:
         return quantize_sb256_aw(w, a)
     raise ValueError("AW search covers the symmetric and superblock formats")

@@ -42,6 +42,42 @@ def f16_from_bits(bits):
 
 
 # --------------------------------------------------------------------------
+# bfloat16
+# --------------------------------------------------------------------------
+# bfloat16 keeps fp32's sign and 8-bit exponent and the top 7 stored mantissa
+# bits.  Every finite fp32 value lies between two consecutive bfloat16 values
+# (its top 16 bits, and the next one up in magnitude); the encoder picks the
+# nearer, and the one with an even last mantissa bit on a tie.  Distances are
+# exact in fp64.  A value that rounds up past the largest finite bfloat16 gives
+# infinity (0x7F80 / 0xFF80).
+
+
+def bf16_decode(bits):
+    """uint16 bfloat16 patterns -> fp64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_encode(v):
+    """Values exactly representable in fp32 -> nearest bfloat16 bits (uint16)."""
+    f = np.asarray(v, dtype=np.float64)
+    f32 = f.astype(np.float32)
+    if not np.array_equal(f32.astype(np.float64), f, equal_nan=True):
+        raise ValueError("bf16_encode takes values representable in fp32")
+    bits = f32.view(np.uint32)
+    lo = (bits >> 16).astype(np.uint16)              # truncation toward zero
+    hi = (lo + 1).astype(np.uint16)                  # next magnitude up
+    a = np.abs(f)
+    dlo = a - np.abs(bf16_decode(lo))
+    # past the largest finite value the next magnitude is 2**128 (the
+    # rounding is done as if the exponent were unbounded; picking it overflows)
+    hv = np.where((hi & 0x7FFF) == 0x7F80, 2.0 ** 128, np.abs(bf16_decode(hi)))
+    dhi = hv - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((lo & 1) == 1))
+    return np.where(pick_hi, hi, lo).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
 # e4m3fn
 # --------------------------------------------------------------------------
 

@@ -39,6 +39,30 @@ W4_ASYM_SB256
     dmin fp16 [N][K/256], sub uint8 [N][K/256][12] = a little-endian 96-bit
     stream with sc_j at bit 6j and mc_j at bit 48 + 6j.
 
+W6_SYM / W5_SYM, group G in {32, 64}
+    The 6- and 5-bit widths of the presets (news article, "Dois presets e seis
+    tamanhos": channel-mix weights at 6 bits in one preset; channel-mix key and
+    head at 5 bits in the other).  The article gives their widths only; the
+    reading here is the symmetric group rule above at b = 6 / 5 (Q = 31 / 15,
+    s = fp16(absmax / Q)), with codes stored in two planes so that the 4-bit
+    machinery reads the low plane unchanged.  Offset binary u = q + 2**(b-1)
+    (1..63 or 1..31).  Low plane: u & 15 as pack_nibbles, uint8 [N][K/2].
+    High plane (pack_hi): for every 8-k word w, the high bits u >> 4 of
+    k = 8w + 2i (even) and 8w + 2i + 1 (odd), i = 0..3:
+      6-bit: one little-endian uint16 per word, nibble i = hi(even) | hi(odd) << 2
+             -> uint16 [N][K/8];
+      5-bit: one byte per word, bit i = hi(even), bit 4 + i = hi(odd)
+             -> uint8 [N][K/8].
+    Scales fp16 [N][K/G].  ("parity unpinned by the pages"; pinned by brute
+    force, exact round trips and a hand-derived layout fixture.)
+
+BF16
+    Plain bfloat16 weights (news article, "Onde o 2.9B quebra": the layer-0
+    output projection kept in bf16): the nearest bfloat16 (8-bit significand,
+    fp32's exponent range) to each fp32 weight, ties to even; uint16 bits
+    [N][K].  A weight that rounds past the largest finite bfloat16 raises
+    OverflowError.
+
 FP8_E4M3_CH / I8_CH
     Per-output-channel scale in fp32, FP8 e4m3fn or int8 codes ("RWKV-7
     Quantization Toolkit", Key Design: FP8 weights on FP8 tensor cores, INT8
@@ -64,6 +88,11 @@ W4_ASYM_SB256 = 3
 FP8_E4M3_CH = 4
 I8_CH = 5
 F16 = 6
+W5_SYM = 7
+W6_SYM = 8
+BF16 = 9
+
+SYM_BITS = {W8_SYM: 8, W6_SYM: 6, W5_SYM: 5, W4_SYM: 4}
 
 SB = 256          # superblock length
 SB_GROUP = 32     # group length inside a superblock
@@ -103,8 +132,7 @@ def quantize_sym(w, bits, group):
     w = np.asarray(w, dtype=np.float32)
     _check_finite(w)
     n, k = w.shape
-    if bits not in (4, 8) or group not in (16, 32, 64) or k % group:
-        raise ValueError("unsupported bits/group/shape")
+    check_sym_shape(bits, group, k)
     qmax = _qmax(bits)
     wd = w.astype(np.float64).reshape(n, k // group, group)
     absmax = np.max(np.abs(wd), axis=2)
@@ -115,7 +143,23 @@ def quantize_sym(w, bits, group):
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.clip(_rne(wd / s), -qmax, qmax)
     q = np.where(s == 0.0, 0.0, q).astype(np.int8).reshape(n, k)
-    return {"codes": pack_sym(q, bits), "scales": s16, "q": q}
+    return sym_parts(q, s16, bits)
+
+
+def check_sym_shape(bits, group, k):
+    """Raise ValueError unless (bits, group, K) is a symmetric group format."""
+    groups = (16, 32, 64) if bits in (4, 8) else (32, 64)
+    if bits not in (4, 5, 6, 8) or group not in groups or k % group or k % 8:
+        raise ValueError("unsupported bits/group/shape")
+
+
+def sym_parts(q, s16, bits):
+    """The stored buffers of symmetric codes q [N][K] with fp16 scales s16:
+    dict(codes, scales, q), plus ``hi`` (the high plane) at 5 and 6 bits."""
+    out = {"codes": pack_sym(q, bits), "scales": s16, "q": q}
+    if bits in (5, 6):
+        out["hi"] = pack_hi((np.asarray(q).astype(np.int16) + (1 << (bits - 1))).astype(np.uint8), bits)
+    return out
 
 
 def pack_nibbles(u):
@@ -155,22 +199,61 @@ def unpack_nibbles(c):
 
 
 def pack_sym(q, bits):
-    """Unpacked int codes [N][K] -> stored layout (int8, or int4 offset nibbles)."""
+    """Unpacked int codes [N][K] -> stored code layout: int8, or the low-nibble
+    plane of the offset codes u = q + 2**(b-1) (all of u at 4 bits)."""
     q = np.asarray(q)
     if bits == 8:
         return q.astype(np.int8)
-    return pack_nibbles((q.astype(np.int16) + 8).astype(np.uint8))
+    u = (q.astype(np.int16) + (1 << (bits - 1))).astype(np.uint8)
+    return pack_nibbles(u & 0xF)
 
 
-def unpack_sym(codes, bits):
+def pack_hi(u, bits):
+    """High plane of 5/6-bit offset codes u [N][K] (see W6_SYM / W5_SYM)."""
+    u = np.asarray(u, dtype=np.uint8)
+    n, k = u.shape
+    h = (u >> 4).reshape(n, k // 8, 8).astype(np.uint16)
+    if bits == 6:
+        out = np.zeros((n, k // 8), dtype=np.uint16)
+        for i in range(4):
+            out |= (h[..., 2 * i] | (h[..., 2 * i + 1] << 2)) << (4 * i)
+        return out
+    if bits == 5:
+        out = np.zeros((n, k // 8), dtype=np.uint16)
+        for i in range(4):
+            out |= (h[..., 2 * i] << i) | (h[..., 2 * i + 1] << (4 + i))
+        return out.astype(np.uint8)
+    raise ValueError("high plane exists at 5 and 6 bits only")
+
+
+def unpack_hi(hi, bits, k):
+    """High plane -> the high bits u >> 4 [N][K] (uint8)."""
+    hi = np.asarray(hi)
+    n = hi.shape[0]
+    hv = hi.reshape(n, k // 8).astype(np.uint16)
+    h = np.empty((n, k // 8, 8), dtype=np.uint8)
+    for i in range(4):
+        if bits == 6:
+            h[..., 2 * i] = (hv >> (4 * i)) & 3
+            h[..., 2 * i + 1] = (hv >> (4 * i + 2)) & 3
+        else:
+            h[..., 2 * i] = (hv >> i) & 1
+            h[..., 2 * i + 1] = (hv >> (4 + i)) & 1
+    return h.reshape(n, k)
+
+
+def unpack_sym(codes, bits, hi=None):
     """Stored layout -> unpacked int codes [N][K] (int8)."""
     if bits == 8:
         return np.asarray(codes).view(np.int8)
-    return (unpack_nibbles(codes).astype(np.int16) - 8).astype(np.int8)
+    u = unpack_nibbles(codes).astype(np.int16)
+    if bits in (5, 6):
+        u = u | (unpack_hi(hi, bits, u.shape[1]).astype(np.int16) << 4)
+    return (u - (1 << (bits - 1))).astype(np.int8)
 
 
-def dequant_sym(codes, scales, bits, group):
-    q = unpack_sym(codes, bits).astype(np.float64)
+def dequant_sym(codes, scales, bits, group, hi=None):
+    q = unpack_sym(codes, bits, hi).astype(np.float64)
     n, k = q.shape
     s = np.asarray(scales, dtype=np.float16).astype(np.float64)
     return (q.reshape(n, k // group, group) * s[:, :, None]).reshape(n, k)
@@ -328,12 +411,20 @@ def dequant_rows(codes, scales, kind):
 # --------------------------------------------------------------------------
 
 
+def quantize_bf16(w):
+    """fp32 W -> bfloat16 bits (uint16), nearest with ties to even."""
+    w = np.asarray(w, dtype=np.float32)
+    _check_finite(w)
+    b = codecs.bf16_encode(w.astype(np.float64))
+    if np.any((b & 0x7FFF) == 0x7F80):
+        raise OverflowError("bfloat16 overflow")
+    return {"codes": b}
+
+
 def quantize(w, fmt, group=0):
     """Quantize fp32 W[N][K] into format ``fmt``; returns a dict of buffers."""
-    if fmt == W8_SYM:
-        return quantize_sym(w, 8, group)
-    if fmt == W4_SYM:
-        return quantize_sym(w, 4, group)
+    if fmt in SYM_BITS:
+        return quantize_sym(w, SYM_BITS[fmt], group)
     if fmt == W4_ASYM_SB256:
         return quantize_sb256(w)
     if fmt == FP8_E4M3_CH:
@@ -342,15 +433,15 @@ def quantize(w, fmt, group=0):
         return quantize_rows(np.asarray(w, dtype=np.float32), "int8")
     if fmt == F16:
         return {"codes": np.asarray(w, dtype=np.float16)}
+    if fmt == BF16:
+        return quantize_bf16(w)
     raise ValueError("unknown format")
 
 
 def dequant(fmt, parts, group=0):
     """Dequantize a dict of buffers (as returned by ``quantize``) to fp64 W_hat."""
-    if fmt == W8_SYM:
-        return dequant_sym(parts["codes"], parts["scales"], 8, group)
-    if fmt == W4_SYM:
-        return dequant_sym(parts["codes"], parts["scales"], 4, group)
+    if fmt in SYM_BITS:
+        return dequant_sym(parts["codes"], parts["scales"], SYM_BITS[fmt], group, parts.get("hi"))
     if fmt == W4_ASYM_SB256:
         return dequant_sb256(parts["qs"], parts["d"], parts["dmin"], parts["sub"])
     if fmt == FP8_E4M3_CH:
@@ -359,4 +450,6 @@ def dequant(fmt, parts, group=0):
         return dequant_rows(parts["codes"], parts["scales"], "int8")
     if fmt == F16:
         return np.asarray(parts["codes"], dtype=np.float16).astype(np.float64)
+    if fmt == BF16:
+        return codecs.bf16_decode(parts["codes"])
     raise ValueError("unknown format")

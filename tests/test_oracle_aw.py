@@ -17,7 +17,7 @@ import pytest
 from gemm_rwkv_amd import synth
 from oracle import aw, codecs, quant, ref
 
-SYM = [(8, 16), (8, 64), (4, 16), (4, 32), (4, 64)]
+SYM = [(8, 16), (8, 64), (4, 16), (4, 32), (4, 64), (6, 32), (5, 64)]
 
 
 def _weights(n, k, seed):
@@ -44,6 +44,8 @@ def test_zero_importance_is_rtn(bits, group):
     assert np.all(got["t"] == 0)
     assert np.array_equal(got["codes"], want["codes"])
     assert np.array_equal(got["scales"].view(np.uint16), want["scales"].view(np.uint16))
+    if bits in (5, 6):
+        assert np.array_equal(got["hi"], want["hi"])
 
 
 def test_zero_importance_is_rtn_sb256():
@@ -67,7 +69,7 @@ def test_weighted_error_not_above_rtn(bits, group):
     wd = w.astype(np.float64)
 
     def err(parts):
-        wh = quant.dequant_sym(parts["codes"], parts["scales"], bits, group)
+        wh = quant.dequant_sym(parts["codes"], parts["scales"], bits, group, parts.get("hi"))
         return np.sum((a * (wd - wh) ** 2).reshape(n, k // group, group), axis=2)
 
     e_aw, e_rtn = err(got), err(rtn)
@@ -83,7 +85,7 @@ def _nearest_code(v, lo, hi):
     return min(max(c, lo), hi)
 
 
-@pytest.mark.parametrize("bits,group", [(4, 16), (8, 16), (4, 32)])
+@pytest.mark.parametrize("bits,group", [(4, 16), (8, 16), (4, 32), (6, 32), (5, 32)])
 def test_sym_choice_matches_exact_bruteforce(bits, group):
     """Each candidate's error computed exactly in rationals (codes by exact
     nearest-integer rounding of w / s_t); the smallest t within the tie factor

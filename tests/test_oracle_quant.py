@@ -47,6 +47,19 @@ def _adversarial_weights(n, k, seed):
 # --------------------------------------------------------------------------
 
 
+def test_sym_hand_examples_5_6_bits():
+    ex_all = _golden("hand_examples.json")
+    for name, bits in (("sym_int6_g32", 6), ("sym_int5_g32", 5)):
+        ex = ex_all[name]
+        w = np.array([ex["w"]], dtype=np.float32)
+        r = quant.quantize_sym(w, bits, ex["group"])
+        assert int(codecs.f16_bits(r["scales"])[0, 0]) == int(ex["scale_f16_bits"], 16)
+        assert r["q"][0].tolist() == ex["codes"], name
+        assert r["codes"][0].tolist() == [int(b, 16) for b in ex["packed_bytes"]], name
+        hb = np.ascontiguousarray(r["hi"][0]).view(np.uint8).tolist()
+        assert hb == [int(b, 16) for b in ex["hi_bytes"]], name
+
+
 @pytest.mark.parametrize("name,bits", [("sym_int8_g16", 8), ("sym_int4_g16", 4),
                                        ("sym_int4_scale_one_seventh", 4)])
 def test_sym_hand_examples(name, bits):
@@ -111,7 +124,7 @@ def check_sym_brute(bits, group, seed, n=24):
     r = quant.quantize_sym(w, bits, group)
     Q = (1 << (bits - 1)) - 1
     s = r["scales"].astype(np.float64)
-    q = quant.unpack_sym(r["codes"], bits).astype(np.int64)
+    q = quant.unpack_sym(r["codes"], bits, r.get("hi")).astype(np.int64)
     assert np.array_equal(q, r["q"].astype(np.int64))
     # scale = nearest fp16 to the exact quotient absmax / Q
     wg = w.reshape(n, k // group, group)
@@ -133,8 +146,10 @@ def check_sym_brute(bits, group, seed, n=24):
     assert np.array_equal(q, want)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("group", [16, 32, 64])
+SYM_CASES = [(b, g) for b in (4, 8) for g in (16, 32, 64)] + [(b, g) for b in (5, 6) for g in (32, 64)]
+
+
+@pytest.mark.parametrize("bits,group", SYM_CASES)
 def test_sym_brute_force(bits, group):
     check_sym_brute(bits, group, seed=bits * 100 + group)
 
@@ -252,11 +267,10 @@ def check_sym_roundtrip(bits, group, seed, n=32):
     r = quant.quantize_sym(w, bits, group)
     assert np.array_equal(codecs.f16_bits(r["scales"]), codecs.f16_bits(s16))
     assert np.array_equal(r["q"].astype(np.int64), q)
-    assert np.array_equal(quant.dequant_sym(r["codes"], r["scales"], bits, group), w64)
+    assert np.array_equal(quant.dequant_sym(r["codes"], r["scales"], bits, group, r.get("hi")), w64)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("group", [16, 32, 64])
+@pytest.mark.parametrize("bits,group", SYM_CASES)
 def test_sym_roundtrip(bits, group):
     check_sym_roundtrip(bits, group, seed=bits + group)
 
@@ -499,6 +513,69 @@ def test_nibble_layout_bitwise():
                 word |= int(u[r, 8 * w + 2 * i + 1]) << (16 + 4 * i)
             assert packed[r, 4 * w:4 * w + 4].tolist() == [(word >> (8 * b)) & 0xFF for b in range(4)]
     assert np.array_equal(quant.unpack_nibbles(packed), u)
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_hi_plane_bitwise(bits):
+    # bit-by-bit construction of each high-plane word, independent of the
+    # packer: 6-bit: bits 4i..4i+1 = hi(8w + 2i), 4i+2..4i+3 = hi(8w + 2i + 1);
+    # 5-bit: bit i = hi(8w + 2i), bit 4 + i = hi(8w + 2i + 1)
+    g = np.random.default_rng(18 + bits)
+    u = g.integers(1, 1 << bits, (5, 64)).astype(np.uint8)
+    hi = quant.pack_hi(u, bits)
+    for r in range(5):
+        for w in range(8):
+            word = 0
+            for i in range(4):
+                he, ho = int(u[r, 8 * w + 2 * i]) >> 4, int(u[r, 8 * w + 2 * i + 1]) >> 4
+                if bits == 6:
+                    word |= (he << (4 * i)) | (ho << (4 * i + 2))
+                else:
+                    word |= (he << i) | (ho << (4 + i))
+            assert int(hi[r, w]) == word, (r, w)
+    assert np.array_equal(quant.unpack_hi(hi, bits, 64), u >> 4)
+    full = (quant.unpack_nibbles(quant.pack_nibbles(u & 0xF)) | (quant.unpack_hi(hi, bits, 64) << 4))
+    assert np.array_equal(full, u)
+
+
+def test_bf16_encoder_against_torch():
+    # a library's float32 -> bfloat16 conversion (round to nearest, ties to
+    # even, overflow to infinity) on random magnitudes, midpoints and edges
+    import torch
+    g = np.random.default_rng(5)
+    v = (g.standard_normal(100000) * 10.0 ** g.uniform(-44, 38, 100000)).astype(np.float32)
+    top = g.integers(0, 0x7F7F, 20000).astype(np.uint32) << 16
+    mids = (top | 0x8000).view(np.float32)                        # exact ties
+    near = ((top | 0x8000) + g.choice([-1, 1], 20000).astype(np.uint32)).view(np.float32)
+    edges = np.float32([0.0, -0.0, 3.4028235e38, -3.4028235e38, 1e-45, -1e-45, 3.3895314e38])
+    v = np.concatenate([v, mids, -mids, near, edges])
+    v = v[np.isfinite(v)]
+    mine = codecs.bf16_encode(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    assert np.array_equal(codecs.bf16_decode(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def test_bf16_quantize_overflow_and_nonfinite():
+    with pytest.raises(OverflowError):
+        quant.quantize_bf16(np.float32([[3.4e38]]))
+    with pytest.raises(ValueError):
+        quant.quantize_bf16(np.float32([[np.nan]]))
+    r = quant.quantize_bf16(np.float32([[1.0, -2.5, 3.3895314e38]]))
+    assert r["codes"].tolist() == [[0x3F80, 0xC020, 0x7F7F]]
+
+
+def test_mutation_hi_plane_parity(monkeypatch):
+    real = quant.pack_hi
+
+    def swapped(u, bits):
+        u = np.asarray(u, dtype=np.uint8)
+        v = u.copy()
+        v[:, 0::2], v[:, 1::2] = u[:, 1::2], u[:, 0::2]   # even / odd exchanged
+        return real(v, bits)
+    monkeypatch.setattr(quant, "pack_hi", swapped)
+    with pytest.raises(AssertionError):
+        test_sym_hand_examples_5_6_bits()
 
 
 def test_mutation_nibble_order(monkeypatch):
