@@ -19,6 +19,10 @@ inline hipStream_t S(void* s) { return (hipStream_t)s; }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? RQ_OK : RQ_ERR_HIP; }
 
+// launch_gemv: hipErrorInvalidConfiguration means no launch shape fits
+// (activation slice too large for the LDS with no split-K workspace)
+inline int gemv_status(hipError_t e) { return e == hipErrorInvalidConfiguration ? RQ_ERR_SHAPE : hip_status(e); }
+
 // y must not overlap x or any weight buffer
 int check_alias_out(const Span& y, const Span* ins, int nin) {
   for (int i = 0; i < nin; ++i)
@@ -32,6 +36,9 @@ int gemv_fmt(int format) {
     case RQ_W8_SYM: return rq::GF_W8;
     case RQ_W4_ASYM_SB256: return rq::GF_SB;
     case RQ_F16: return rq::GF_F16;
+    case RQ_W5_SYM: return rq::GF_W5;
+    case RQ_W6_SYM: return rq::GF_W6;
+    case RQ_BF16: return rq::GF_BF16;
   }
   return -1;
 }
@@ -104,7 +111,7 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
   gemv_workspace(S(stream), b);
-  return hip_status(rq::launch_gemv(b, gf, w->group, S(stream)));
+  return gemv_status(rq::launch_gemv(b, gf, w->group, S(stream)));
 }
 
 // rq_gemm_w4: int4 codes (symmetric groups or asymmetric superblocks), any m.
@@ -219,7 +226,15 @@ int quantize_impl(const float* w, const float* imp, const rq_qweight* out, void*
       case RQ_W8_SYM:
       case RQ_W4_SYM:
         e = rq::launch_quant_sym(w, n, k, out->format == RQ_W8_SYM ? 8 : 4, out->group, out->codes,
-                                 (uint16_t*)out->scales, flags, imp, s);
+                                 (uint16_t*)out->scales, nullptr, flags, imp, s);
+        break;
+      case RQ_W6_SYM:
+      case RQ_W5_SYM:
+        e = rq::launch_quant_sym(w, n, k, out->format == RQ_W6_SYM ? 6 : 5, out->group, out->codes,
+                                 (uint16_t*)out->scales, out->sub, flags, imp, s);
+        break;
+      case RQ_BF16:
+        e = rq::launch_to_bf16(w, n * k, (uint16_t*)out->codes, flags, s);
         break;
       case RQ_W4_ASYM_SB256:
         e = rq::launch_quant_sb256(w, n, k, out->codes, out->scales, out->mins, out->sub, flags, imp, s);
@@ -252,7 +267,8 @@ int rq_quantize_rtn(const float* w, const rq_qweight* out, void* stream) {
 
 int rq_quantize_aw(const float* w, const float* act_sq, const rq_qweight* out, void* stream) {
   if (!act_sq || !out) return RQ_ERR_NULL;
-  if (out->format != RQ_W8_SYM && out->format != RQ_W4_SYM && out->format != RQ_W4_ASYM_SB256)
+  if (out->format != RQ_W8_SYM && out->format != RQ_W4_SYM && out->format != RQ_W4_ASYM_SB256 &&
+      out->format != RQ_W6_SYM && out->format != RQ_W5_SYM)
     return RQ_ERR_FORMAT;
   return quantize_impl(w, act_sq, out, stream);
 }
@@ -319,7 +335,7 @@ int rq_fused_rkv(const uint16_t* xr, const uint16_t* xk, const uint16_t* xv, int
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
   gemv_workspace(S(stream), b);
-  return hip_status(rq::launch_gemv(b, gf, wr->group, S(stream)));
+  return gemv_status(rq::launch_gemv(b, gf, wr->group, S(stream)));
 }
 
 int rq_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int format, void* xq,

@@ -350,8 +350,15 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(const GemvBatch p) {
 // scalar offset, so the loop body has no branches).
 template <int FMT, int G>
 struct F2 {
-  static constexpr int CK = (FMT == GF_W4 || FMT == GF_SB) ? 128 : (FMT == GF_W8 ? 64 : 32);
-  static constexpr int GK = (FMT == GF_SB || FMT == GF_F16) ? 32 : G;
+  // NIB: symmetric codes whose low (or only) plane is int4 code words;
+  // SYMS: one fp16 scale per (row, group); PLAIN: unscaled 16-bit weights;
+  // HW: 32-bit words of the high plane per lane and chunk (6-bit 2, 5-bit 1)
+  static constexpr bool NIB = FMT == GF_W4 || FMT == GF_W5 || FMT == GF_W6;
+  static constexpr bool SYMS = NIB || FMT == GF_W8;
+  static constexpr bool PLAIN = FMT == GF_F16 || FMT == GF_BF16;
+  static constexpr int HW = FMT == GF_W6 ? 2 : (FMT == GF_W5 ? 1 : 0);
+  static constexpr int CK = (NIB || FMT == GF_SB) ? 128 : (FMT == GF_W8 ? 64 : 32);
+  static constexpr int GK = (FMT == GF_SB || PLAIN) ? 32 : G;
   static constexpr int GPC = CK / GK;
   static constexpr int KPM = (FMT == GF_W8 && G == 16) ? 16 : 32;  // k per MFMA
   static constexpr int MPG = GK / KPM;                             // MFMAs per group
@@ -383,10 +390,10 @@ template <int FMT, int G>
 __device__ __forceinline__ int x_base(int kq) {
   typedef F2<FMT, G> F;
   if constexpr (F::GPC == 1) {
-    if constexpr (FMT == GF_F16) return 8 * kq;
+    if constexpr (F::PLAIN) return 8 * kq;
     return 16 * kq;  // int8 g64
   } else if constexpr (F::GPC == 2) {
-    if constexpr (FMT == GF_W4) return (kq & 1) * 32 + (kq >> 1) * 16;
+    if constexpr (F::NIB) return (kq & 1) * 32 + (kq >> 1) * 16;
     return (kq & 1) * 16 + (kq >> 1) * 8;  // int8 g32
   } else {
     return kq * F::XH;  // int4 g32 / SB (8 k), int8 g16 (4 k)
@@ -395,8 +402,8 @@ __device__ __forceinline__ int x_base(int kq) {
 template <int FMT, int G>
 constexpr int x_const(int g, int p) {
   typedef F2<FMT, G> F;
-  if constexpr (F::GPC == 1) return FMT == GF_F16 ? 0 : 8 * p;
-  else if constexpr (F::GPC == 2) return FMT == GF_W4 ? 64 * g + 8 * p : 32 * g;
+  if constexpr (F::GPC == 1) return F::PLAIN ? 0 : 8 * p;
+  else if constexpr (F::GPC == 2) return F::NIB ? 64 * g + 8 * p : 32 * g;
   else return g * F::GK;
 }
 
@@ -434,10 +441,61 @@ struct Split5 {
 
 template <int FMT, int G>
 struct CodeSlot {
-  uint4 c;                              // codes
+  uint4 c;                              // codes (the low plane for W6 / W5)
   uint32_t s;                           // SB: d | dmin << 16
   uint32_t sub[FMT == GF_SB ? 3 : 1];   // SB: packed 6-bit sub-scale codes
+  uint32_t hi[FMT == GF_W6 ? 2 : 1];    // W6 / W5: the high plane of the lane's four words
 };
+
+// High plane of one code word -> a word shaped like it: the high bits of the
+// code in nibble i of each half sit in bits 0..1 of that nibble.  6-bit: hc
+// is the word's uint16 (nibble i = hi(even) | hi(odd) << 2); 5-bit: its byte
+// (bit i = hi(even), bit 4 + i = hi(odd)).
+template <int FMT>
+__device__ __forceinline__ uint32_t hi_spread(uint32_t hc) {
+  if constexpr (FMT == GF_W6) {
+    return (hc & 0x3333u) | ((hc & 0xccccu) << 14);
+  } else {
+    uint32_t x = (hc & 0x0fu) | ((hc & 0xf0u) << 12);  // bits 0-3 and 16-19
+    x = (x | (x << 6)) & 0x03030303u;                  // -> bits 0,1,8,9 of each half
+    return (x | (x << 3)) & 0x11111111u;               // -> bit 0 of each nibble
+  }
+}
+
+// One int4 code word v plus its spread high bits h -> fp16 (u - 2^(b-1)) for
+// k = 0..7 in natural order, u = nibble | hi << 4 (b = 6 or 5).  As in dec4n,
+// nibbles 0 and 2 land in the mantissa of 1024 (ulp 1) and nibbles 1 and 3 in
+// that of 64 (ulp 1/16); the high bits join them at bits 4..5 or 8..9, one
+// AND-OR each, and one packed subtract removes 1024 + 2^(b-1) or 64 + 2^(b-1).
+template <int BITS>
+__device__ __forceinline__ half8 dec56(uint32_t v, uint32_t h) {
+  constexpr uint32_t blo = BITS == 6 ? 0x64206420u : 0x64106410u;  // 1056 : 1040
+  constexpr uint32_t bhi = BITS == 6 ? 0x56005600u : 0x55005500u;  // 96 : 80
+  const uint32_t hl = h << 4, hr = h >> 4, v8 = v >> 8;
+  const uint32_t o0 = and_or(hl, 0x00300030u, 0x64006400u);
+  const uint32_t o1 = and_or(hl, 0x03000300u, 0x54005400u);
+  const uint32_t o2 = and_or(hr, 0x00300030u, 0x64006400u);
+  const uint32_t o3 = and_or(hr, 0x03000300u, 0x54005400u);
+  const uint32_t h0 = hsub2(and_or(v, 0x000f000fu, o0), blo);
+  const uint32_t h1 = hsub2(and_or(v, 0x00f000f0u, o1), bhi);
+  const uint32_t h2 = hsub2(and_or(v8, 0x000f000fu, o2), blo);
+  const uint32_t h3 = hsub2(and_or(v8, 0x00f000f0u, o3), bhi);
+  return __builtin_bit_cast(half8, make_uint4(h0, h1, h2, h3));
+}
+
+// fp16 activations -> bf16 hi + lo with hi + lo exact: hi keeps the top 8
+// significant bits (truncation of the fp32 value), lo = x - hi has at most 3
+// and is exact in bf16.  Both products with bf16 weights are exact in fp32.
+__device__ __forceinline__ void split_bf16(const half8& a, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float f = (float)a[i];
+    const uint32_t fb = __float_as_uint(f) & 0xffff0000u;
+    const float r = f - __uint_as_float(fb);
+    hi[i] = __builtin_bit_cast(__bf16, (uint16_t)(fb >> 16));
+    lo[i] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(r) >> 16));
+  }
+}
 
 // MR: activation rows that can be non-zero among a lane's four outputs
 // (m <= MR), so scale multiplications skip rows that are known to be zero.
@@ -493,7 +551,12 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   const uint32_t coff = (nvalid ? (uint32_t)n * rowbytes : 0u) + (uint32_t)kq * 16u;
   __amdgpu_buffer_rsrc_t rs = rc, rm = rc, rb = rc;
   uint32_t soff = 0, sboff = 0, subb = 0;
-  if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+  if constexpr (F::HW > 0) {
+    const uint32_t hrow = (uint32_t)(k / 8) * (FMT == GF_W6 ? 2u : 1u);
+    rb = __builtin_amdgcn_make_buffer_rsrc((void*)A.sub, (short)0, (int)((uint32_t)A.n * hrow), 0x00020000);
+    subb = (nvalid ? (uint32_t)n * hrow : 0u) + (uint32_t)kq * (4u * F::HW);
+  }
+  if constexpr (F::SYMS) {
     const uint32_t srow = (uint32_t)(k / F::GK) * 2u;
     rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * srow), 0x00020000);
     soff = nvalid ? (uint32_t)n * srow : 0u;
@@ -589,9 +652,9 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   //    the next slice or row)
   const int c0 = cbeg + wv * CPW;
   S sl[CPW];
-  constexpr int SW = (FMT == GF_W4 || FMT == GF_W8) ? (CPW * F::GPC * 2 + 3) / 4 : 1;  // scale words
+  constexpr int SW = F::SYMS ? (CPW * F::GPC * 2 + 3) / 4 : 1;  // scale words
   uint32_t sw[SW];
-  if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+  if constexpr (F::SYMS) {
     const uint32_t ss = tvalid ? (uint32_t)c0 * (F::GPC * 2) : kOOB;
     if constexpr (SW >= 4) {
 #pragma unroll
@@ -612,6 +675,13 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     const bool valid = tvalid && c < cend;
     auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, valid ? (uint32_t)c * 64u : kOOB, 0);
     sl[i].c = make_uint4(v[0], v[1], v[2], v[3]);
+    if constexpr (F::HW == 2) {
+      auto h = __builtin_amdgcn_raw_buffer_load_b64(rb, subb, valid ? (uint32_t)c * 32u : kOOB, 0);
+      sl[i].hi[0] = h[0];
+      sl[i].hi[1] = h[1];
+    } else if constexpr (F::HW == 1) {
+      sl[i].hi[0] = __builtin_amdgcn_raw_buffer_load_b32(rb, subb, valid ? (uint32_t)c * 16u : kOOB, 0);
+    }
     if constexpr (FMT == GF_SB) {
       const uint32_t sb = (uint32_t)c >> 1;
       const uint32_t s2 = valid ? sb * 2u : kOOB;
@@ -640,7 +710,9 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     copy_x();
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(CPW) : "memory");
+    // with a high plane two loads follow per chunk: every copy has landed
+    // once no more than 2 * CPW are in flight
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(F::HW > 0 ? 2 * CPW : CPW) : "memory");
   }
 
   int xrow[MT];
@@ -661,21 +733,43 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     const int c = c0 + i < cend ? c0 + i : cend - 1;  // activation offset inside the slice
     const int kk = (c - cbeg) * F::CK;
     uint32_t w[4] = {sl[i].c.x, sl[i].c.y, sl[i].c.z, sl[i].c.w};
-    uint32_t gw[4][2];
+    uint32_t gw[4][2], gh[4][2];
+    // the high plane's words go through the same exchange as the code words
+    uint32_t hw[4] = {0u, 0u, 0u, 0u};
+    if constexpr (F::HW == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hw[j] = hi_spread<FMT>((sl[i].hi[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+    } else if constexpr (F::HW == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hw[j] = hi_spread<FMT>((sl[i].hi[0] >> (8 * j)) & 0xffu);
+    }
     if constexpr (F::GPC == 2) {
       swap32(w[0], w[2]);
       swap32(w[1], w[3]);
       gw[0][0] = w[0]; gw[0][1] = w[1];
       gw[1][0] = w[2]; gw[1][1] = w[3];
+      if constexpr (F::HW > 0) {
+        swap32(hw[0], hw[2]);
+        swap32(hw[1], hw[3]);
+        gh[0][0] = hw[0]; gh[0][1] = hw[1];
+        gh[1][0] = hw[2]; gh[1][1] = hw[3];
+      }
     } else if constexpr (F::GPC == 4) {
       swap32(w[0], w[2]);
       swap32(w[1], w[3]);
       swap16(w[0], w[1]);
       swap16(w[2], w[3]);
       gw[0][0] = w[0]; gw[1][0] = w[1]; gw[2][0] = w[2]; gw[3][0] = w[3];
+      if constexpr (F::HW > 0) {
+        swap32(hw[0], hw[2]);
+        swap32(hw[1], hw[3]);
+        swap16(hw[0], hw[1]);
+        swap16(hw[2], hw[3]);
+        gh[0][0] = hw[0]; gh[1][0] = hw[1]; gh[2][0] = hw[2]; gh[3][0] = hw[3];
+      }
     }
     float scl[4], mnv[4];
-    if constexpr (FMT == GF_W4 || FMT == GF_W8) {
+    if constexpr (F::SYMS) {
 #pragma unroll
       for (int g = 0; g < F::GPC; ++g) {
         const int h = i * F::GPC + g;  // half-word index in the wave's scale span
@@ -703,10 +797,12 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
         const int xo = kk + x_const<FMT, G>(g, pp);
         if constexpr (F::KPM == 32) {
           half8 b;
-          if constexpr (FMT == GF_F16) {
-            b = __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));
+          if constexpr (F::PLAIN) {
+            b = __builtin_bit_cast(half8, make_uint4(w[0], w[1], w[2], w[3]));  // bf16 bits for GF_BF16
           } else if constexpr (FMT == GF_W4 || FMT == GF_SB) {
             b = dec4n<FMT == GF_W4>(F::GPC == 2 ? gw[g][pp] : gw[g][0]);
+          } else if constexpr (F::HW > 0) {
+            b = dec56<FMT == GF_W6 ? 6 : 5>(F::GPC == 2 ? gw[g][pp] : gw[g][0], F::GPC == 2 ? gh[g][pp] : gh[g][0]);
           } else {
             uint32_t wa, wb;
             if constexpr (F::GPC == 1) {
@@ -724,6 +820,12 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
             const half8 a = *(const half8*)(xl + xrow[t] + xo);
             if constexpr (FMT == GF_F16) {
               acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+            } else if constexpr (FMT == GF_BF16) {
+              bf16x8 ahi, alo;
+              split_bf16(a, ahi, alo);
+              const bf16x8 wb = __builtin_bit_cast(bf16x8, b);
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, wb, acc[t], 0, 0, 0);
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, wb, acc[t], 0, 0, 0);
             } else {
               grp[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, pp == 0 ? zero4 : grp[t], 0, 0, 0);
               if constexpr (FMT == GF_SB) {
@@ -742,7 +844,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
           }
         }
       }
-      if constexpr (FMT != GF_F16) {
+      if constexpr (!F::PLAIN) {
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -850,7 +952,7 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
     const size_t xb = (size_t)(b.m + 1) * (nchunks * F::CK + 8) * 2;
     // two activation tiles over a short K: eight waves of two chunks issue
     // the activation copies twice as fast as four of four
-    const int cpw = (mt == 2 && nchunks <= 16) ? 2 : pick_cpw(nchunks, mt == 1 && FMT != GF_SB);
+    const int cpw = (mt == 2 && nchunks <= 16) ? 2 : pick_cpw(nchunks, mt == 1 && FMT != GF_SB && F::HW == 0);
     const int wpt = (nchunks + cpw - 1) / cpw;
     int tiles = 0;
     for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
@@ -882,13 +984,13 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
     // a wave's scale span is loaded from byte c0 * 2 * GPC and must start on a
     // 4-byte boundary: with one scale per chunk (int8 group 64) slices hold an
     // even number of chunks (CPW is even)
-    constexpr int cmult = (F::GPC == 1 && (FMT == GF_W4 || FMT == GF_W8)) ? 2 : 1;
+    constexpr int cmult = (F::GPC == 1 && F::SYMS) ? 2 : 1;
     const int cps = ((nchunks + split - 1) / split + cmult - 1) / cmult * cmult;
     if ((split - 1) * cps >= nchunks) continue;  // an empty slice
     const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
     if (xb > (size_t)kXBudget) continue;
     // from M = 3 on, a split slice does better with more waves of fewer chunks
-    const int cpw = b.m <= 2 ? pick_cpw(cps, FMT != GF_SB) : (cps <= 64 ? 4 : 8);
+    const int cpw = b.m <= 2 ? pick_cpw(cps, FMT != GF_SB && F::HW == 0) : (cps <= 64 ? 4 : 8);
     const int wpt = (cps + cpw - 1) / cpw;
     if (wpt > 16) continue;
     int rt = 1;
@@ -939,7 +1041,7 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   } while (0)
   if (mt == 2) {
     if (cpw == 2) RQ_L5(2, 2, 4); else if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
-  } else if constexpr (FMT == GF_SB) {
+  } else if constexpr (FMT == GF_SB || F::HW > 0) {
     if (b.m == 1) {
       if (cpw == 4) RQ_L5(1, 4, 1); else RQ_L5(1, 8, 1);
     } else if (b.m == 2) {
@@ -1002,8 +1104,12 @@ static hipError_t launch_mt(const GemvBatch& b, hipStream_t st) {
       if (launch5<FMT, G>(b, st, err)) return err;
     }
   }
-  if (b.m <= 16) return launch_nw<FMT, G, 1>(b, st);
-  return launch_nw<FMT, G, 2>(b, st);
+  if constexpr (FMT == GF_W5 || FMT == GF_W6 || FMT == GF_BF16) {
+    return hipErrorInvalidConfiguration;  // no launch shape (the formats have no other path)
+  } else {
+    if (b.m <= 16) return launch_nw<FMT, G, 1>(b, st);
+    return launch_nw<FMT, G, 2>(b, st);
+  }
 }
 
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st) {
@@ -1023,6 +1129,16 @@ hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st) {
       return launch_mt<GF_SB, 32>(b, st);
     case GF_F16:
       return launch_mt<GF_F16, 32>(b, st);
+    case GF_W6:
+      if (group == 64) return launch_mt<GF_W6, 64>(b, st);
+      if (group == 32) return launch_mt<GF_W6, 32>(b, st);
+      break;
+    case GF_W5:
+      if (group == 64) return launch_mt<GF_W5, 64>(b, st);
+      if (group == 32) return launch_mt<GF_W5, 32>(b, st);
+      break;
+    case GF_BF16:
+      return launch_mt<GF_BF16, 32>(b, st);
   }
   return hipErrorInvalidValue;
 }

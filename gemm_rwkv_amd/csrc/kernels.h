@@ -9,8 +9,9 @@ namespace rq {
 // ---- quantizers (quant.hip) ------------------------------------------------
 // imp (may be null): fp32 [k] E[x^2] importances; non-null selects the
 // activation-weighted scale search instead of RTN
+// bits 5 / 6 also write the high plane `hi` (uint16 or uint8 per 8-k word)
 hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int group, void* codes,
-                            uint16_t* scales, int* flags, const float* imp, hipStream_t st);
+                            uint16_t* scales, void* hi, int* flags, const float* imp, hipStream_t st);
 hipError_t launch_quant_sb256(const float* w, int64_t n, int64_t k, void* qs, void* d, void* dmin,
                               void* sub, int* flags, const float* imp, hipStream_t st);
 hipError_t launch_quant_rows_f32(const float* w, int64_t n, int64_t k, bool fp8, void* codes,
@@ -18,15 +19,16 @@ hipError_t launch_quant_rows_f32(const float* w, int64_t n, int64_t k, bool fp8,
 hipError_t launch_quant_rows_f16(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, bool fp8,
                                  void* codes, float* scales, int* flags, hipStream_t st);
 hipError_t launch_to_f16(const float* w, int64_t count, uint16_t* out, int* flags, hipStream_t st);
+hipError_t launch_to_bf16(const float* w, int64_t count, uint16_t* out, int* flags, hipStream_t st);
 
 // ---- weight-streaming products, 1 <= m <= 32 (gemv.hip) ----------------------
-enum GemvFormat { GF_W4 = 0, GF_W8 = 1, GF_SB = 2, GF_F16 = 3 };
+enum GemvFormat { GF_W4 = 0, GF_W8 = 1, GF_SB = 2, GF_F16 = 3, GF_W5 = 4, GF_W6 = 5, GF_BF16 = 6 };
 
 struct GemvMatrix {
   const void* codes;
   const uint16_t* scales;  // W4/W8: fp16 [n][k/g]; SB: d [n][k/256]
   const uint16_t* mins;    // SB: dmin [n][k/256]
-  const uint32_t* sub;     // SB: [n][k/256][3] words
+  const uint32_t* sub;     // SB: [n][k/256][3] words; W6 / W5: high plane [n][k/8] (uint16 / uint8)
   const uint16_t* x;       // fp16 [m][ldx]
   uint16_t* y;             // fp16 [m][ldy]
   int n;

@@ -74,10 +74,28 @@ __device__ __forceinline__ float4 aw_importance(const float* imp, int64_t k, boo
 // symmetric group RTN: one lane per 4 consecutive weights, G/4 lanes a group
 // (AW: the scale comes from the search above; imp is fp32 [K])
 // ---------------------------------------------------------------------------
+// 5 and 6 bits: the low nibble of u = q + 2^(BITS-1) goes to the int4 layout
+// and u >> 4 to the high plane.  A lane holds k = 4t .. 4t+3, half of an 8-k
+// word: the even lane of a pair k = 8w + 0..3 (pairs i = 0, 1), the odd lane
+// 8w + 4..7 (i = 2, 3).  6-bit: nibble i = hi(8w+2i) | hi(8w+2i+1) << 2 of a
+// uint16; 5-bit: bit i = hi(8w+2i), bit 4+i = hi(8w+2i+1) of a byte.
+template <int BITS>
+__device__ __forceinline__ uint32_t hi_word_part(uint32_t h0, uint32_t h1, uint32_t h2, uint32_t h3, int odd) {
+  uint32_t mine;
+  if (BITS == 6) {
+    const uint32_t lo8 = (h0 | (h1 << 2)) | ((h2 | (h3 << 2)) << 4);  // pairs 0,1 (or 2,3)
+    mine = odd ? (lo8 << 8) : lo8;
+  } else {
+    const uint32_t sh = odd ? 2u : 0u;
+    mine = ((h0 | (h2 << 1)) << sh) | ((h1 | (h3 << 1)) << (4 + sh));
+  }
+  return mine | (uint32_t)__shfl_xor((int)mine, 1);
+}
+
 template <int BITS, int G, bool AW>
 __global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict__ w, int64_t total4,
                                                         void* __restrict__ codes,
-                                                        uint16_t* __restrict__ scales,
+                                                        uint16_t* __restrict__ scales, void* __restrict__ hi,
                                                         int* __restrict__ flags, const float* __restrict__ imp,
                                                         int64_t K) {
   constexpr int LPG = G / 4;
@@ -128,8 +146,19 @@ __global__ void __launch_bounds__(256) quant_sym_kernel(const float4* __restrict
                       ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
     if (active) ((uint32_t*)codes)[t] = packed;
   } else {
-    const uint32_t w = nibble_word_part(q[0] + 8, q[1] + 8, q[2] + 8, q[3] + 8, t & 1);
+    constexpr int OFF = 1 << (BITS - 1);
+    const uint32_t u0 = (uint32_t)(q[0] + OFF), u1 = (uint32_t)(q[1] + OFF), u2 = (uint32_t)(q[2] + OFF),
+                   u3 = (uint32_t)(q[3] + OFF);
+    const uint32_t w = nibble_word_part(u0 & 15u, u1 & 15u, u2 & 15u, u3 & 15u, t & 1);
     if (active && (t & 1) == 0) ((uint32_t*)codes)[t >> 1] = w;
+    if constexpr (BITS == 5 || BITS == 6) {
+      // lane t holds k = 4t .. 4t+3: pairs (k, k+1) = (u0, u1) and (u2, u3)
+      const uint32_t h = hi_word_part<BITS>(u0 >> 4, u1 >> 4, u2 >> 4, u3 >> 4, t & 1);
+      if (active && (t & 1) == 0) {
+        if (BITS == 6) ((uint16_t*)hi)[t >> 1] = (uint16_t)h;
+        else ((uint8_t*)hi)[t >> 1] = (uint8_t)h;
+      }
+    }
   }
   if (active && (t % LPG) == 0) scales[t / LPG] = sbits;
 }
@@ -372,13 +401,29 @@ __global__ void __launch_bounds__(256) to_f16_kernel(const float* __restrict__ w
   out[i] = h;
 }
 
+// fp32 -> bfloat16, round to nearest with ties to even: add 0x7fff plus the
+// lowest kept bit to the fp32 pattern and keep the top half (a carry out of
+// the mantissa moves the exponent up, which is the correct rounding; past
+// the largest finite value it gives infinity, reported as a range error)
+__global__ void __launch_bounds__(256) to_bf16_kernel(const float* __restrict__ w, int64_t count,
+                                                      uint16_t* __restrict__ out, int* __restrict__ flags) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const float v = w[i];
+  if (!finite_f32(v)) raise_flag(flags, 0);
+  const uint32_t b = __float_as_uint(v);
+  const uint16_t h = (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+  if ((h & 0x7fffu) == 0x7f80u) raise_flag(flags, 1);
+  out[i] = h;
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int group, void* codes,
-                            uint16_t* scales, int* flags, const float* imp, hipStream_t st) {
+                            uint16_t* scales, void* hi, int* flags, const float* imp, hipStream_t st) {
   const int64_t total4 = n * k / 4;
   if (total4 == 0) return hipSuccess;
   const dim3 grid(grid_for(total4)), block(256);
@@ -387,10 +432,10 @@ hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int 
   if (bits == B && group == G) {                                                                   \
     if (imp)                                                                                       \
       hipLaunchKernelGGL((quant_sym_kernel<B, G, true>), grid, block, 0, st, w4, total4, codes,    \
-                         scales, flags, imp, k);                                                   \
+                         scales, hi, flags, imp, k);                                               \
     else                                                                                           \
       hipLaunchKernelGGL((quant_sym_kernel<B, G, false>), grid, block, 0, st, w4, total4, codes,   \
-                         scales, flags, imp, k);                                                   \
+                         scales, hi, flags, imp, k);                                               \
     return hipGetLastError();                                                                      \
   }
   RQ_SYM_CASE(8, 16)
@@ -399,6 +444,10 @@ hipError_t launch_quant_sym(const float* w, int64_t n, int64_t k, int bits, int 
   RQ_SYM_CASE(4, 16)
   RQ_SYM_CASE(4, 32)
   RQ_SYM_CASE(4, 64)
+  RQ_SYM_CASE(6, 32)
+  RQ_SYM_CASE(6, 64)
+  RQ_SYM_CASE(5, 32)
+  RQ_SYM_CASE(5, 64)
 #undef RQ_SYM_CASE
   return hipErrorInvalidValue;
 }
@@ -455,6 +504,12 @@ hipError_t launch_quant_rows_f16(const uint16_t* x, int64_t m, int64_t k, int64_
   else
     hipLaunchKernelGGL((quant_rows_kernel<uint16_t, false>), dim3((unsigned)m), dim3(256), 0, st, x, k,
                        ldx, (uint32_t*)codes, scales, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* w, int64_t count, uint16_t* out, int* flags, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for(count)), dim3(256), 0, st, w, count, out, flags);
   return hipGetLastError();
 }
 

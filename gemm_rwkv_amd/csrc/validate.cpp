@@ -15,11 +15,15 @@ int check_format(int format, int group) {
     case RQ_W8_SYM:
     case RQ_W4_SYM:
       return (group == 16 || group == 32 || group == 64) ? RQ_OK : RQ_ERR_FORMAT;
+    case RQ_W6_SYM:
+    case RQ_W5_SYM:
+      return (group == 32 || group == 64) ? RQ_OK : RQ_ERR_FORMAT;
     case RQ_W4_ASYM_SB256:
       return group == 32 ? RQ_OK : RQ_ERR_FORMAT;
     case RQ_FP8_E4M3_CH:
     case RQ_I8_CH:
     case RQ_F16:
+    case RQ_BF16:
       return RQ_OK;
     default:
       return RQ_ERR_FORMAT;
@@ -34,6 +38,9 @@ int check_shape(int format, int group, int64_t n, int64_t k) {
     case RQ_W8_SYM:
     case RQ_W4_SYM:
       return (k % group == 0) ? RQ_OK : RQ_ERR_SHAPE;
+    case RQ_W6_SYM:
+    case RQ_W5_SYM:
+      return (k % 128 == 0) ? RQ_OK : RQ_ERR_SHAPE;
     case RQ_W4_ASYM_SB256:
       return (k % 256 == 0) ? RQ_OK : RQ_ERR_SHAPE;
     case RQ_FP8_E4M3_CH:
@@ -41,6 +48,8 @@ int check_shape(int format, int group, int64_t n, int64_t k) {
       return (k % 16 == 0) ? RQ_OK : RQ_ERR_SHAPE;
     case RQ_F16:
       return (k % 8 == 0) ? RQ_OK : RQ_ERR_SHAPE;
+    case RQ_BF16:
+      return (k % 32 == 0) ? RQ_OK : RQ_ERR_SHAPE;
   }
   return RQ_ERR_FORMAT;
 }
@@ -71,7 +80,14 @@ int weight_bytes(int format, int group, int64_t n, int64_t k, size_t* codes, siz
       c = N * K;
       s = N * 4;
       break;
+    case RQ_W6_SYM:
+    case RQ_W5_SYM:
+      c = N * K / 2;
+      s = N * (K / (size_t)group) * 2;
+      b = N * (K / 8) * (format == RQ_W6_SYM ? 2 : 1);
+      break;
     case RQ_F16:
+    case RQ_BF16:
       c = N * K * 2;
       break;
   }
@@ -87,14 +103,18 @@ int check_weight(const rq_qweight* w) {
   int st = check_format(w->format, w->group);
   if (st != RQ_OK) return st;
   if (!w->codes) return RQ_ERR_NULL;
-  if (w->format != RQ_F16 && !w->scales) return RQ_ERR_NULL;
+  const bool plain = w->format == RQ_F16 || w->format == RQ_BF16;
+  const bool two_plane = w->format == RQ_W6_SYM || w->format == RQ_W5_SYM;
+  if (!plain && !w->scales) return RQ_ERR_NULL;
   if (w->format == RQ_W4_ASYM_SB256 && (!w->mins || !w->sub)) return RQ_ERR_NULL;
+  if (two_plane && !w->sub) return RQ_ERR_NULL;
   st = check_shape(w->format, w->group, w->n, w->k);
   if (st != RQ_OK) return st;
   if (!aligned16(w->codes)) return RQ_ERR_ALIGN;
-  if (w->format != RQ_F16 && !aligned16(w->scales)) return RQ_ERR_ALIGN;
+  if (!plain && !aligned16(w->scales)) return RQ_ERR_ALIGN;
   if (w->format == RQ_W4_ASYM_SB256 && (!aligned16(w->mins) || !aligned16(w->sub)))
     return RQ_ERR_ALIGN;
+  if (two_plane && !aligned16(w->sub)) return RQ_ERR_ALIGN;
   return RQ_OK;
 }
 

@@ -29,6 +29,9 @@ RQ_W4_ASYM_SB256 = 3
 RQ_FP8_E4M3_CH = 4
 RQ_I8_CH = 5
 RQ_F16 = 6
+RQ_W5_SYM = 7
+RQ_W6_SYM = 8
+RQ_BF16 = 9
 
 # every symbol include/rq.h declares
 EXPORTS = (

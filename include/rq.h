@@ -110,6 +110,23 @@ enum rq_status {
  *   Unquantized fp16 weights, used for the output head, which the toolkit
  *   keeps in FP16 (Key Design) and the model card keeps full precision.
  *     codes : fp16 [n][k];  scales, mins, sub: unused
+ * RQ_W6_SYM, RQ_W5_SYM (group 32 or 64; k % 128 == 0)
+ *   The 6- and 5-bit widths of the news article's presets ("Dois presets e
+ *   seis tamanhos": channel-mix weights at 6 bits; channel-mix key and head at
+ *   5 bits).  The article gives the widths only; these are the symmetric rule
+ *   above with Q = 31 / 15.  Codes are offset binary u = q + 32 / q + 16 in two
+ *   planes:
+ *     codes : uint8 [n][k/2], the low nibbles u & 15 as int4 code words
+ *     sub   : the high bits u >> 4 per 8-k word w, with e = hi(8w + 2i) and
+ *             o = hi(8w + 2i + 1), i = 0..3:
+ *             W6: uint16 [n][k/8], bits 4i..4i+1 = e, 4i+2..4i+3 = o;
+ *             W5: uint8  [n][k/8], bit i = e, bit 4 + i = o
+ *     scales: fp16 [n][k/group];  mins: unused
+ * RQ_BF16 (group ignored; k % 32 == 0)
+ *   bfloat16 weights (news article, "Onde o 2.9B quebra": the first block's
+ *   output projection kept in bf16).  The quantizer rounds fp32 to nearest,
+ *   ties to even; a weight past the largest finite bf16 is RQ_ERR_RANGE.
+ *     codes : bf16 [n][k];  scales, mins, sub: unused
  *
  * int4 code words (RQ_W4_SYM, RQ_W4_ASYM_SB256).  The pages fix no nibble
  * order; each run of 8 consecutive k of a row is one little-endian 32-bit
@@ -127,7 +144,10 @@ enum rq_format {
   RQ_W4_ASYM_SB256 = 3,
   RQ_FP8_E4M3_CH = 4,
   RQ_I8_CH = 5,
-  RQ_F16 = 6
+  RQ_F16 = 6,
+  RQ_W5_SYM = 7,
+  RQ_W6_SYM = 8,
+  RQ_BF16 = 9
 };
 
 /* Host-side descriptor of one quantized weight; the four buffers are device

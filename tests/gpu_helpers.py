@@ -37,12 +37,15 @@ def qweight_from_oracle(fmt, group, parts, n, k):
     """QWeight whose device buffers hold the oracle's packed layout."""
     if fmt in (quant.W4_SYM, quant.W8_SYM):
         return rq.QWeight(fmt, group, n, k, dev_bytes(parts["codes"]), dev_bytes(parts["scales"]))
+    if fmt in (quant.W6_SYM, quant.W5_SYM):
+        return rq.QWeight(fmt, group, n, k, dev_bytes(parts["codes"]), dev_bytes(parts["scales"]),
+                          None, dev_bytes(parts["hi"]))
     if fmt == quant.W4_ASYM_SB256:
         return rq.QWeight(fmt, 32, n, k, dev_bytes(parts["qs"]), dev_bytes(parts["d"]),
                           dev_bytes(parts["dmin"]), dev_bytes(parts["sub"]))
     if fmt in (quant.FP8_E4M3_CH, quant.I8_CH):
         return rq.QWeight(fmt, 0, n, k, dev_bytes(parts["codes"]), dev_bytes(parts["scales"]))
-    if fmt == quant.F16:
+    if fmt in (quant.F16, quant.BF16):
         return rq.QWeight(fmt, 0, n, k, dev_bytes(parts["codes"]))
     raise ValueError(fmt)
 
@@ -51,6 +54,8 @@ def oracle_buffers(fmt, parts):
     """The oracle's packed buffers in the library's order (codes, scales, mins, sub)."""
     if fmt in (quant.W4_SYM, quant.W8_SYM):
         return {"codes": parts["codes"], "scales": parts["scales"]}
+    if fmt in (quant.W6_SYM, quant.W5_SYM):
+        return {"codes": parts["codes"], "scales": parts["scales"], "sub": parts["hi"]}
     if fmt == quant.W4_ASYM_SB256:
         return {"codes": parts["qs"], "scales": parts["d"], "mins": parts["dmin"], "sub": parts["sub"]}
     if fmt in (quant.FP8_E4M3_CH, quant.I8_CH):

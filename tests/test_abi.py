@@ -56,12 +56,22 @@ def test_qweight_bytes():
     # SB256 is 4.5 bits per weight, w4g64 4.25
     c, s, m, sub = rq.rq_qweight_bytes(rq.RQ_W4_ASYM_SB256, 32, 1, 256)
     assert (c + s + m + sub) * 8 / 256 == 4.5
-    for bad in [(rq.RQ_W4_SYM, 48, 4, 96), (9, 0, 4, 64), (rq.RQ_W4_ASYM_SB256, 64, 4, 256)]:
+    # 6 and 5 bits: low plane k/2, fp16 scales, high plane k/4 or k/8 bytes
+    assert rq.rq_qweight_bytes(rq.RQ_W6_SYM, 32, 2560, 10240) == (2560 * 5120, 2560 * 320 * 2, 0, 2560 * 2560)
+    assert rq.rq_qweight_bytes(rq.RQ_W5_SYM, 64, 3, 256) == (3 * 128, 3 * 4 * 2, 0, 3 * 32)
+    assert rq.rq_qweight_bytes(rq.RQ_BF16, 0, 2560, 2560) == (2560 * 2560 * 2, 0, 0, 0)
+    c, s, m, sub = rq.rq_qweight_bytes(rq.RQ_W6_SYM, 64, 1, 128)
+    assert (c + s + m + sub) * 8 / 128 == 6.25
+    c, s, m, sub = rq.rq_qweight_bytes(rq.RQ_W5_SYM, 32, 1, 128)
+    assert (c + s + m + sub) * 8 / 128 == 5.5
+    for bad in [(rq.RQ_W4_SYM, 48, 4, 96), (10, 0, 4, 64), (rq.RQ_W4_ASYM_SB256, 64, 4, 256),
+                (rq.RQ_W6_SYM, 16, 4, 128), (rq.RQ_W5_SYM, 48, 4, 128)]:
         with pytest.raises(rq.RqError) as e:
             rq.rq_qweight_bytes(*bad)
         assert e.value.status == rq.RQ_ERR_FORMAT
     for bad in [(rq.RQ_W4_SYM, 64, 4, 96), (rq.RQ_W4_ASYM_SB256, 32, 4, 128), (rq.RQ_W8_SYM, 16, -1, 16),
-                (rq.RQ_W8_SYM, 16, 1, 0), (rq.RQ_F16, 0, 1, 12), (rq.RQ_W8_SYM, 16, 2 ** 31, 16)]:
+                (rq.RQ_W8_SYM, 16, 1, 0), (rq.RQ_F16, 0, 1, 12), (rq.RQ_W8_SYM, 16, 2 ** 31, 16),
+                (rq.RQ_W6_SYM, 32, 4, 96), (rq.RQ_W5_SYM, 64, 4, 192), (rq.RQ_BF16, 0, 4, 48)]:
         with pytest.raises(rq.RqError) as e:
             rq.rq_qweight_bytes(*bad)
         assert e.value.status == rq.RQ_ERR_SHAPE
@@ -249,3 +259,18 @@ def test_quantize_aw_validation():
     sb = _w(rq.RQ_W4_ASYM_SB256, 32, 4, 384, B, C, C + 0x1000, C + 0x2000)
     assert _status(rq.rq_quantize_aw, A, imp, sb) == rq.RQ_ERR_SHAPE         # K % 256
     rq.rq_quantize_aw(A, imp, _w(n=0, codes=B, scales=C))                    # empty: no-op
+
+
+def test_two_plane_and_bf16_validation():
+    x, y = C, C + 0x100000
+    w6 = _w(rq.RQ_W6_SYM, 32, 32, 256, A, B, None, A + 0x10000)
+    assert _status(rq.rq_gemm_small_m, x, 4, 256, _w(rq.RQ_W6_SYM, 32, 32, 256, A, B), y, 32) == rq.RQ_ERR_NULL
+    assert _status(rq.rq_gemm_small_m, x, 4, 256, _w(rq.RQ_W5_SYM, 32, 32, 256, A, B, None, A + 0x10008),
+                   y, 32) == rq.RQ_ERR_ALIGN
+    assert _status(rq.rq_gemm_small_m, x, 4, 256, _w(rq.RQ_W6_SYM, 16, 32, 256, A, B, None, A + 0x10000),
+                   y, 32) == rq.RQ_ERR_FORMAT
+    assert _status(rq.rq_gemm_small_m, x, 4, 256, w6, A + 0x10000, 32) == rq.RQ_ERR_ALIAS  # y on the high plane
+    assert _status(rq.rq_quantize_rtn, x, _w(rq.RQ_W6_SYM, 32, 32, 192, A, B, None, A + 0x10000)) == rq.RQ_ERR_SHAPE
+    assert _status(rq.rq_gemm_small_m, x, 4, 48, _w(rq.RQ_BF16, 0, 32, 48, A), y, 32) == rq.RQ_ERR_SHAPE
+    assert _status(rq.rq_gemm_w4, x, 4, 256, w6, y, 32) == rq.RQ_ERR_FORMAT
+    rq.rq_gemm_small_m(x, 0, 256, w6, y, 32)   # m == 0: no-op
