@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import gemm_rwkv_amd.rq as rq  # noqa: E402
-from gemm_rwkv_amd import synth  # noqa: E402
+from gemm_rwkv_amd import presets, synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
@@ -286,6 +286,84 @@ def _w4_gemm_rows(gen, dev, c, fmt, group, ms, label, graph_us):
             "frac_of_fp16_peak": round(flops / us / 1e6 / F16_PEAK_TFLOPS, 4)}
     del wsets
     return out
+
+
+class PresetSweep:
+    """Decode steps of the 2.9B shape (32 layers of width 2560, head
+    65536x2560) with every tensor in the format its rwkv-quant preset assigns
+    (gemm_rwkv_amd.presets): REDUCTION, COMPRESSION, and COMPRESSION with the
+    first block's output projection in bf16.  Weights are quantized on the GPU
+    from seeded normal fp32 matrices; one graph per (preset, M), activations
+    reused across layers as in Sweep."""
+
+    LAYERS, C, VOCAB = 32, 2560, 65536
+    NAMES = ("r", "k", "v", "o", "cmix_key", "cmix_value")
+
+    def __init__(self, gen, dev):
+        c = self.C
+        self.layers = {}
+        self.heads = {}
+        self.bf16_o0 = None
+        for name in presets.PRESETS:
+            ls = []
+            for li in range(self.LAYERS):
+                s = {}
+                for (mat, n, k), tn in zip(synth.layer_shapes(c), self.NAMES):
+                    wf = torch.randn(n, k, generator=gen, device=dev, dtype=torch.float32) * (1.0 / k ** 0.5)
+                    fmt, group = presets.scheme(name, tn, li)
+                    s[tn] = rq.quantize(wf, fmt, group)
+                    if name == "COMPRESSION" and tn == "o" and li == 0:
+                        self.bf16_o0 = rq.quantize(wf, *presets.BF16_FIRST_O)
+                    del wf
+                ls.append(s)
+            self.layers[name] = ls
+            wf = torch.randn(self.VOCAB, c, generator=gen, device=dev, dtype=torch.float32) * (1.0 / c ** 0.5)
+            self.heads[name] = rq.quantize(wf, *presets.scheme(name, "head", 0))
+            del wf
+        torch.cuda.empty_cache()
+        self.x = {}
+        self.y = {}
+
+    def variants(self):
+        return (("REDUCTION", "REDUCTION", False), ("COMPRESSION", "COMPRESSION", False),
+                ("COMPRESSION+bf16_o0", "COMPRESSION", True))
+
+    def weight_bytes(self, name, bf16_o0):
+        b = sum(q.nbytes() for s in self.layers[name] for q in s.values()) + self.heads[name].nbytes()
+        if bf16_o0:
+            b += self.bf16_o0.nbytes() - self.layers[name][0]["o"].nbytes()
+        return b
+
+    def step(self, name, bf16_o0, m):
+        c = self.C
+        if m not in self.x:
+            self.x[m] = (f16_dev(synth.act_massive(m, c, cfg=2, salt=1), "cuda"),
+                         f16_dev(synth.act_massive(m, 4 * c, cfg=2, salt=2), "cuda"))
+            self.y[m] = {nm: torch.empty(m * n, dtype=torch.int16, device="cuda")
+                         for nm, n in (("r", c), ("k", c), ("v", c), ("o", c), ("key", 4 * c), ("val", c),
+                                       ("head", self.VOCAB))}
+        x, x4 = self.x[m]
+        y = self.y[m]
+        for li, s in enumerate(self.layers[name]):
+            o = self.bf16_o0 if (bf16_o0 and li == 0) else s["o"]
+            rq.rq_fused_rkv(x, x, x, m, c, s["r"], s["k"], s["v"], y["r"], y["k"], y["v"], c)
+            rq.rq_gemm_small_m(x, m, c, o, y["o"], c)
+            rq.rq_gemm_small_m(x, m, c, s["cmix_key"], y["key"], 4 * c)
+            rq.rq_gemm_small_m(x4, m, 4 * c, s["cmix_value"], y["val"], c)
+        rq.rq_gemm_small_m(x, m, c, self.heads[name], y["head"], self.VOCAB)
+
+    def run(self, steps, warmup):
+        out = {}
+        for label, name, b16 in self.variants():
+            wb = self.weight_bytes(name, b16)
+            per_m = {}
+            for m in (1, 4, 16):
+                g = capture(lambda m=m: self.step(name, b16, m))
+                ms = time_graph(g, steps, warmup)
+                per_m[str(m)] = {"ms": round(ms, 4), "GB_s": round(wb / (ms * 1e-3) / 1e9, 1)}
+                del g
+            out[label] = {"weight_bytes": wb, "per_m": per_m}
+        return out
 
 
 def measure_rows(gen, dev, reps=20):
@@ -684,6 +762,7 @@ def main():
     ap.add_argument("--class-reps", type=int, default=20)
     ap.add_argument("--no-sweep", action="store_true", help="skip the 13.3B decode-step sweep")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    ap.add_argument("--no-presets", action="store_true", help="skip the 2.9B preset decode sweeps")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per kernel and launch shape: dispatches and mean duration, from a "
                          "rocprofv3 --kernel-trace CSV")
@@ -777,6 +856,18 @@ def main():
             for m, r in res.items():
                 print("sweep 13.3B M=%-2s %8.3f ms  %7.1f GB/s" % (m, r["ms"], r["GB_s"]), file=sys.stderr)
         del sw
+    if not args.no_presets:
+        torch.cuda.empty_cache()
+        ps = PresetSweep(gen, dev)
+        res = ps.run(max(3, args.steps // 2), 2)
+        out["presets_2p9b"] = {"workload": "32 x (fused R/K/V, O, cmix key, cmix value) at width 2560 + head "
+                                           "65536x2560, each tensor in its rwkv-quant preset format, one graph "
+                                           "of 129 launches per M", "variants": res}
+        if args.phases:
+            for label, r in res.items():
+                for m, v in r["per_m"].items():
+                    print("preset %-20s M=%-2s %8.3f ms  %7.1f GB/s" % (label, m, v["ms"], v["GB_s"]), file=sys.stderr)
+        del ps
     if not args.no_rows:
         torch.cuda.empty_cache()
         out["rows"] = measure_rows(gen, dev)
