@@ -499,10 +499,22 @@ __device__ __forceinline__ void split_bf16(const half8& a, bf16x8& hi, bf16x8& l
 
 // MR: activation rows that can be non-zero among a lane's four outputs
 // (m <= MR), so scale multiplications skip rows that are known to be zero.
-template <int FMT, int G, int MT, int CPW, int MR>
+//
+// ST (streamed, two activation tiles, 128-k chunks, one row tile, no split):
+// instead of one activation slice shared through LDS, every wave copies the
+// activations of its own chunks, one chunk at a time, into a private double
+// buffer of 32 rows x 128 k (rows >= M read zeros through the buffer
+// resource's range check), and computes chunk i while chunk i + 1 arrives.
+// Rows are 256 bytes with the 16-byte segment s of row r stored at slot
+// s ^ (r & 15), so the sixteen rows an MFMA operand read touches fall in
+// distinct banks.  A workgroup then covers all of K for its 16 rows without a
+// second, reducing launch, at any K; the cost is that each workgroup reads all
+// of x.
+template <int FMT, int G, int MT, int CPW, int MR, bool ST = false>
 __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
   typedef CodeSlot<FMT, G> S;
+  static_assert(!ST || (MT == 2 && F::CK == 128), "streamed activations: two tiles, 128-k chunks");
   extern __shared__ uint4 lds4[];
   uint16_t* xl = (uint16_t*)lds4;
 
@@ -644,7 +656,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
   };
   constexpr bool kCodesFirst = MT == 2;
-  if constexpr (!kCodesFirst) copy_x();
+  if constexpr (!kCodesFirst && !ST) copy_x();
 
   // 2. this wave's codes and scales, all at once.  Chunks outside the slice
   //    (or of a tile past the matrix) read zero codes; their scales are zeroed
@@ -706,7 +718,27 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   //    (a wave's vector loads complete in issue order), and each chunk below
   //    waits only for its own code load.  Codes first: everything.  Then a
   //    plain barrier.
-  if constexpr (kCodesFirst) {
+  // streamed: this wave's buffers and the copy of one chunk (8 DMA reads of
+  // 4 rows x 256 bytes; lane l: row 4q + l / 16, slot l % 16)
+  constexpr int kStBuf = 32 * 128 * 2;  // bytes per buffer
+  const uint32_t st_lds = lds_base + (uint32_t)wave * (2u * kStBuf);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A.x, (short)0, (int)((uint32_t)M * (uint32_t)p.ldx * 2u), 0x00020000);
+  const uint32_t st_r = (uint32_t)(lane >> 4), st_s = (uint32_t)(lane & 15);
+  auto st_copy = [&](int i) {  // chunk c0 + i (clamped inside the slice) into buffer i & 1
+    const int c = c0 + i < cend ? c0 + i : cend - 1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t r = 4u * q + st_r;
+      const uint32_t voff = r * (uint32_t)p.ldx * 2u + (uint32_t)c * 256u + ((st_s ^ (r & 15u)) << 4);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :: "v"(voff), "s"(rx), "s"(st_lds + (uint32_t)(i & 1) * kStBuf + 1024u * q) : "memory", "m0");
+    }
+  };
+  if constexpr (ST) {
+    st_copy(0);
+    if (CPW > 1) st_copy(1);
+  } else if constexpr (kCodesFirst) {
     copy_x();
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
@@ -732,6 +764,11 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     const bool valid = tvalid && c0 + i < cend;
     const int c = c0 + i < cend ? c0 + i : cend - 1;  // activation offset inside the slice
     const int kk = (c - cbeg) * F::CK;
+    if constexpr (ST) {
+      // chunk i has landed once only chunk i + 1's eight copies may be in flight
+      if (i + 1 < CPW) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     uint32_t w[4] = {sl[i].c.x, sl[i].c.y, sl[i].c.z, sl[i].c.w};
     uint32_t gw[4][2], gh[4][2];
     // the high plane's words go through the same exchange as the code words
@@ -817,7 +854,15 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
           }
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
-            const half8 a = *(const half8*)(xl + xrow[t] + xo);
+            half8 a;
+            if constexpr (ST) {
+              // row t * 16 + j of buffer i & 1, segment (x offset / 8) at slot seg ^ j
+              const int seg = (x_base<FMT, G>(kq) + x_const<FMT, G>(g, pp)) >> 3;
+              a = *(const half8*)(xl + ((i & 1) * kStBuf + wave * 2 * kStBuf) / 2 + (t * 16 + j) * 128 +
+                                  ((seg ^ j) << 3));
+            } else {
+              a = *(const half8*)(xl + xrow[t] + xo);
+            }
             if constexpr (FMT == GF_F16) {
               acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
             } else if constexpr (FMT == GF_BF16) {
@@ -852,6 +897,13 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
             acc[t][q] += scl[g] * grp[t][q];
             if constexpr (FMT == GF_SB) acc[t][q] -= mnv[g] * xs[t][q];
           }
+      }
+    }
+    if constexpr (ST) {
+      // buffer i & 1 is free once this chunk's reads have returned
+      if (i + 2 < CPW) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        st_copy(i + 2);
       }
     }
   }
@@ -938,11 +990,34 @@ static int pick_cpw(int cps, bool allow16) {
 // unit; then as many row tiles per workgroup (up to 4, sharing the x slice)
 // as still keep that many workgroups.
 template <int FMT, int G>
-static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out) {
+static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out) {
   typedef F2<FMT, G> F;
   const int nchunks = b.k / F::CK;
   const int mt = b.m <= 16 ? 1 : 2;
   bool found = false;
+  stream_out = false;
+  // two activation tiles whose slice does not fit one workgroup's LDS: stream
+  // it per wave (one row tile per workgroup, eight waves of 2, 4 or 8 chunks)
+  // rather than split K, when that makes 192 to 256 workgroups (one per CU).
+  // Measured: O 4096x4096 at M = 32 gains 2.6 us over the split plan; with
+  // fewer row tiles (2048x8192, 128) the split plan is faster, since each
+  // workgroup streams all of x through one CU.
+  if constexpr (F::CK == 128) {
+    int tiles = 0;
+    for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
+    const size_t xb = (size_t)(b.m + 1) * (nchunks * F::CK + 8) * 2;
+    if (mt == 2 && xb > (size_t)kXBudgetUnsplit && nchunks <= 64 && tiles >= 192 && tiles <= 256) {
+      const int cpw = nchunks <= 16 ? 2 : (nchunks <= 32 ? 4 : 8);
+      sp.split = 1;
+      sp.cps = nchunks;
+      sp.wpt = (nchunks + cpw - 1) / cpw;
+      sp.rt = 1;
+      for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? b.mat[i].tiles : 0;
+      cpw_out = cpw;
+      stream_out = true;
+      return true;
+    }
+  }
   // row tiles share a workgroup (and its activation slice) only where that
   // slice is larger than the tile's codes, 16 rows x 64 bytes per chunk
   const bool share_x = (b.m + 1) * F::CK * 2 > 16 * 64;
@@ -1020,10 +1095,11 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   typedef F2<FMT, G> F;
   Split5 sp;
   int cpw = 4;
-  if (!plan5<FMT, G>(b, sp, cpw)) return false;
+  bool stream = false;
+  if (!plan5<FMT, G>(b, sp, cpw, stream)) return false;
   const int mt = b.m <= 16 ? 1 : 2;
   const int nw = sp.rt * sp.wpt;
-  const size_t xb = (size_t)(b.m + 1) * (sp.cps * F::CK + 8) * 2;
+  const size_t xb = stream ? (size_t)nw * 2 * (32 * 128 * 2) : (size_t)(b.m + 1) * (sp.cps * F::CK + 8) * 2;
   const size_t red = (size_t)nw * mt * 4 * 64 * 4;
   const size_t lds = xb > red ? xb : red;
   const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
@@ -1039,6 +1115,23 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
     (void)attr_set;                                                                               \
     hipLaunchKernelGGL((gemv5_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b, sp);         \
   } while (0)
+#define RQ_L5S(CPW)                                                                               \
+  do {                                                                                            \
+    static const bool attr_set =                                                                  \
+        hipFuncSetAttribute((const void*)gemv5_kernel<FMT, G, 2, CPW, 4, true>,                   \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kXBudgetUnsplit + 1024) == \
+        hipSuccess;                                                                               \
+    (void)attr_set;                                                                               \
+    hipLaunchKernelGGL((gemv5_kernel<FMT, G, 2, CPW, 4, true>), grid, block, lds, st, b, sp);     \
+  } while (0)
+  if constexpr (F::CK == 128) {
+    if (stream) {
+      if (cpw == 2) RQ_L5S(2); else if (cpw == 4) RQ_L5S(4); else RQ_L5S(8);
+      err = hipGetLastError();
+      return true;
+    }
+  }
+#undef RQ_L5S
   if (mt == 2) {
     if (cpw == 2) RQ_L5(2, 2, 4); else if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
   } else if constexpr (FMT == GF_SB || F::HW > 0) {

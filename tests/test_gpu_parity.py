@@ -424,3 +424,25 @@ def test_fp8_integer_operands_exact():
     exact = x.astype(np.int64) @ w.astype(np.int64).T
     assert np.abs(exact).max() < 2048
     assert np.array_equal(host(y.t, np.float16).reshape(m, n).astype(np.float64), exact.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt,group", [(quant.W4_SYM, 64), (quant.W4_SYM, 32), (quant.W4_ASYM_SB256, 32),
+                                       (quant.W6_SYM, 64), (quant.W5_SYM, 32)])
+@pytest.mark.parametrize("n,k", [(3100, 2560), (4000, 4096), (3580, 8192), (200, 4096)])
+def test_streamed_activation_chunks(fmt, group, n, k):
+    """M > 16 with an activation slice too large for one workgroup's LDS and
+    192..256 row tiles: each wave streams its own chunks through a private
+    double buffer (K = 2560 leaves the last wave with a ragged chunk range;
+    rows >= M read zeros; n = 3100 and 3580 end in a partial tile).  The
+    200-row case takes the split plan."""
+    w = _weights(n, k, seed=n * 5 + k)
+    parts = quant.quantize(w, fmt, group)
+    qw = qweight_from_oracle(fmt, group, parts, n, k)
+    ldx = k + 16
+    for m in (17, 24, 32):
+        g = np.random.default_rng(m + k)
+        x = g.standard_normal((m, ldx)).astype(np.float16)
+        y = _run_small_m(qw, x, m, ldx, n)
+        y_ref, b = ref.weight_only_ref(x[:, :k], fmt, parts, group)
+        ok, info = ref.compare(y, y_ref, b)
+        assert ok, (m, info)
