@@ -515,6 +515,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   typedef F2<FMT, G> F;
   typedef CodeSlot<FMT, G> S;
   static_assert(!ST || (MT == 2 && F::CK == 128), "streamed activations: two tiles, 128-k chunks");
+  static_assert(FMT != GF_SB || CPW % 2 == 0, "SB256: a wave's chunks pair into superblocks");
   extern __shared__ uint4 lds4[];
   uint16_t* xl = (uint16_t*)lds4;
 
@@ -695,6 +696,10 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
       sl[i].hi[0] = __builtin_amdgcn_raw_buffer_load_b32(rb, subb, valid ? (uint32_t)c * 16u : kOOB, 0);
     }
     if constexpr (FMT == GF_SB) {
+      // a superblock is two chunks and a wave's chunk range starts even (CPW
+      // and the slice length are even): load its scales once, with the pair's
+      // first chunk
+      if (i & 1) continue;
       const uint32_t sb = (uint32_t)c >> 1;
       const uint32_t s2 = valid ? sb * 2u : kOOB;
       const uint32_t s12 = valid ? sb * 12u : kOOB;
@@ -815,10 +820,11 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
         scl[g] = valid ? v : 0.f;
       }
     } else if constexpr (FMT == GF_SB) {
-      const float d = f16_bits_to_f32((uint16_t)(sl[i].s & 0xffffu));
-      const float dm = f16_bits_to_f32((uint16_t)(sl[i].s >> 16));
-      const uint64_t lo48 = (uint64_t)sl[i].sub[0] | ((uint64_t)(sl[i].sub[1] & 0xffffu) << 32);
-      const uint64_t hi48 = (uint64_t)(sl[i].sub[1] >> 16) | ((uint64_t)sl[i].sub[2] << 16);
+      const S& sp2 = sl[i & ~1];  // the superblock's scales, loaded with its first chunk
+      const float d = f16_bits_to_f32((uint16_t)(sp2.s & 0xffffu));
+      const float dm = f16_bits_to_f32((uint16_t)(sp2.s >> 16));
+      const uint64_t lo48 = (uint64_t)sp2.sub[0] | ((uint64_t)(sp2.sub[1] & 0xffffu) << 32);
+      const uint64_t hi48 = (uint64_t)(sp2.sub[1] >> 16) | ((uint64_t)sp2.sub[2] << 16);
       const int half = (c & 1) * 4;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -1058,8 +1064,9 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     if (split > 1 && !b.ws) break;
     // a wave's scale span is loaded from byte c0 * 2 * GPC and must start on a
     // 4-byte boundary: with one scale per chunk (int8 group 64) slices hold an
-    // even number of chunks (CPW is even)
-    constexpr int cmult = (F::GPC == 1 && F::SYMS) ? 2 : 1;
+    // even number of chunks (CPW is even).  SB256 slices are even too, so a
+    // wave's chunk pairs are whole superblocks.
+    constexpr int cmult = ((F::GPC == 1 && F::SYMS) || FMT == GF_SB) ? 2 : 1;
     const int cps = ((nchunks + split - 1) / split + cmult - 1) / cmult * cmult;
     if ((split - 1) * cps >= nchunks) continue;  // an empty slice
     const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
