@@ -105,7 +105,7 @@ def _run_small_m(qw, x, m, ldx, n):
 
 
 @pytest.mark.parametrize("fmt,group", W56 + [(quant.BF16, 0)])
-@pytest.mark.parametrize("n,k", [(1, 256), (7, 512), (65, 768), (160, 2048), (48, 8192)])
+@pytest.mark.parametrize("n,k", [(3, 128), (1, 256), (7, 512), (65, 768), (160, 2048), (48, 8192)])
 @pytest.mark.parametrize("m", [1, 2, 5, 16, 17, 32])
 def test_small_m_56_bf16_parity(fmt, group, n, k, m):
     w = _weights(n, k, seed=n + k + m)
