@@ -1002,6 +1002,17 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
   const int mt = b.m <= 16 ? 1 : 2;
   bool found = false;
   stream_out = false;
+  // the kernel addresses every buffer through a buffer resource with a 32-bit
+  // size and 32-bit offsets: each must stay below 2 GiB
+  constexpr size_t kLim = (size_t)1 << 31;
+  for (int i = 0; i < b.nmat; ++i) {
+    const size_t n = (size_t)b.mat[i].n;
+    if (n * (size_t)nchunks * 64u >= kLim) return false;
+    if (F::SYMS && n * (size_t)(b.k / F::GK) * 2u >= kLim) return false;
+    if (FMT == GF_SB && n * (size_t)(b.k / 256) * 12u >= kLim) return false;
+    if (F::HW > 0 && n * (size_t)(b.k / 8) * 2u >= kLim) return false;
+  }
+  if ((size_t)b.m * (size_t)b.ldx * 2u >= kLim) return false;
   // two activation tiles whose slice does not fit one workgroup's LDS: stream
   // it per wave (one row tile per workgroup, eight waves of 2, 4 or 8 chunks)
   // rather than split K, when that makes 192 to 256 workgroups (one per CU).

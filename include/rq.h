@@ -197,8 +197,8 @@ int rq_quantize_rtn(const float *w, const rq_qweight *out, void *stream);
  * in fp64; the smallest t within a factor 1 + 2^-40 of the lowest score is
  * kept (step 0 is RTN, so an all-zero act_sq gives rq_quantize_rtn's bytes).
  * Superblock weights then take the RTN superblock step with the chosen group
- * parameters.  Formats: RQ_W8_SYM, RQ_W4_SYM, RQ_W4_ASYM_SB256, else
- * RQ_ERR_FORMAT.  Synchronization, allocation and errors as rq_quantize_rtn;
+ * parameters.  Formats: RQ_W8_SYM, RQ_W4_SYM, RQ_W6_SYM, RQ_W5_SYM,
+ * RQ_W4_ASYM_SB256, else RQ_ERR_FORMAT.  Synchronization, allocation and errors as rq_quantize_rtn;
  * a NaN, Inf or negative act_sq entry gives RQ_ERR_NONFINITE.  act_sq may
  * not overlap an output buffer (RQ_ERR_ALIAS). */
 int rq_quantize_aw(const float *w, const float *act_sq, const rq_qweight *out, void *stream);
@@ -220,8 +220,11 @@ int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *strea
 /* Small-M products for decode batches 1 <= m <= 32 (model card, summary:
  * batch sizes up to 32).  x: fp16 [m][ldx], ldx >= k, ldx % 8 == 0;
  * y: fp16 [m][ldy], ldy >= n.  Accepts RQ_W8_SYM, RQ_W4_SYM,
- * RQ_W4_ASYM_SB256 and RQ_F16.  The weights are read once per call.
- * Errors: RQ_ERR_SHAPE for m outside 0..32. */
+ * RQ_W4_ASYM_SB256, RQ_F16, RQ_W6_SYM, RQ_W5_SYM and RQ_BF16.  The weights
+ * are read once per call.
+ * Errors: RQ_ERR_SHAPE for m outside 0..32, and for RQ_W6_SYM, RQ_W5_SYM and
+ * RQ_BF16 when one weight buffer or the activation span m * ldx * 2 reaches
+ * 2^31 bytes (the other formats take any size). */
 int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w,
                     uint16_t *y, int64_t ldy, void *stream);
 
