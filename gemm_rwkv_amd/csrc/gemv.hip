@@ -417,12 +417,15 @@ constexpr int kXBudgetUnsplit = 150 * 1024;
 // ---------------------------------------------------------------------------
 // the streaming kernel: a workgroup = RT row tiles x one slice of K
 // ---------------------------------------------------------------------------
-// Every wave owns CPW chunks of one 16-row tile and issues all of their code
-// and scale loads before it computes (with few chunks per wave that keeps the
-// most bytes in flight; vector loads of a wave complete in issue order, so
-// nothing is loaded behind them).  The workgroup's waves then copy its slice
-// of the activations (rows < M) into LDS with global_load_lds, a zero row
-// stands for m >= M, and after one barrier the waves compute from LDS.
+// Every wave owns CPW chunks of one 16-row tile and issues its code and scale
+// loads before it computes: all of them up to eight chunks (that keeps the most
+// bytes in flight; vector loads of a wave complete in issue order, so nothing
+// is loaded behind them), a window of eight for sixteen.  The workgroup's waves
+// copy its slice of the activations (rows < M) into LDS with global_load_lds,
+// a zero row stands for m >= M, and after one barrier the waves compute from
+// LDS.  (An output row depends only on its own operand row, so rows >= M
+// could read any row; reading row 0, or a zeroed region of one chunk, and not
+// writing a whole zero row both measured 6-11% slower at M = 1.)
 //
 // K is cut into `split` slices of cps chunks.  The waves of a tile reduce
 // through LDS in wave order; with split = 1 they store fp16, otherwise each
@@ -659,10 +662,14 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   constexpr bool kCodesFirst = MT == 2;
   if constexpr (!kCodesFirst && !ST) copy_x();
 
-  // 2. this wave's codes and scales, all at once.  Chunks outside the slice
-  //    (or of a tile past the matrix) read zero codes; their scales are zeroed
-  //    after loading (the scale span is read in one piece and may run into
-  //    the next slice or row)
+  // 2. this wave's scales and codes: all of them, or for sixteen chunks at
+  //    M <= 2 a window of eight, the next issued as each chunk is computed.
+  //    (With all sixteen issued at once a wave reaches its first chunk's math
+  //    only once its last load has issued, when most of its bytes have
+  //    arrived; the window made 4096x16384 at M = 1 and 2 8% faster.)
+  //    Chunks outside the slice (or of a tile past the matrix) read zero
+  //    codes; their scales are zeroed after loading (the scale span is read
+  //    in one piece and may run into the next slice or row)
   const int c0 = cbeg + wv * CPW;
   S sl[CPW];
   constexpr int SW = F::SYMS ? (CPW * F::GPC * 2 + 3) / 4 : 1;  // scale words
@@ -682,8 +689,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
       sw[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, ss, 0);
     }
   }
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
+  auto load_chunk = [&](int i) {
     const int c = c0 + i;
     const bool valid = tvalid && c < cend;
     auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, valid ? (uint32_t)c * 64u : kOOB, 0);
@@ -699,7 +705,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
       // a superblock is two chunks and a wave's chunk range starts even (CPW
       // and the slice length are even): load its scales once, with the pair's
       // first chunk
-      if (i & 1) continue;
+      if (i & 1) return;
       const uint32_t sb = (uint32_t)c >> 1;
       const uint32_t s2 = valid ? sb * 2u : kOOB;
       const uint32_t s12 = valid ? sb * 12u : kOOB;
@@ -711,15 +717,18 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
       sl[i].sub[1] = t[1];
       sl[i].sub[2] = t[2];
     }
-  }
+  };
+  constexpr int RD = (CPW == 16 && MR <= 2 && !ST && !kCodesFirst) ? 8 : CPW;  // loads in flight
+#pragma unroll
+  for (int i = 0; i < RD; ++i) load_chunk(i);
 
   // keep everything that uses the loaded scales below this point: hoisted
   // between the loads, it would wait for the scale load before the first
   // code load is issued
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. wait for this wave's copies.  Copies first: with at most CPW loads
-  //    still in flight, every DMA issued before the CPW code loads has landed
+  // 3. wait for this wave's copies.  Copies first: with at most RD loads
+  //    still in flight, every DMA issued before the RD code loads has landed
   //    (a wave's vector loads complete in issue order), and each chunk below
   //    waits only for its own code load.  Codes first: everything.  Then a
   //    plain barrier.
@@ -748,8 +757,8 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
     // with a high plane two loads follow per chunk: every copy has landed
-    // once no more than 2 * CPW are in flight
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(F::HW > 0 ? 2 * CPW : CPW) : "memory");
+    // once no more than 2 * RD are in flight
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(F::HW > 0 ? 2 * RD : RD) : "memory");
   }
 
   int xrow[MT];
@@ -769,6 +778,10 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     const bool valid = tvalid && c0 + i < cend;
     const int c = c0 + i < cend ? c0 + i : cend - 1;  // activation offset inside the slice
     const int kk = (c - cbeg) * F::CK;
+    if constexpr (RD < CPW) {
+      if (i + RD < CPW) load_chunk(i + RD);
+      __builtin_amdgcn_sched_barrier(0);  // keep the load here, ahead of this chunk's math
+    }
     if constexpr (ST) {
       // chunk i has landed once only chunk i + 1's eight copies may be in flight
       if (i + 1 < CPW) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
