@@ -503,11 +503,11 @@ __device__ __forceinline__ void split_bf16(const half8& a, bf16x8& hi, bf16x8& l
 // MR: activation rows that can be non-zero among a lane's four outputs
 // (m <= MR), so scale multiplications skip rows that are known to be zero.
 //
-// ST (streamed, two activation tiles, 128-k chunks, one row tile, no split):
-// instead of one activation slice shared through LDS, every wave copies the
-// activations of its own chunks, one chunk at a time, into a private double
-// buffer of 32 rows x 128 k (rows >= M read zeros through the buffer
-// resource's range check), and computes chunk i while chunk i + 1 arrives.
+// ST (streamed, 128-k chunks, one row tile, no split): instead of one
+// activation slice shared through LDS, every wave copies the activations of
+// its own chunks, one chunk at a time, into a private double buffer of 16 MT
+// rows x 128 k (rows >= M read zeros through the buffer resource's range
+// check), and computes chunk i while chunk i + 1 arrives.
 // Rows are 256 bytes with the 16-byte segment s of row r stored at slot
 // s ^ (r & 15), so the sixteen rows an MFMA operand read touches fall in
 // distinct banks.  A workgroup then covers all of K for its 16 rows without a
@@ -517,7 +517,7 @@ template <int FMT, int G, int MT, int CPW, int MR, bool ST = false>
 __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
   typedef CodeSlot<FMT, G> S;
-  static_assert(!ST || (MT == 2 && F::CK == 128), "streamed activations: two tiles, 128-k chunks");
+  static_assert(!ST || F::CK == 128, "streamed activations: 128-k chunks");
   static_assert(FMT != GF_SB || CPW % 2 == 0, "SB256: a wave's chunks pair into superblocks");
   extern __shared__ uint4 lds4[];
   uint16_t* xl = (uint16_t*)lds4;
@@ -567,15 +567,35 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   const uint32_t coff = (nvalid ? (uint32_t)n * rowbytes : 0u) + (uint32_t)kq * 16u;
   __amdgpu_buffer_rsrc_t rs = rc, rm = rc, rb = rc;
   uint32_t soff = 0, sboff = 0, subb = 0;
+  // int8 group 64 stores 2 bytes of scales per chunk, so after a row with an
+  // odd number of chunks the next row starts in the middle of a dword.  Such
+  // a row loads its scale span from the dword below, one word longer, and
+  // shifts it down 16 bits (sh16) before use: every dword the range check
+  // sees is then aligned to the buffer, and only the buffer's last dword can
+  // end past the (rounded-up) range.
+  constexpr bool kHalfRow = F::SYMS && F::GPC == 1;
+  uint32_t sh16 = 0;
   if constexpr (F::HW > 0) {
     const uint32_t hrow = (uint32_t)(k / 8) * (FMT == GF_W6 ? 2u : 1u);
     rb = __builtin_amdgcn_make_buffer_rsrc((void*)A.sub, (short)0, (int)((uint32_t)A.n * hrow), 0x00020000);
     subb = (nvalid ? (uint32_t)n * hrow : 0u) + (uint32_t)kq * (4u * F::HW);
   }
   if constexpr (F::SYMS) {
+    // the range is rounded up to whole dwords: the range check zeroes a
+    // dword that ends past it as a whole, and with an odd number of groups
+    // per row (int8 group 64) and an odd number of rows the last scale shares
+    // its dword with the two bytes after the buffer.  Those bytes lie in the
+    // same aligned dword (the buffer starts 16-byte aligned), so never in
+    // another page; like the next row's scales that a wave's span reaches,
+    // they belong to chunks past the slice, whose scales are dropped.
     const uint32_t srow = (uint32_t)(k / F::GK) * 2u;
-    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * srow), 0x00020000);
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)(((uint32_t)A.n * srow + 3u) & ~3u),
+                                           0x00020000);
     soff = nvalid ? (uint32_t)n * srow : 0u;
+    if constexpr (kHalfRow) {
+      sh16 = (soff & 2u) << 3;
+      soff &= ~3u;
+    }
   } else if constexpr (FMT == GF_SB) {
     const uint32_t nsb = (uint32_t)(k / 256);
     rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)((uint32_t)A.n * nsb * 2u), 0x00020000);
@@ -672,21 +692,24 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   //    in one piece and may run into the next slice or row)
   const int c0 = cbeg + wv * CPW;
   S sl[CPW];
-  constexpr int SW = F::SYMS ? (CPW * F::GPC * 2 + 3) / 4 : 1;  // scale words
+  constexpr int SW = F::SYMS ? (CPW * F::GPC * 2 + 3) / 4 + (kHalfRow ? 1 : 0) : 1;  // scale words
   uint32_t sw[SW];
   if constexpr (F::SYMS) {
     const uint32_t ss = tvalid ? (uint32_t)c0 * (F::GPC * 2) : kOOB;
-    if constexpr (SW >= 4) {
 #pragma unroll
-      for (int q = 0; q < SW / 4; ++q) {
-        auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, soff, ss + 16u * q, 0);
-        sw[4 * q] = t[0]; sw[4 * q + 1] = t[1]; sw[4 * q + 2] = t[2]; sw[4 * q + 3] = t[3];
-      }
-    } else if constexpr (SW == 2) {
-      auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, ss, 0);
-      sw[0] = t[0]; sw[1] = t[1];
-    } else {
-      sw[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, ss, 0);
+    for (int q = 0; q < SW / 4; ++q) {
+      auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, soff, ss + 16u * q, 0);
+      sw[4 * q] = t[0]; sw[4 * q + 1] = t[1]; sw[4 * q + 2] = t[2]; sw[4 * q + 3] = t[3];
+    }
+    constexpr int B = SW / 4 * 4;
+    if constexpr (SW % 4 == 3) {
+      auto t = __builtin_amdgcn_raw_buffer_load_b96(rs, soff, ss + 4u * B, 0);
+      sw[B] = t[0]; sw[B + 1] = t[1]; sw[B + 2] = t[2];
+    } else if constexpr (SW % 4 == 2) {
+      auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, soff, ss + 4u * B, 0);
+      sw[B] = t[0]; sw[B + 1] = t[1];
+    } else if constexpr (SW % 4 == 1) {
+      sw[B] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, ss + 4u * B, 0);
     }
   }
   auto load_chunk = [&](int i) {
@@ -732,9 +755,10 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   //    (a wave's vector loads complete in issue order), and each chunk below
   //    waits only for its own code load.  Codes first: everything.  Then a
   //    plain barrier.
-  // streamed: this wave's buffers and the copy of one chunk (8 DMA reads of
-  // 4 rows x 256 bytes; lane l: row 4q + l / 16, slot l % 16)
-  constexpr int kStBuf = 32 * 128 * 2;  // bytes per buffer
+  // streamed: this wave's buffers and the copy of one chunk (4 MT DMA reads
+  // of 4 rows x 256 bytes; lane l: row 4q + l / 16, slot l % 16)
+  constexpr int kStBuf = 16 * MT * 128 * 2;  // bytes per buffer
+  constexpr int kStCopies = 4 * MT;          // DMA reads per chunk
   const uint32_t st_lds = lds_base + (uint32_t)wave * (2u * kStBuf);
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc((void*)A.x, (short)0, (int)((uint32_t)M * (uint32_t)p.ldx * 2u), 0x00020000);
@@ -742,7 +766,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   auto st_copy = [&](int i) {  // chunk c0 + i (clamped inside the slice) into buffer i & 1
     const int c = c0 + i < cend ? c0 + i : cend - 1;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kStCopies; ++q) {
       const uint32_t r = 4u * q + st_r;
       const uint32_t voff = r * (uint32_t)p.ldx * 2u + (uint32_t)c * 256u + ((st_s ^ (r & 15u)) << 4);
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
@@ -771,6 +795,10 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
   const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kHalfRow) {
+#pragma unroll
+    for (int i = 0; i + 1 < SW; ++i) sw[i] = __builtin_amdgcn_alignbit(sw[i + 1], sw[i], sh16);
+  }
 
   // 4. compute, chunk by chunk
 #pragma unroll
@@ -783,8 +811,8 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
       __builtin_amdgcn_sched_barrier(0);  // keep the load here, ahead of this chunk's math
     }
     if constexpr (ST) {
-      // chunk i has landed once only chunk i + 1's eight copies may be in flight
-      if (i + 1 < CPW) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      // chunk i has landed once only chunk i + 1's copies may be in flight
+      if (i + 1 < CPW) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kStCopies) : "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     uint32_t w[4] = {sl[i].c.x, sl[i].c.y, sl[i].c.z, sl[i].c.w};
@@ -1026,17 +1054,20 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     if (F::HW > 0 && n * (size_t)(b.k / 8) * 2u >= kLim) return false;
   }
   if ((size_t)b.m * (size_t)b.ldx * 2u >= kLim) return false;
-  // two activation tiles whose slice does not fit one workgroup's LDS: stream
-  // it per wave (one row tile per workgroup, eight waves of 2, 4 or 8 chunks)
-  // rather than split K, when that makes 192 to 256 workgroups (one per CU).
-  // Measured: O 4096x4096 at M = 32 gains 2.6 us over the split plan; with
-  // fewer row tiles (2048x8192, 128) the split plan is faster, since each
-  // workgroup streams all of x through one CU.
+  // an activation slice that does not fit one workgroup's LDS: stream it per
+  // wave (one row tile per workgroup, waves of 2, 4 or 8 chunks) rather than
+  // split K, when that makes 192 to 256 workgroups (one per CU) and the
+  // waves' buffers fit.  Measured: O 4096x4096 at M = 32 gains 2.6 us over
+  // the split plan, 4096x16384 at M = 4 and 8 0.9 and 1.2 us (at M = 12 no
+  // change, at M = 16 0.5 us slower: one activation tile streams only up to
+  // M = 8); with fewer row tiles (2048x8192, 128) the split plan is faster,
+  // since each workgroup streams all of x through one CU.
   if constexpr (F::CK == 128) {
     int tiles = 0;
     for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
     const size_t xb = (size_t)(b.m + 1) * (nchunks * F::CK + 8) * 2;
-    if (mt == 2 && xb > (size_t)kXBudgetUnsplit && nchunks <= 64 && tiles >= 192 && tiles <= 256) {
+    if (xb > (size_t)kXBudgetUnsplit && (mt == 2 || b.m <= 8) && nchunks <= 64 * (3 - mt) && tiles >= 192 &&
+        tiles <= 256) {
       const int cpw = nchunks <= 16 ? 2 : (nchunks <= 32 ? 4 : 8);
       sp.split = 1;
       sp.cps = nchunks;
@@ -1130,7 +1161,7 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   if (!plan5<FMT, G>(b, sp, cpw, stream)) return false;
   const int mt = b.m <= 16 ? 1 : 2;
   const int nw = sp.rt * sp.wpt;
-  const size_t xb = stream ? (size_t)nw * 2 * (32 * 128 * 2) : (size_t)(b.m + 1) * (sp.cps * F::CK + 8) * 2;
+  const size_t xb = stream ? (size_t)nw * 2 * (16 * mt * 128 * 2) : (size_t)(b.m + 1) * (sp.cps * F::CK + 8) * 2;
   const size_t red = (size_t)nw * mt * 4 * 64 * 4;
   const size_t lds = xb > red ? xb : red;
   const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
@@ -1146,18 +1177,22 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
     (void)attr_set;                                                                               \
     hipLaunchKernelGGL((gemv5_kernel<FMT, G, MT, CPW, MR>), grid, block, lds, st, b, sp);         \
   } while (0)
-#define RQ_L5S(CPW)                                                                               \
+#define RQ_L5S(MT, CPW)                                                                           \
   do {                                                                                            \
     static const bool attr_set =                                                                  \
-        hipFuncSetAttribute((const void*)gemv5_kernel<FMT, G, 2, CPW, 4, true>,                   \
+        hipFuncSetAttribute((const void*)gemv5_kernel<FMT, G, MT, CPW, 4, true>,                  \
                             hipFuncAttributeMaxDynamicSharedMemorySize, kXBudgetUnsplit + 1024) == \
         hipSuccess;                                                                               \
     (void)attr_set;                                                                               \
-    hipLaunchKernelGGL((gemv5_kernel<FMT, G, 2, CPW, 4, true>), grid, block, lds, st, b, sp);     \
+    hipLaunchKernelGGL((gemv5_kernel<FMT, G, MT, CPW, 4, true>), grid, block, lds, st, b, sp);    \
   } while (0)
   if constexpr (F::CK == 128) {
     if (stream) {
-      if (cpw == 2) RQ_L5S(2); else if (cpw == 4) RQ_L5S(4); else RQ_L5S(8);
+      if (mt == 2) {
+        if (cpw == 2) RQ_L5S(2, 2); else if (cpw == 4) RQ_L5S(2, 4); else RQ_L5S(2, 8);
+      } else {
+        if (cpw == 2) RQ_L5S(1, 2); else if (cpw == 4) RQ_L5S(1, 4); else RQ_L5S(1, 8);
+      }
       err = hipGetLastError();
       return true;
     }

@@ -446,3 +446,108 @@ def test_streamed_activation_chunks(fmt, group, n, k):
         y_ref, b = ref.weight_only_ref(x[:, :k], fmt, parts, group)
         ok, info = ref.compare(y, y_ref, b)
         assert ok, (m, info)
+
+
+@pytest.mark.parametrize("fmt,group,k", [(quant.W4_SYM, 64, 128 * 131), (quant.W4_SYM, 32, 128 * 131),
+                                         (quant.W8_SYM, 64, 64 * 133), (quant.W8_SYM, 16, 64 * 133),
+                                         (quant.F16, 0, 32 * 131), (quant.BF16, 0, 32 * 131)])
+@pytest.mark.parametrize("m", [1, 2])
+def test_sixteen_chunk_waves(fmt, group, k, m):
+    """With 128 or more row tiles and 128 or more chunks in the slice, M <= 2
+    gives waves of sixteen chunks that keep a window of eight code loads in
+    flight and issue the rest while they compute.  K is 131 or 133 chunks, so
+    the last wave of a tile holds 3 or 5 valid chunks and 13 or 11 past the
+    end (their codes read zero, their scales are dropped); n = 2085 ends in a
+    partial tile.  Codes and scales are seeded random bytes (inputs); the
+    oracle multiplies sampled rows."""
+    n = 2085
+    g = np.random.default_rng(k + m)
+    if fmt in (quant.W4_SYM, quant.W8_SYM):
+        nbytes = k // 2 if fmt == quant.W4_SYM else k
+        codes = g.integers(0, 256, (n, nbytes), dtype=np.uint8)
+        sbits = (g.integers(0, 1024, (n, k // group)) | (5 << 10)).astype(np.uint16)  # [2^-10, 2^-9)
+        full = {"codes": codes, "scales": sbits.view(np.float16)}
+        sample = lambda r: {"codes": codes[r], "scales": full["scales"][r]}  # noqa: E731
+    elif fmt == quant.F16:
+        codes = (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float16)
+        full = {"codes": codes}
+        sample = lambda r: {"codes": codes[r]}  # noqa: E731
+    else:
+        f = (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
+        codes = (f.view(np.uint32) >> 16).astype(np.uint16)   # bf16 patterns (truncated)
+        full = {"codes": codes}
+        sample = lambda r: {"codes": codes[r]}  # noqa: E731
+    qw = qweight_from_oracle(fmt, group, full, n, k)
+    ldx = k + 8
+    x = g.standard_normal((m, ldx)).astype(np.float16)
+    y = _run_small_m(qw, x, m, ldx, n)
+    rows = np.concatenate([np.sort(g.choice(n - 5, 24, replace=False)), np.arange(n - 5, n)])
+    y_ref, b = ref.weight_only_ref(x[:, :k], fmt, sample(rows), group)
+    ok, info = ref.compare(y[:, rows], y_ref, b)
+    assert ok, info
+
+
+def _random_parts(fmt, group, n, k, g):
+    """Seeded random packed buffers of a format (every byte pattern is a valid
+    code; fp16 scales in [2^-10, 2^-9))."""
+    def scales(cols):
+        return (g.integers(0, 1024, (n, cols)) | (5 << 10)).astype(np.uint16).view(np.float16)
+    if fmt == quant.W4_ASYM_SB256:
+        nsb = k // 256
+        return {"qs": g.integers(0, 256, (n, k // 2), dtype=np.uint8), "d": scales(nsb), "dmin": scales(nsb),
+                "sub": g.integers(0, 256, (n, nsb, 12), dtype=np.uint8)}
+    parts = {"codes": g.integers(0, 256, (n, k // 2), dtype=np.uint8), "scales": scales(k // group)}
+    if fmt == quant.W6_SYM:
+        parts["hi"] = g.integers(0, 1 << 16, (n, k // 8)).astype(np.uint16)
+    elif fmt == quant.W5_SYM:
+        parts["hi"] = g.integers(0, 256, (n, k // 8), dtype=np.uint8)
+    return parts
+
+
+def _rows(parts, rows):
+    return {name: arr[rows] for name, arr in parts.items()}
+
+
+@pytest.mark.parametrize("fmt,group,k", [(quant.W4_SYM, 64, 16000), (quant.W4_SYM, 32, 16384),
+                                         (quant.W4_ASYM_SB256, 32, 16128), (quant.W6_SYM, 32, 16000),
+                                         (quant.W5_SYM, 64, 16384)])
+def test_streamed_one_tile(fmt, group, k):
+    """M = 4..8 with an activation slice too large for one workgroup's LDS
+    and 192..256 row tiles: each wave streams its chunks (16 rows, rows >= M
+    read zeros) through a private double buffer.  K = 16000 and 16128 leave
+    the last wave with 5 or 6 of its 8 chunks; n = 3100 ends in a partial
+    tile.  Codes are seeded random bytes; the oracle multiplies sampled
+    rows."""
+    n = 3100
+    g = np.random.default_rng(k + group)
+    parts = _random_parts(fmt, group, n, k, g)
+    qw = qweight_from_oracle(fmt, group, parts, n, k)
+    rows = np.concatenate([np.sort(g.choice(n - 4, 28, replace=False)), np.arange(n - 4, n)])
+    for m in (4, 7, 8):
+        ldx = k + 8 * m
+        x = g.standard_normal((m, ldx)).astype(np.float16)
+        y = _run_small_m(qw, x, m, ldx, n)
+        y_ref, b = ref.weight_only_ref(x[:, :k], fmt, _rows(parts, rows), group)
+        ok, info = ref.compare(y[:, rows], y_ref, b)
+        assert ok, (m, info)
+
+
+@pytest.mark.parametrize("n,k", [(9, 64 * 13), (33, 64 * 5), (300, 64 * 129), (2085, 64 * 133)])
+@pytest.mark.parametrize("m", [1, 2, 5, 17])
+def test_int8_g64_odd_groups_per_row(n, k, m):
+    """int8 with group 64 is the one format whose rows can hold an odd number
+    of fp16 scales, so a row's scales end in the middle of a dword; the last
+    row's last scale shares its dword with the bytes after the buffer (this
+    once lost that scale to the buffer range check)."""
+    w = _weights(n, k, seed=n + k)
+    parts = quant.quantize(w, quant.W8_SYM, 64)
+    qw = qweight_from_oracle(quant.W8_SYM, 64, parts, n, k)
+    g = np.random.default_rng(n * 7 + m)
+    x = g.standard_normal((m, k)).astype(np.float16)
+    y = _run_small_m(qw, x, m, k, n)
+    y_ref, b = ref.weight_only_ref(x, quant.W8_SYM, parts, 64)
+    ok, info = ref.compare(y, y_ref, b)
+    assert ok, info
+    # the last row's error is fp16 output rounding only; one dropped chunk of
+    # 64 k would move it by about |y| / sqrt(chunks)
+    assert np.all(np.abs(y[:, -1] - y_ref[:, -1]) <= 4e-3 * np.abs(y_ref[:, -1]) + 2e-3)
