@@ -1123,7 +1123,10 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     // wave's chunk pairs are whole superblocks.
     constexpr int cmult = ((F::GPC == 1 && F::SYMS) || FMT == GF_SB) ? 2 : 1;
     const int cps = ((nchunks + split - 1) / split + cmult - 1) / cmult * cmult;
-    if ((split - 1) * cps >= nchunks) continue;  // an empty slice
+    // slices of cps chunks that are not empty (fewer than split where the
+    // rounding of cps leaves the last ones with nothing: 41 chunks in 8
+    // slices of 6 make 7)
+    const int used = (nchunks + cps - 1) / cps;
     const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
     if (xb > (size_t)kXBudget) continue;
     // from M = 3 on, a split slice does better with more waves of fewer chunks
@@ -1136,9 +1139,9 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
       for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
       return g;
     };
-    while (share_x && rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) * split >= 256) rt *= 2;
-    if (split > 1 && (size_t)groups(rt) * rt * split * mt * 1024 > kGemvWsPartialBytes) break;
-    sp.split = split;
+    while (share_x && rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) * used >= 256) rt *= 2;
+    if (used > 1 && (size_t)groups(rt) * rt * used * mt * 1024 > kGemvWsPartialBytes) break;
+    sp.split = used;
     sp.cps = cps;
     sp.wpt = wpt;
     sp.rt = rt;
@@ -1147,7 +1150,7 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     found = true;
     // a split costs a second launch: worth it only to occupy more than half
     // of the compute units, or to fit the activations
-    if (groups(rt) * split >= (split == 1 ? 128 : 256)) break;
+    if (groups(rt) * used >= (used == 1 ? 128 : 256)) break;
   }
   return found;
 }

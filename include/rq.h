@@ -222,9 +222,16 @@ int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *strea
  * y: fp16 [m][ldy], ldy >= n.  Accepts RQ_W8_SYM, RQ_W4_SYM,
  * RQ_W4_ASYM_SB256, RQ_F16, RQ_W6_SYM, RQ_W5_SYM and RQ_BF16.  The weights
  * are read once per call.
- * Errors: RQ_ERR_SHAPE for m outside 0..32, and for RQ_W6_SYM, RQ_W5_SYM and
- * RQ_BF16 when one weight buffer or the activation span m * ldx * 2 reaches
- * 2^31 bytes (the other formats take any size). */
+ * Errors: RQ_ERR_SHAPE for m outside 0..32.  RQ_W6_SYM, RQ_W5_SYM and
+ * RQ_BF16 have one kernel, whose activation slice must fit LDS; they also
+ * return RQ_ERR_SHAPE when one weight buffer or the activation span
+ * m * ldx * 2 reaches 2^31 bytes, or when (m + 1) * (ceil(k / 16 / C) * C + 8)
+ * exceeds 40960 with C = 128 (RQ_W6_SYM, RQ_W5_SYM) or 32 (RQ_BF16), i.e. K
+ * cut into 16 slices still leaves too large a slice (k above 18432 at
+ * m = 32, 36864 at m = 16).  Cutting K needs the stream's workspace (see
+ * Workspace); without one, (m + 1) * (k + 8) must stay within 40960, or
+ * 76800 for 128 or more row tiles (192 to 256 row tiles also stream k up to
+ * 8192 at m > 16 and 16384 at m = 4..8).  Other formats take any shape. */
 int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w,
                     uint16_t *y, int64_t ldy, void *stream);
 

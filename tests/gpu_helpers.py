@@ -84,3 +84,32 @@ def say(*args):
     """Print what names the case before a GPU step, flushed."""
     print("[case]", *args, flush=True)
     sys.stdout.flush()
+
+
+def random_parts(fmt, group, n, k, g):
+    """Seeded random packed buffers of a weight format, in the oracle's layout
+    (inputs for products; every byte pattern is a valid code).  Scales are
+    fp16 in [2^-10, 2^-9); fp16 / bf16 weights are N(0, 1/k)."""
+    def scales(cols):
+        return (g.integers(0, 1024, (n, cols)) | (5 << 10)).astype(np.uint16).view(np.float16)
+    if fmt == quant.W4_ASYM_SB256:
+        nsb = k // 256
+        return {"qs": g.integers(0, 256, (n, k // 2), dtype=np.uint8), "d": scales(nsb), "dmin": scales(nsb),
+                "sub": g.integers(0, 256, (n, nsb, 12), dtype=np.uint8)}
+    if fmt == quant.F16:
+        return {"codes": (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float16)}
+    if fmt == quant.BF16:
+        f = (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
+        return {"codes": (f.view(np.uint32) >> 16).astype(np.uint16)}   # truncated to bf16
+    nbytes = k if fmt == quant.W8_SYM else k // 2
+    parts = {"codes": g.integers(0, 256, (n, nbytes), dtype=np.uint8), "scales": scales(k // group)}
+    if fmt == quant.W6_SYM:
+        parts["hi"] = g.integers(0, 1 << 16, (n, k // 8)).astype(np.uint16)
+    elif fmt == quant.W5_SYM:
+        parts["hi"] = g.integers(0, 256, (n, k // 8), dtype=np.uint8)
+    return parts
+
+
+def rows_of(parts, rows):
+    """The same buffers restricted to the given weight rows."""
+    return {name: arr[rows] for name, arr in parts.items()}

@@ -13,7 +13,7 @@ import torch
 
 import gemm_rwkv_amd.rq as rq
 from gemm_rwkv_amd import synth
-from gpu_helpers import dev_f16, dev_f32, host, oracle_buffers, qweight_from_oracle, say
+from gpu_helpers import dev_f16, dev_f32, host, oracle_buffers, qweight_from_oracle, random_parts, say
 from oracle import aw, quant, ref
 
 pytestmark = pytest.mark.gpu
@@ -197,3 +197,29 @@ def test_56_product_on_gpu_quantized_weights_fullsize():
             y_ref, b = ref.weight_only_ref(x, fmt, parts, group)
             ok, info = ref.compare(y, y_ref, b)
             assert ok, (fmt, m, info)
+
+
+def test_56_bf16_shape_limit():
+    """The 6-/5-bit and bf16 products have one kernel: K may be cut into at
+    most 16 slices, whose activation slices must fit LDS.  At m = 32,
+    k = 18432 is the largest 6-bit K that fits; k = 25600 is refused with
+    RQ_ERR_SHAPE and leaves the output untouched."""
+    n, m = 64, 32
+    for k, fits in ((18432, True), (25600, False)):
+        g = np.random.default_rng(k)
+        parts = random_parts(quant.W6_SYM, 32, n, k, g)
+        qw = qweight_from_oracle(quant.W6_SYM, 32, parts, n, k)
+        x = g.standard_normal((m, k)).astype(np.float16)
+        say("w6 limit", k, fits)
+        if fits:
+            y = _run_small_m(qw, x, m, k, n)
+            y_ref, b = ref.weight_only_ref(x, quant.W6_SYM, parts, 32)
+            ok, info = ref.compare(y, y_ref, b)
+            assert ok, info
+        else:
+            y = torch.full((m * n,), 7, dtype=torch.int16, device="cuda")
+            with pytest.raises(rq.RqError) as e:
+                rq.rq_gemm_small_m(dev_f16(x), m, k, qw, y, n)
+            assert e.value.status == rq.RQ_ERR_SHAPE
+            torch.cuda.synchronize()
+            assert bool((y == 7).all())

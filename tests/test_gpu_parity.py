@@ -14,7 +14,7 @@ import torch
 import gemm_rwkv_amd.rq as rq
 from gemm_rwkv_amd import synth
 from gpu_helpers import (Guarded, dev_bytes, dev_f16, dev_f32, host, oracle_buffers,
-                         qweight_from_oracle, say)
+                         qweight_from_oracle, random_parts, rows_of, say)
 from oracle import codecs, quant, ref
 
 pytestmark = pytest.mark.gpu
@@ -462,50 +462,15 @@ def test_sixteen_chunk_waves(fmt, group, k, m):
     oracle multiplies sampled rows."""
     n = 2085
     g = np.random.default_rng(k + m)
-    if fmt in (quant.W4_SYM, quant.W8_SYM):
-        nbytes = k // 2 if fmt == quant.W4_SYM else k
-        codes = g.integers(0, 256, (n, nbytes), dtype=np.uint8)
-        sbits = (g.integers(0, 1024, (n, k // group)) | (5 << 10)).astype(np.uint16)  # [2^-10, 2^-9)
-        full = {"codes": codes, "scales": sbits.view(np.float16)}
-        sample = lambda r: {"codes": codes[r], "scales": full["scales"][r]}  # noqa: E731
-    elif fmt == quant.F16:
-        codes = (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float16)
-        full = {"codes": codes}
-        sample = lambda r: {"codes": codes[r]}  # noqa: E731
-    else:
-        f = (g.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)
-        codes = (f.view(np.uint32) >> 16).astype(np.uint16)   # bf16 patterns (truncated)
-        full = {"codes": codes}
-        sample = lambda r: {"codes": codes[r]}  # noqa: E731
+    full = random_parts(fmt, group, n, k, g)
     qw = qweight_from_oracle(fmt, group, full, n, k)
     ldx = k + 8
     x = g.standard_normal((m, ldx)).astype(np.float16)
     y = _run_small_m(qw, x, m, ldx, n)
     rows = np.concatenate([np.sort(g.choice(n - 5, 24, replace=False)), np.arange(n - 5, n)])
-    y_ref, b = ref.weight_only_ref(x[:, :k], fmt, sample(rows), group)
+    y_ref, b = ref.weight_only_ref(x[:, :k], fmt, rows_of(full, rows), group)
     ok, info = ref.compare(y[:, rows], y_ref, b)
     assert ok, info
-
-
-def _random_parts(fmt, group, n, k, g):
-    """Seeded random packed buffers of a format (every byte pattern is a valid
-    code; fp16 scales in [2^-10, 2^-9))."""
-    def scales(cols):
-        return (g.integers(0, 1024, (n, cols)) | (5 << 10)).astype(np.uint16).view(np.float16)
-    if fmt == quant.W4_ASYM_SB256:
-        nsb = k // 256
-        return {"qs": g.integers(0, 256, (n, k // 2), dtype=np.uint8), "d": scales(nsb), "dmin": scales(nsb),
-                "sub": g.integers(0, 256, (n, nsb, 12), dtype=np.uint8)}
-    parts = {"codes": g.integers(0, 256, (n, k // 2), dtype=np.uint8), "scales": scales(k // group)}
-    if fmt == quant.W6_SYM:
-        parts["hi"] = g.integers(0, 1 << 16, (n, k // 8)).astype(np.uint16)
-    elif fmt == quant.W5_SYM:
-        parts["hi"] = g.integers(0, 256, (n, k // 8), dtype=np.uint8)
-    return parts
-
-
-def _rows(parts, rows):
-    return {name: arr[rows] for name, arr in parts.items()}
 
 
 @pytest.mark.parametrize("fmt,group,k", [(quant.W4_SYM, 64, 16000), (quant.W4_SYM, 32, 16384),
@@ -520,14 +485,14 @@ def test_streamed_one_tile(fmt, group, k):
     rows."""
     n = 3100
     g = np.random.default_rng(k + group)
-    parts = _random_parts(fmt, group, n, k, g)
+    parts = random_parts(fmt, group, n, k, g)
     qw = qweight_from_oracle(fmt, group, parts, n, k)
     rows = np.concatenate([np.sort(g.choice(n - 4, 28, replace=False)), np.arange(n - 4, n)])
     for m in (4, 7, 8):
         ldx = k + 8 * m
         x = g.standard_normal((m, ldx)).astype(np.float16)
         y = _run_small_m(qw, x, m, ldx, n)
-        y_ref, b = ref.weight_only_ref(x[:, :k], fmt, _rows(parts, rows), group)
+        y_ref, b = ref.weight_only_ref(x[:, :k], fmt, rows_of(parts, rows), group)
         ok, info = ref.compare(y[:, rows], y_ref, b)
         assert ok, (m, info)
 
