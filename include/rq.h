@@ -225,10 +225,11 @@ int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *strea
  * Errors: RQ_ERR_SHAPE for m outside 0..32.  RQ_W6_SYM, RQ_W5_SYM and
  * RQ_BF16 have one kernel, whose activation slice must fit LDS; they also
  * return RQ_ERR_SHAPE when one weight buffer or the activation span
- * m * ldx * 2 reaches 2^31 bytes, or when (m + 1) * (ceil(k / 16 / C) * C + 8)
- * exceeds 40960 with C = 128 (RQ_W6_SYM, RQ_W5_SYM) or 32 (RQ_BF16), i.e. K
- * cut into 16 slices still leaves too large a slice (k above 18432 at
- * m = 32, 36864 at m = 16).  Cutting K needs the stream's workspace (see
+ * m * ldx * 2 reaches 2^31 bytes, or when K cut into 16 slices still leaves
+ * a slice too large: with chunks of C = 128 k (RQ_W6_SYM, RQ_W5_SYM) or 32 k
+ * (RQ_BF16) and c = ceil(k / 16 / C) chunks per slice, (m + 1) * (c * C + 8)
+ * above 40960 (k above 18432 at m = 32, 36864 at m = 16) or c above 128
+ * (256 for RQ_BF16 at m <= 2).  Cutting K needs the stream's workspace (see
  * Workspace); without one, (m + 1) * (k + 8) must stay within 40960, or
  * 76800 for 128 or more row tiles (192 to 256 row tiles also stream k up to
  * 8192 at m > 16 and 16384 at m = 4..8).  Other formats take any shape. */
