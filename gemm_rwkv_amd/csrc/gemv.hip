@@ -1136,8 +1136,10 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     const int used = (nchunks + cps - 1) / cps;
     const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
     if (xb > (size_t)kXBudget) continue;
-    // from M = 3 on, a split slice does better with more waves of fewer chunks
-    const int cpw = b.m <= 2 ? pick_cpw(cps, FMT != GF_SB && F::HW == 0, b.m) : (cps <= 64 ? 4 : 8);
+    // from M = 3 on: waves of four chunks for slices of up to 24, of eight
+    // above (4096-wide matrices, 32 chunks, at M = 3..8: 3-19% faster than
+    // four)
+    const int cpw = b.m <= 2 ? pick_cpw(cps, FMT != GF_SB && F::HW == 0, b.m) : (cps <= 24 ? 4 : 8);
     const int wpt = (cps + cpw - 1) / cpw;
     if (wpt > 16) continue;
     int rt = 1;
@@ -1146,7 +1148,24 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
       for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
       return g;
     };
-    while (share_x && rt < 4 && 2 * rt * wpt <= 16 && groups(2 * rt) * used >= 256) rt *= 2;
+    // row tiles share a workgroup while the workgroups would not all be
+    // resident at once (each CU holds as many as its 160 KB of LDS and its
+    // waves allow), or while the activation slice outweighs four times the
+    // group's codes and at least 256 workgroups remain.  Measured: fused
+    // R/K/V 3x4096^2 at M = 4 8.7 us with one tile per workgroup (768, three
+    // per CU) against 10.3 with two; cmix value 2048x8192 at M = 32 (K in
+    // 8 slices) 10.0 us with four tiles against 10.7 with two.
+    auto one_round = [&](int r) {
+      const size_t red = (size_t)r * wpt * mt * 1024;
+      const size_t lds = xb > red ? xb : red;
+      const int by_lds = (int)((size_t)(160 * 1024) / lds);
+      const int by_waves = (mt == 1 ? 32 : 24) / (r * wpt);
+      return (size_t)groups(r) * used <= (size_t)256 * (by_lds < by_waves ? by_lds : by_waves);
+    };
+    auto x_heavy = [&](int r) { return xb > (size_t)4 * r * 16 * 64 * cps; };
+    while (share_x && rt < 4 && 2 * rt * wpt <= 16 &&
+           (!one_round(rt) || (x_heavy(rt) && groups(2 * rt) * used >= 256)))
+      rt *= 2;
     if (used > 1 && (size_t)groups(rt) * rt * used * mt * 1024 > kGemvWsPartialBytes) break;
     sp.split = used;
     sp.cps = cps;
