@@ -1112,13 +1112,19 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
       // tiles while at least 128 workgroups remain (fused R/K/V 3 x 4096^2
       // at M = 9, 12, 16: 13.2, 13.7, 14.1 -> 11.9, 12.1, 12.4 us)
       while (rt < 4 && 2 * rt * wpt <= 16 && groups(rt) > 256 && groups(2 * rt) >= 128) rt *= 2;
-      sp.split = 1;
-      sp.cps = nchunks;
-      sp.wpt = wpt;
-      sp.rt = rt;
-      for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
-      cpw_out = cpw;
-      return true;
+      // still more than 256 makes two rounds of one workgroup per CU: a K
+      // split with small slices does better (10240x2560 at M = 16, 5-/6-bit
+      // codes and SB256: 15.1-16.8 -> 14.4-15.6 us), where the stream has
+      // the workspace for it
+      if (groups(rt) <= 256 || !b.ws) {
+        sp.split = 1;
+        sp.cps = nchunks;
+        sp.wpt = wpt;
+        sp.rt = rt;
+        for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
+        cpw_out = cpw;
+        return true;
+      }
     }
   }
   for (int split = 1; split <= 16; split *= 2) {
