@@ -72,3 +72,14 @@ def test_plans_194_tiles(fmt, group, k, m):
     # large for LDS (two tiles from M = 17, one tile from M = 4 at the
     # larger K)
     _check(fmt, group, 3100, 2 * k if k < 8192 else k, m)
+
+
+@pytest.mark.parametrize("fmt,group", [(quant.W5_SYM, 32), (quant.W6_SYM, 32), (quant.W4_ASYM_SB256, 32),
+                                       (quant.W8_SYM, 16)])
+@pytest.mark.parametrize("n,k,m", [(10240, 2560, 9), (10240, 2560, 16), (2560, 10240, 1), (2560, 10240, 4),
+                                   (2560, 10240, 16), (7680, 2560, 16)])
+def test_plans_2p9b_shapes(fmt, group, n, k, m):
+    # the 2.9B-width channel-mix shapes and three stacked projections: at
+    # M = 9..16 the key's 640 row tiles would need two rounds of one
+    # workgroup per CU unsplit, so K is split
+    _check(fmt, group, n, k, m)
