@@ -1169,7 +1169,11 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     // from M = 3 on: waves of four chunks for slices of up to 24, of eight
     // above (4096-wide matrices, 32 chunks, at M = 3..8: 3-19% faster than
     // four)
-    const int cpw = b.m <= 2 ? pick_cpw(cps, FMT != GF_SB && F::HW == 0, b.m) : (cps <= 24 ? 4 : 8);
+    // int8 group 16 (sixteen 16-k MFMAs per chunk) keeps waves of four chunks
+    // up to 48 (width 2560 at M = 1 and 4: 6-7% faster than eight)
+    constexpr int kCpw4Max = (FMT == GF_W8 && G == 16) ? 48 : 24;
+    const int cpw = (FMT == GF_W8 && G == 16 && cps <= kCpw4Max) ? 4
+                    : b.m <= 2 ? pick_cpw(cps, FMT != GF_SB && F::HW == 0, b.m) : (cps <= kCpw4Max ? 4 : 8);
     const int wpt = (cps + cpw - 1) / cpw;
     if (wpt > 16) continue;
     int rt = 1;
