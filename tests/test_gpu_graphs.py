@@ -152,3 +152,47 @@ def test_graph_gemm_w4_and_fused_rkv():
         torch.cuda.synchronize()
         for t, e in zip([y] + ys, eager):
             assert torch.equal(t, e), rep
+
+
+def test_graph_replays_planner_shapes():
+    """Launch shapes added to the planner, captured and replayed: a long K
+    cut four ways for SB256 on 160 row tiles (M = 1), one-tile streamed
+    activations (4-bit codes, 194 row tiles, M = 6) and a split whose last
+    slices are empty (6-bit, 41 chunks, M = 32)."""
+    from gpu_helpers import random_parts
+    cases = [(quant.W4_ASYM_SB256, 32, 2560, 10240, 1), (quant.W4_SYM, 32, 3100, 16384, 6),
+             (quant.W6_SYM, 32, 2085, 5248, 32)]
+    items = []
+    for i, (fmt, group, n, k, m) in enumerate(cases):
+        g = np.random.default_rng(300 + i)
+        parts = random_parts(fmt, group, n, k, g)
+        x = _x(m, k, 400 + i)
+        items.append({"fmt": fmt, "group": group, "n": n, "k": k, "m": m, "parts": parts, "x": x,
+                      "qw": qweight_from_oracle(fmt, group, parts, n, k), "xd": dev_f16(x),
+                      "y": torch.zeros(m * n, dtype=torch.int16, device="cuda")})
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        _run(items)
+    torch.cuda.synchronize()
+    eager = [it["y"].clone() for it in items]
+    g = torch.cuda.CUDAGraph()
+    say("graph: capture planner shapes")
+    with torch.cuda.graph(g, stream=s):
+        _run(items)
+    for rep in range(3):
+        _run(items)                      # eager, default stream
+        torch.cuda.synchronize()
+        for it in items:
+            it["y"].fill_(-1)
+        torch.cuda.synchronize()
+        say("graph: replay planner shapes", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for it, e in zip(items, eager):
+            assert torch.equal(it["y"], e), (rep, it["fmt"], it["n"], it["k"], it["m"])
+    rows = np.arange(0, 2560, 97)
+    it = items[0]
+    y_ref, b = ref.weight_only_ref(it["x"], it["fmt"], {nm: a[rows] for nm, a in it["parts"].items()}, 32)
+    ok, info = ref.compare(host(eager[0], np.float16, (1, 2560))[:, rows].astype(np.float64), y_ref, b)
+    assert ok, info
