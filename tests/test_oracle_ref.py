@@ -96,6 +96,56 @@ def test_w8a8_integer_closed_form():
     assert y.tolist() == (x.astype(np.int64) @ w.astype(np.int64).T).tolist()
 
 
+def check_w8a8_int8_closed_form(as_bytes):
+    """int8 W8A8: rows whose absmax is 127 * 2**e get the exact scale 2**e
+    (Toolkit page, Key Design: int8 x int8 products with one scale per token
+    and per output channel), so y = s_x[m] * s_w[n] * (integer dot product)
+    exactly.  Codes are passed as signed int8 or as the raw bytes a device
+    buffer holds; -127 and 127 sit in every row."""
+    g = np.random.default_rng(11)
+    xi = g.integers(-127, 128, (4, 96))
+    wi = g.integers(-127, 128, (6, 96))
+    xi[:, 0], xi[:, 1] = 127, -127
+    wi[:, 0], wi[:, 1] = -127, 127
+    ex = g.integers(-6, 7, 4)
+    ew = g.integers(-6, 7, 6)
+    x = (xi * np.exp2(ex)[:, None]).astype(np.float32)
+    w = (wi * np.exp2(ew)[:, None]).astype(np.float32)
+    xq = quant.quantize_rows(x, "int8")
+    wq = quant.quantize(w, quant.I8_CH)
+    assert np.array_equal(xq["codes"].astype(np.int64), xi)
+    assert np.array_equal(wq["codes"].astype(np.int64), wi)
+    assert np.array_equal(xq["scales"], np.exp2(ex).astype(np.float32))
+    codes = xq["codes"].view(np.uint8) if as_bytes else xq["codes"]
+    if as_bytes:
+        wq = dict(wq, codes=wq["codes"].view(np.uint8))
+    y, b = ref.w8a8_ref(codes, xq["scales"], "int8", quant.I8_CH, wq)
+    want = [[float(sum(int(xi[m, k]) * int(wi[n, k]) for k in range(96))) * 2.0 ** (int(ex[m]) + int(ew[n]))
+             for n in range(6)] for m in range(4)]
+    assert y.tolist() == want
+    bw = [[float(sum(abs(int(xi[m, k]) * int(wi[n, k])) for k in range(96))) * 2.0 ** (int(ex[m]) + int(ew[n]))
+           for n in range(6)] for m in range(4)]
+    assert b.tolist() == bw
+
+
+@pytest.mark.parametrize("as_bytes", [False, True])
+def test_w8a8_int8_closed_form(as_bytes):
+    check_w8a8_int8_closed_form(as_bytes)
+
+
+def test_mutation_int8_codes_read_unsigned(monkeypatch):
+    """Reading the int8 activation codes as unsigned bytes (a plausible slip
+    in dequant_rows) must fail the closed form above."""
+    def unsigned(codes, scales, kind):
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)[:, None]
+        if kind == "fp8":
+            return codecs.e4m3_decode(codes) * s
+        return np.asarray(codes).view(np.uint8).astype(np.float64) * s
+    monkeypatch.setattr(quant, "dequant_rows", unsigned)
+    with pytest.raises(AssertionError):
+        check_w8a8_int8_closed_form(True)
+
+
 def test_int_acc_ref():
     g = np.random.default_rng(8)
     a = g.integers(-127, 128, (3, 40)).astype(np.int8)
