@@ -1,8 +1,6 @@
 // The librq C ABI (include/rq.h): validate, pick the kernel for the format
 // and batch size, launch on the caller's stream.
 #include <hip/hip_runtime.h>
-#include <stdio.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -377,71 +375,6 @@ int rq_gemm_int8(const int8_t* xq, const float* sx, int64_t m, const rq_qweight*
 int rq_gemm_int8_acc(const int8_t* xq, int64_t m, const rq_qweight* w, int32_t* acc, void* stream) {
   if (!acc || !w) return RQ_ERR_NULL;
   return w8a8(xq, nullptr, m, w, nullptr, w->n, acc, stream, RQ_I8_CH);
-}
-
-int rq_chain_create(const rq_chain_op* ops, int32_t nops, int64_t m, void** plan) {
-  if (!ops || !plan) return RQ_ERR_NULL;
-  *plan = nullptr;
-  if (nops < 1 || m != 1) return RQ_ERR_SHAPE;
-  std::vector<rq::ChainOpIn> in(nops);
-  std::vector<Span> wsp(4 * (size_t)nops), xs, ysp(nops);
-  int st;
-  for (int q = 0; q < nops; ++q) {
-    const rq_chain_op& o = ops[q];
-    if ((st = rqv::check_weight(&o.w)) != RQ_OK) return st;
-    const bool w4 = o.w.format == RQ_W4_SYM && o.w.group == 64;
-    if (!w4 && o.w.format != RQ_F16) return RQ_ERR_FORMAT;
-    if (o.w.k % (w4 ? 128 : 32) != 0 || o.w.n % 16 != 0 || o.w.n < 16) return RQ_ERR_SHAPE;
-    if (o.src < -1 || o.src >= q) return RQ_ERR_SHAPE;
-    if (o.src >= 0 && ops[o.src].w.n != o.w.k) return RQ_ERR_SHAPE;
-    if (o.src < 0) {
-      if ((st = rqv::check_act(o.x, 1, o.w.k, o.w.k + (8 - o.w.k % 8) % 8)) != RQ_OK) return st;
-      xs.push_back(rqv::act_span(o.x, 1, o.w.k, o.w.k, 2));
-    }
-    if ((st = rqv::check_out(o.y, 1, o.w.n, o.w.n + (8 - o.w.n % 8) % 8)) != RQ_OK) return st;
-    rqv::weight_spans(&o.w, &wsp[4 * (size_t)q]);
-    ysp[q] = rqv::act_span(o.y, 1, o.w.n, o.w.n, 2);
-    in[q] = rq::ChainOpIn{w4 ? rq::kChainW4G64 : rq::kChainF16, (int)o.w.n, (int)o.w.k, o.w.codes,
-                          (const uint16_t*)o.w.scales, o.src, o.x, o.y};
-  }
-  for (int q = 0; q < nops; ++q) {
-    if ((st = check_alias_out(ysp[q], wsp.data(), (int)wsp.size())) != RQ_OK) return st;
-    if (!xs.empty() && (st = check_alias_out(ysp[q], xs.data(), (int)xs.size())) != RQ_OK) return st;
-    for (int p = q + 1; p < nops; ++p)
-      if (rqv::overlaps(ysp[q], ysp[p])) return RQ_ERR_ALIAS;
-  }
-  return rq::chain_create(in.data(), nops, plan);
-}
-
-int rq_chain_run(void* plan, void* stream) {
-  if (!plan) return RQ_ERR_NULL;
-  return hip_status(rq::chain_run(plan, S(stream)));
-}
-
-int rq_chain_check(void* plan) {
-  if (!plan) return RQ_ERR_NULL;
-  uint32_t err[3] = {0, 0, 0};
-  const int st = rq::chain_error(plan, err);
-  if (st != 0) return st;
-  if (err[0] && getenv("RQ_CHAIN_DEBUG"))
-    fprintf(stderr, "rq_chain: wait expired: op %u producers %u..%u, epoch %u\n", (err[1] >> 16) - 1,
-            (err[1] >> 8) & 0xffu, err[1] & 0xffu, err[2]);
-  return err[0] ? RQ_ERR_HIP : RQ_OK;
-}
-
-int rq_chain_grid(void* plan, int32_t op, int32_t* row_blocks, int32_t* k_slices) {
-  if (!plan || !row_blocks || !k_slices) return RQ_ERR_NULL;
-  int R = 0, Sg = 0;
-  const int st = rq::chain_grid(plan, op, &R, &Sg);
-  *row_blocks = R;
-  *k_slices = Sg;
-  return st;
-}
-
-int rq_chain_destroy(void* plan) {
-  if (!plan) return RQ_ERR_NULL;
-  rq::chain_destroy(plan);
-  return RQ_OK;
 }
 
 int rq_host_convert(int kind, const double* in, void* out, int64_t count) {

@@ -74,28 +74,4 @@ hipError_t launch_gemm_w8a8(const void* xq, const float* sx, int m, const void* 
                             int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out, void* ws,
                             size_t ws_bytes, hipStream_t st);
 
-// ---- decode chain, M = 1 (chain.hip) ----------------------------------------
-constexpr int kChainWorkgroups = 256;
-enum { kChainW4G64 = 0, kChainF16 = 1 };
-struct ChainOpIn {
-  int fmt;                 // kChainW4G64 or kChainF16
-  int n, k;
-  const void* codes;       // int4 g64 code words [n][k/2] or fp16 [n][k]
-  const uint16_t* scales;  // fp16 [n][k/64] (int4)
-  int src;                 // earlier product whose output is the input; -1: x
-  const uint16_t* x;       // input [k] when src < 0
-  uint16_t* y;             // output [n]
-};
-// Plans the chain and allocates its device memory (partials, flags,
-// descriptors).  Returns 0 or an rq_status value.
-int chain_create(const ChainOpIn* ops, int nops, void** plan);
-// One pass over the chain: two launches on st, no allocation.
-hipError_t chain_run(void* plan, hipStream_t st);
-// Synchronizes the device and reads the plan's error words: err[0] non-zero
-// when a wait expired in some launch, err[1] the first expiry ((op + 1) << 16
-// | first producer << 8 | last producer), err[2] the next launch's epoch.
-int chain_error(void* plan, uint32_t err[3]);
-int chain_grid(void* plan, int q, int* R, int* S);
-void chain_destroy(void* plan);
-
 }  // namespace rq

@@ -39,8 +39,7 @@ EXPORTS = (
     "rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16", "rq_gemv_w8g32",
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
-    "rq_gemm_w4", "rq_quantize_aw", "rq_chain_create", "rq_chain_run", "rq_chain_check",
-    "rq_chain_grid", "rq_chain_destroy",
+    "rq_gemm_w4", "rq_quantize_aw",
 )
 
 
@@ -54,11 +53,6 @@ class _QW(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("group", ctypes.c_int32), ("n", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("mins", ctypes.c_void_p), ("sub", ctypes.c_void_p)]
-
-
-class _ChainOp(ctypes.Structure):
-    _fields_ = [("w", _QW), ("src", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 _lib = None
@@ -87,11 +81,6 @@ def lib():
             "rq_gemm_int8": ([vp, vp, i64, qp, vp, i64, vp], i32),
             "rq_gemm_int8_acc": ([vp, i64, qp, vp, vp], i32),
             "rq_host_convert": ([i32, vp, vp, i64], i32),
-            "rq_chain_create": ([ctypes.POINTER(_ChainOp), i32, i64, ctypes.POINTER(vp)], i32),
-            "rq_chain_run": ([vp, vp], i32),
-            "rq_chain_check": ([vp], i32),
-            "rq_chain_grid": ([vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)], i32),
-            "rq_chain_destroy": ([vp], i32),
         }
         for name in ("rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16",
                      "rq_gemv_w8g32", "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16"):
@@ -287,46 +276,6 @@ def rq_gemm_int8_acc(xq, m, w, acc, stream=None):
     st = lib().rq_gemm_int8_acc(_ptr(xq), m, ctypes.byref(d), _ptr(acc), _stream(stream))
     _check(st, "rq_gemm_int8_acc")
     return acc
-
-
-class Chain:
-    """A planned decode chain (rq_chain_create): ops is a list of
-    (QWeight, src, x, y) with src the index of an earlier op whose output is
-    this op's input, or -1 for the fp16 device vector x; y is the fp16 output.
-    The plan keeps the tensors' pointers, so this object keeps the tensors."""
-
-    def __init__(self, ops, m=1):
-        self._keep = list(ops)
-        arr = (_ChainOp * len(ops))()
-        for i, (w, src, x, y) in enumerate(ops):
-            arr[i] = _ChainOp(w.desc(), int(src), 0, _ptr(x), _ptr(y))
-        h = ctypes.c_void_p()
-        st = lib().rq_chain_create(arr, len(ops), m, ctypes.byref(h))
-        _check(st, "rq_chain_create")
-        self.handle = h.value
-
-    def run(self, stream=None):
-        st = lib().rq_chain_run(self.handle, _stream(stream))
-        _check(st, "rq_chain_run")
-
-    def check(self):
-        _check(lib().rq_chain_check(self.handle), "rq_chain_check")
-
-    def grid(self, q):
-        r, s = ctypes.c_int32(), ctypes.c_int32()
-        _check(lib().rq_chain_grid(self.handle, q, ctypes.byref(r), ctypes.byref(s)), "rq_chain_grid")
-        return r.value, s.value
-
-    def destroy(self):
-        if self.handle:
-            lib().rq_chain_destroy(self.handle)
-            self.handle = None
-
-    def __del__(self):
-        try:
-            self.destroy()
-        except Exception:
-            pass
 
 
 def rq_host_convert(kind, values):

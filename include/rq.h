@@ -286,52 +286,6 @@ int rq_gemm_int8(const int8_t *xq, const float *sx, int64_t m, const rq_qweight 
  * for bit-exact checking of the integer contraction. */
 int rq_gemm_int8_acc(const int8_t *xq, int64_t m, const rq_qweight *w, int32_t *acc, void *stream);
 
-/* Decode chain (M = 1): a sequence of dependent products run by one
- * persistent launch.  A decode step of RWKV-7 is such a chain -- R/K/V, the
- * output projection, channel-mix key and value, layer after layer, then the
- * head -- each product reading an earlier product's output (model card,
- * summary: int4 GEMV family for decode).  Op q computes
- * y_q = x_q * W_hat_q^T (fp32 accumulation, fp16 output) where x_q is the
- * output y_src of op src (< q) or, for src = -1, the caller's fp16 vector x.
- * Weights: RQ_W4_SYM group 64 (k % 128 == 0) or RQ_F16 (k % 32 == 0);
- * n % 16 == 0; a product's k must equal its source's n.  Each product is cut
- * into row blocks and K slices; a slice's partial sum is rounded to fp16 and
- * the consumer adds the partials of its input slice in a fixed order (fp32),
- * so every output is within the tolerance of the exact product and the same
- * inputs give bit-identical outputs.
- *
- * rq_chain_create validates the ops (RQ_ERR_NULL, RQ_ERR_FORMAT,
- * RQ_ERR_SHAPE for shapes the planner cannot cut, RQ_ERR_ALIGN,
- * RQ_ERR_ALIAS when an output overlaps a weight, an input or another
- * output), allocates the plan's device memory (descriptors, fp16 partials,
- * flags) and returns an opaque handle in *plan; it synchronizes the device.
- * The plan keeps the caller's pointers: weights, x and y must stay valid
- * until rq_chain_destroy.  m must be 1.
- * rq_chain_run enqueues one pass over the chain on `stream` (two kernel
- * launches, no allocation; capturable in a graph).  Its launch uses one
- * workgroup on every compute unit, all resident at once: run nothing else on
- * the device that could hold compute units until it ends.  Runs of one plan
- * must not overlap.  Every cross-workgroup wait is bounded; if one expires the
- * launch still ends, its outputs are unspecified and rq_chain_check reports
- * it.
- * rq_chain_check synchronizes the device and returns RQ_OK, or RQ_ERR_HIP if
- * any run of the plan had a wait expire.
- * rq_chain_grid (test aid) gives the row blocks and K slices chosen for op q.
- * rq_chain_destroy synchronizes the device and frees the plan. */
-typedef struct rq_chain_op {
-  rq_qweight w;
-  int32_t src;
-  int32_t reserved;
-  const uint16_t *x;
-  uint16_t *y;
-} rq_chain_op;
-
-int rq_chain_create(const rq_chain_op *ops, int32_t nops, int64_t m, void **plan);
-int rq_chain_run(void *plan, void *stream);
-int rq_chain_check(void *plan);
-int rq_chain_grid(void *plan, int32_t op, int32_t *row_blocks, int32_t *k_slices);
-int rq_chain_destroy(void *plan);
-
 /* Test aid: the library's own fp64 -> fp16 (kind 0, uint16 out), fp64 ->
  * fp32 (kind 1, uint32 out) and fp64 -> e4m3fn (kind 2, uint8 out)
  * round-to-nearest-even conversions, run on the host over `count` values of

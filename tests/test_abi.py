@@ -274,42 +274,3 @@ def test_two_plane_and_bf16_validation():
     assert _status(rq.rq_gemm_small_m, x, 4, 48, _w(rq.RQ_BF16, 0, 32, 48, A), y, 32) == rq.RQ_ERR_SHAPE
     assert _status(rq.rq_gemm_w4, x, 4, 256, w6, y, 32) == rq.RQ_ERR_FORMAT
     rq.rq_gemm_small_m(x, 0, 256, w6, y, 32)   # m == 0: no-op
-
-
-def _chain(ops, m=1):
-    arr = (rq._ChainOp * len(ops))()
-    for i, (w, src, x, y) in enumerate(ops):
-        arr[i] = rq._ChainOp(w.desc(), src, 0, x or 0, y or 0)
-    h = rq.ctypes.c_void_p()
-    return rq.lib().rq_chain_create(arr, len(ops), m, rq.ctypes.byref(h))
-
-
-def test_chain_validation():
-    """rq_chain_create rejects bad chains before any device call."""
-    D = 0x7f0030000000
-    E = 0x7f0040000000
-    w = _w(n=32, k=128)
-    assert rq.lib().rq_chain_create(None, 1, 1, None) == rq.RQ_ERR_NULL
-    assert _chain([(w, -1, C, D)], m=2) == rq.RQ_ERR_SHAPE             # M = 1 only
-    assert _chain([(w, -1, C, D)], m=0) == rq.RQ_ERR_SHAPE
-    assert _chain([(w, 0, C, D)]) == rq.RQ_ERR_SHAPE                   # src must be earlier
-    assert _chain([(w, -2, C, D)]) == rq.RQ_ERR_SHAPE
-    assert _chain([(w, -1, 0, D)]) == rq.RQ_ERR_NULL                   # no external x
-    assert _chain([(w, -1, C, 0)]) == rq.RQ_ERR_NULL                   # no output
-    assert _chain([(w, -1, C + 8, D)]) == rq.RQ_ERR_ALIGN
-    assert _chain([(_w(group=32, n=32, k=128), -1, C, D)]) == rq.RQ_ERR_FORMAT   # int4 group 64 only
-    assert _chain([(_w(fmt=rq.RQ_W8_SYM, n=32, k=128), -1, C, D)]) == rq.RQ_ERR_FORMAT
-    assert _chain([(_w(n=32, k=192), -1, C, D)]) == rq.RQ_ERR_SHAPE     # k % 128
-    assert _chain([(_w(n=24, k=128), -1, C, D)]) == rq.RQ_ERR_SHAPE     # n % 16
-    # the consumer's k must equal its source's n
-    w1 = _w(n=128, k=128)
-    w2 = _w(n=32, k=128, codes=B + 0x100000, scales=C + 0x100000)
-    assert _chain([(w, -1, C, D), (_w(n=32, k=256, codes=B, scales=A + 0x100000), 0, None, E)]) == rq.RQ_ERR_SHAPE
-    # outputs may not overlap weights, the input or each other
-    assert _chain([(w, -1, C, A)]) == rq.RQ_ERR_ALIAS
-    assert _chain([(w, -1, C, C)]) == rq.RQ_ERR_ALIAS
-    assert _chain([(w1, -1, C, D), (w2, 0, None, D)]) == rq.RQ_ERR_ALIAS
-    assert _chain([(w1, -1, C, D), (w2, 0, None, B + 0x100000)]) == rq.RQ_ERR_ALIAS
-    assert rq.lib().rq_chain_run(None, None) == rq.RQ_ERR_NULL
-    assert rq.lib().rq_chain_check(None) == rq.RQ_ERR_NULL
-    assert rq.lib().rq_chain_destroy(None) == rq.RQ_ERR_NULL
