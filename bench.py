@@ -55,9 +55,9 @@ _CAPTURE_STREAM = None
 
 
 def capture(fn):
-    """Graph of fn's launches.  The eager run goes first on the capture stream
-    itself: it loads the code objects and gives that stream its K-split
-    workspace (the library allocates nothing while a stream is capturing)."""
+    """Graph of fn's launches.  An eager run goes first on the capture stream:
+    it loads the code objects and allocates the binding's default workspace,
+    which the graph's products then share."""
     global _CAPTURE_STREAM
     if _CAPTURE_STREAM is None:
         _CAPTURE_STREAM = torch.cuda.Stream()

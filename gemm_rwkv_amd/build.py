@@ -59,6 +59,55 @@ def build(verbose=True):
     return LIB
 
 
+SANITIZED = os.path.join(BUILD, "sanitized", "librq.so")
+# host-side sanitizers only (device code is built as usual)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+HOST_SOURCES = ["api.hip", "validate.cpp"]
+
+
+def build_sanitized(verbose=True):
+    """librq.so with the host-side C ABI layer (argument validation, planning
+    inputs) built under AddressSanitizer and UndefinedBehaviorSanitizer, linked
+    with the kernel objects of the regular build, at _build/sanitized/.  Load
+    it with the sanitizer runtime preloaded (see tests/test_abi_sanitized.py)."""
+    out = os.path.dirname(SANITIZED)
+    os.makedirs(out, exist_ok=True)
+    kernel_objs = [os.path.join(BUILD, src + ".o") for src in SOURCES if src not in HOST_SOURCES]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        build(verbose)
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(out, src + ".o")
+        cmd = [HIPCC] + FLAGS + SAN_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+        objs.append(obj)
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan",
+           "-o", SANITIZED] + objs + kernel_objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed: %s\n%s" % (r.stdout, r.stderr))
+    if verbose:
+        print("built", SANITIZED)
+    return SANITIZED
+
+
+def sanitizer_runtime():
+    """Path of the clang AddressSanitizer runtime the sanitized build links."""
+    r = subprocess.run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        import glob
+        cands = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        path = cands[0] if cands else ""
+    return path
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "sanitized":
+        build_sanitized()
+    else:
+        build()
     sys.exit(0)

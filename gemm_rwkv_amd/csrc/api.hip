@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
-#include <mutex>
 #include <vector>
 
 #include "device_common.h"
@@ -54,40 +53,24 @@ void fill_matrix(rq::GemvMatrix& g, const rq_qweight* w, const uint16_t* x, uint
   g.tiles = (int)((w->n + 15) / 16);
 }
 
-// Workspace of the K-split products (fp32 or int32 partial tiles), one per
-// (device, stream) so that products on different streams never share it; on
-// one stream the kernels that use it run one after another.  It is allocated
-// on the first product on that stream.  During graph capture nothing is
-// allocated: a stream without a workspace runs unsplit launch shapes (same
-// results for the weight-streaming products; the dense GEMMs then sum K in
-// one workgroup, equal within rounding).
-struct Workspace {
-  int dev;
-  hipStream_t stream;
-  void* mem;
-};
-std::mutex g_ws_mu;
-std::vector<Workspace> g_ws;
-
-void* stream_workspace(hipStream_t st) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  for (const Workspace& w : g_ws)
-    if (w.dev == dev && w.stream == st) return w.mem;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  void* mem = nullptr;
-  if (hipMalloc(&mem, rq::kGemvWsPartialBytes) != hipSuccess) return nullptr;
-  g_ws.push_back(Workspace{dev, st, mem});
-  return mem;
+// The caller's workspace (may be NULL): 16-byte aligned, and disjoint from
+// every input and output of the call.  RQ_OK or the error to return.
+int check_ws(const void* ws, size_t ws_bytes, const Span* io, int nio) {
+  if (!ws) return RQ_OK;
+  if (!rqv::aligned16(ws)) return RQ_ERR_ALIGN;
+  Span w;
+  w.lo = (uintptr_t)ws;
+  w.hi = w.lo + ws_bytes;
+  for (int i = 0; i < nio; ++i)
+    if (rqv::overlaps(w, io[i])) return RQ_ERR_ALIAS;
+  return RQ_OK;
 }
 
-void gemv_workspace(hipStream_t st, rq::GemvBatch& b) { b.ws = (float*)stream_workspace(st); }
+inline size_t ws_size(const void* ws, size_t ws_bytes) { return ws ? ws_bytes : 0; }
 
 // Shared path of the gemv entry points and rq_gemm_small_m.
 int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
-            void* stream, int want_format, int want_group) {
+            void* ws, size_t ws_bytes, void* stream, int want_format, int want_group) {
   int st = rqv::check_weight(w);
   if (st != RQ_OK) return st;
   const int gf = gemv_fmt(w->format);
@@ -97,10 +80,12 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   if (m < 0 || m > 32) return RQ_ERR_SHAPE;
   if ((st = rqv::check_act(x, m, w->k, ldx)) != RQ_OK) return st;
   if ((st = rqv::check_out(y, m, w->n, ldy)) != RQ_OK) return st;
-  Span ins[5];
+  Span ins[6];
   rqv::weight_spans(w, ins);
   ins[4] = rqv::act_span(x, m, w->k, ldx, 2);
-  if ((st = check_alias_out(rqv::act_span(y, m, w->n, ldy, 2), ins, 5)) != RQ_OK) return st;
+  ins[5] = rqv::act_span(y, m, w->n, ldy, 2);
+  if ((st = check_alias_out(ins[5], ins, 5)) != RQ_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, ins, 6)) != RQ_OK) return st;
   if (m == 0 || w->n == 0) return RQ_OK;
   rq::GemvBatch b;
   memset(&b, 0, sizeof(b));
@@ -110,13 +95,14 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   b.m = (int)m;
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
-  gemv_workspace(S(stream), b);
+  b.ws = (float*)ws;
+  b.ws_bytes = ws_size(ws, ws_bytes);
   return gemv_status(rq::launch_gemv(b, gf, w->group, S(stream)));
 }
 
 // rq_gemm_w4: int4 codes (symmetric groups or asymmetric superblocks), any m.
 int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
-            void* stream) {
+            void* ws, size_t ws_bytes, void* stream) {
   int st = rqv::check_weight(w);
   if (st != RQ_OK) return st;
   if (w->format != RQ_W4_SYM && w->format != RQ_W4_ASYM_SB256) return RQ_ERR_FORMAT;
@@ -124,10 +110,12 @@ int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   if (m < 0 || m >= rqv::kMaxDim) return RQ_ERR_SHAPE;
   if ((st = rqv::check_act(x, m, w->k, ldx)) != RQ_OK) return st;
   if ((st = rqv::check_out(y, m, w->n, ldy)) != RQ_OK) return st;
-  Span ins[5];
+  Span ins[6];
   rqv::weight_spans(w, ins);
   ins[4] = rqv::act_span(x, m, w->k, ldx, 2);
-  if ((st = check_alias_out(rqv::act_span(y, m, w->n, ldy, 2), ins, 5)) != RQ_OK) return st;
+  ins[5] = rqv::act_span(y, m, w->n, ldy, 2);
+  if ((st = check_alias_out(ins[5], ins, 5)) != RQ_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, ins, 6)) != RQ_OK) return st;
   if (m == 0 || w->n == 0) return RQ_OK;
   rq::W4Gemm p;
   p.x = x;
@@ -141,12 +129,12 @@ int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   p.k = (int)w->k;
   p.ldx = (int)ldx;
   p.ldy = (int)ldy;
-  return hip_status(rq::launch_gemm_w4(p, w->format == RQ_W4_ASYM_SB256, w->group, (float*)stream_workspace(S(stream)),
-                                       rq::kGemvWsPartialBytes, S(stream)));
+  return hip_status(rq::launch_gemm_w4(p, w->format == RQ_W4_ASYM_SB256, w->group, (float*)ws,
+                                       ws_size(ws, ws_bytes), S(stream)));
 }
 
 int w8a8(const void* xq, const float* sx, int64_t m, const rq_qweight* w, uint16_t* y, int64_t ldy,
-         int32_t* acc, void* stream, int want_format) {
+         int32_t* acc, void* ws, size_t ws_bytes, void* stream, int want_format) {
   int st = rqv::check_weight(w);
   if (st != RQ_OK) return st;
   if (w->format != want_format) return RQ_ERR_FORMAT;
@@ -155,22 +143,25 @@ int w8a8(const void* xq, const float* sx, int64_t m, const rq_qweight* w, uint16
   if (!xq || (y && !sx)) return RQ_ERR_NULL;
   if (m < 0 || m >= rqv::kMaxDim) return RQ_ERR_SHAPE;
   if (!rqv::aligned16(xq) || (sx && !rqv::aligned16(sx))) return RQ_ERR_ALIGN;
-  Span ins[6];
+  Span ins[8];
   rqv::weight_spans(w, ins);
   ins[4] = rqv::act_span(xq, m, w->k, w->k, 1);
   ins[5] = sx ? rqv::act_span(sx, m > 0 ? 1 : 0, m, m, 4) : Span();
   if (y) {
     if ((st = rqv::check_out(y, m, w->n, ldy)) != RQ_OK) return st;
-    if ((st = check_alias_out(rqv::act_span(y, m, w->n, ldy, 2), ins, 6)) != RQ_OK) return st;
+    ins[6] = rqv::act_span(y, m, w->n, ldy, 2);
+    if ((st = check_alias_out(ins[6], ins, 6)) != RQ_OK) return st;
   }
   if (acc) {
     if (!rqv::aligned16(acc)) return RQ_ERR_ALIGN;
-    if ((st = check_alias_out(rqv::act_span(acc, m, w->n, w->n, 4), ins, 6)) != RQ_OK) return st;
+    ins[7] = rqv::act_span(acc, m, w->n, w->n, 4);
+    if ((st = check_alias_out(ins[7], ins, 6)) != RQ_OK) return st;
   }
+  if ((st = check_ws(ws, ws_bytes, ins, 8)) != RQ_OK) return st;
   if (m == 0 || w->n == 0) return RQ_OK;
   return hip_status(rq::launch_gemm_w8a8(xq, sx, (int)m, w->codes, (const float*)w->scales, (int)w->n,
-                                         (int)w->k, want_format == RQ_FP8_E4M3_CH, y, (int)ldy, acc,
-                                         stream_workspace(S(stream)), rq::kGemvWsPartialBytes, S(stream)));
+                                         (int)w->k, want_format == RQ_FP8_E4M3_CH, y, (int)ldy, acc, ws,
+                                         ws_size(ws, ws_bytes), S(stream)));
 }
 
 }  // namespace
@@ -273,11 +264,11 @@ int rq_quantize_aw(const float* w, const float* act_sq, const rq_qweight* out, v
   return quantize_impl(w, act_sq, out, stream);
 }
 
-#define RQ_GEMV_ENTRY(NAME, FORMAT, GROUP)                                                    \
-  int NAME(const uint16_t* x, const rq_qweight* w, uint16_t* y, void* stream) {               \
-    if (!w) return RQ_ERR_NULL;                                                               \
-    return small_m(x, 1, w->k + (8 - w->k % 8) % 8, w, y, w->n > 0 ? w->n : 1, stream, FORMAT, \
-                   GROUP);                                                                    \
+#define RQ_GEMV_ENTRY(NAME, FORMAT, GROUP)                                                           \
+  int NAME(const uint16_t* x, const rq_qweight* w, uint16_t* y, void* ws, size_t ws_bytes, void* stream) { \
+    if (!w) return RQ_ERR_NULL;                                                                      \
+    return small_m(x, 1, w->k + (8 - w->k % 8) % 8, w, y, w->n > 0 ? w->n : 1, ws, ws_bytes, stream,   \
+                   FORMAT, GROUP);                                                                   \
   }
 
 RQ_GEMV_ENTRY(rq_gemv_w4g16, RQ_W4_SYM, 16)
@@ -291,13 +282,13 @@ RQ_GEMV_ENTRY(rq_gemv_f16, RQ_F16, 0)
 #undef RQ_GEMV_ENTRY
 
 int rq_gemm_small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y,
-                    int64_t ldy, void* stream) {
-  return small_m(x, m, ldx, w, y, ldy, stream, 0, 0);
+                    int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return small_m(x, m, ldx, w, y, ldy, ws, ws_bytes, stream, 0, 0);
 }
 
 int rq_fused_rkv(const uint16_t* xr, const uint16_t* xk, const uint16_t* xv, int64_t m, int64_t ldx,
                  const rq_qweight* wr, const rq_qweight* wk, const rq_qweight* wv, uint16_t* yr,
-                 uint16_t* yk, uint16_t* yv, int64_t ldy, void* stream) {
+                 uint16_t* yk, uint16_t* yv, int64_t ldy, void* wsp, size_t ws_bytes, void* stream) {
   const rq_qweight* ws[3] = {wr, wk, wv};
   const uint16_t* xs[3] = {xr, xk, xv};
   uint16_t* ys[3] = {yr, yk, yv};
@@ -325,6 +316,8 @@ int rq_fused_rkv(const uint16_t* xr, const uint16_t* xk, const uint16_t* xv, int
     for (int j = i + 1; j < 3; ++j)
       if (rqv::overlaps(outs[i], outs[j])) return RQ_ERR_ALIAS;
   }
+  if ((st = check_ws(wsp, ws_bytes, ins, 15)) != RQ_OK) return st;
+  if ((st = check_ws(wsp, ws_bytes, outs, 3)) != RQ_OK) return st;
   if (m == 0) return RQ_OK;
   rq::GemvBatch b;
   memset(&b, 0, sizeof(b));
@@ -334,7 +327,8 @@ int rq_fused_rkv(const uint16_t* xr, const uint16_t* xk, const uint16_t* xv, int
   b.m = (int)m;
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
-  gemv_workspace(S(stream), b);
+  b.ws = (float*)wsp;
+  b.ws_bytes = ws_size(wsp, ws_bytes);
   return gemv_status(rq::launch_gemv(b, gf, wr->group, S(stream)));
 }
 
@@ -356,26 +350,29 @@ int rq_quantize_act(const uint16_t* x, int64_t m, int64_t k, int64_t ldx, int fo
 }
 
 int rq_gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
-               void* stream) {
-  return gemm_w4(x, m, ldx, w, y, ldy, stream);
+               void* ws, size_t ws_bytes, void* stream) {
+  return gemm_w4(x, m, ldx, w, y, ldy, ws, ws_bytes, stream);
 }
 
 int rq_gemm_fp8(const uint8_t* xq, const float* sx, int64_t m, const rq_qweight* w, uint16_t* y,
-                int64_t ldy, void* stream) {
+                int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   if (!y) return RQ_ERR_NULL;
-  return w8a8(xq, sx, m, w, y, ldy, nullptr, stream, RQ_FP8_E4M3_CH);
+  return w8a8(xq, sx, m, w, y, ldy, nullptr, ws, ws_bytes, stream, RQ_FP8_E4M3_CH);
 }
 
 int rq_gemm_int8(const int8_t* xq, const float* sx, int64_t m, const rq_qweight* w, uint16_t* y,
-                 int64_t ldy, void* stream) {
+                 int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   if (!y) return RQ_ERR_NULL;
-  return w8a8(xq, sx, m, w, y, ldy, nullptr, stream, RQ_I8_CH);
+  return w8a8(xq, sx, m, w, y, ldy, nullptr, ws, ws_bytes, stream, RQ_I8_CH);
 }
 
-int rq_gemm_int8_acc(const int8_t* xq, int64_t m, const rq_qweight* w, int32_t* acc, void* stream) {
+int rq_gemm_int8_acc(const int8_t* xq, int64_t m, const rq_qweight* w, int32_t* acc, void* ws, size_t ws_bytes,
+                     void* stream) {
   if (!acc || !w) return RQ_ERR_NULL;
-  return w8a8(xq, nullptr, m, w, nullptr, w->n, acc, stream, RQ_I8_CH);
+  return w8a8(xq, nullptr, m, w, nullptr, w->n, acc, ws, ws_bytes, stream, RQ_I8_CH);
 }
+
+size_t rq_workspace_bytes(void) { return rq::kWorkspaceBytes; }
 
 int rq_host_convert(int kind, const double* in, void* out, int64_t count) {
   if (!in || !out) return RQ_ERR_NULL;

@@ -1070,7 +1070,7 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     const int wpt = (cps + 3) / 4;
     const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
     if (b.ws && b.m <= 4 && tiles < 256 && nchunks >= 64 && wpt <= 16 && xb <= (size_t)kXBudget &&
-        (size_t)tiles * used * mt * 1024 <= kGemvWsPartialBytes) {
+        (size_t)tiles * used * mt * 1024 <= b.ws_bytes) {
       sp.split = used;
       sp.cps = cps;
       sp.wpt = wpt;
@@ -1108,6 +1108,9 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
   // row tiles share a workgroup (and its activation slice) only where that
   // slice is larger than the tile's codes, 16 rows x 64 bytes per chunk
   const bool share_x = (b.m + 1) * F::CK * 2 > 16 * 64;
+  Split5 unsplit;
+  int unsplit_cpw = 0;
+  bool have_unsplit = false;
   // unsplit with a large activation slice, if that occupies at least half
   // of the compute units
   {
@@ -1140,15 +1143,21 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
       // split with small slices does better (10240x2560 at M = 16, 5-/6-bit
       // codes and SB256: 15.1-16.8 -> 14.4-15.6 us), where the stream has
       // the workspace for it
+      Split5 u;
+      u.split = 1;
+      u.cps = nchunks;
+      u.wpt = wpt;
+      u.rt = rt;
+      for (int i = 0; i < 3; ++i) u.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
       if (groups(rt) <= 256 || !b.ws) {
-        sp.split = 1;
-        sp.cps = nchunks;
-        sp.wpt = wpt;
-        sp.rt = rt;
-        for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
+        sp = u;
         cpw_out = cpw;
         return true;
       }
+      // kept in case the workspace is too small for any split
+      unsplit = u;
+      unsplit_cpw = cpw;
+      have_unsplit = true;
     }
   }
   for (int split = 1; split <= 16; split *= 2) {
@@ -1200,7 +1209,7 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     while (share_x && rt < 4 && 2 * rt * wpt <= 16 &&
            (!one_round(rt) || (x_heavy(rt) && groups(2 * rt) * used >= 256)))
       rt *= 2;
-    if (used > 1 && (size_t)groups(rt) * rt * used * mt * 1024 > kGemvWsPartialBytes) break;
+    if (used > 1 && (size_t)groups(rt) * rt * used * mt * 1024 > b.ws_bytes) break;
     sp.split = used;
     sp.cps = cps;
     sp.wpt = wpt;
@@ -1211,6 +1220,11 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     // a split costs a second launch: worth it only to occupy more than half
     // of the compute units, or to fit the activations
     if (groups(rt) * used >= (used == 1 ? 128 : 256)) break;
+  }
+  if (!found && have_unsplit) {
+    sp = unsplit;
+    cpw_out = unsplit_cpw;
+    return true;
   }
   return found;
 }

@@ -42,12 +42,14 @@ struct GemvBatch {
   int m;
   int ldx;
   int ldy;
-  // workspace for products split along K (null: no split): fp32 partial
-  // tiles, summed by a second kernel
+  // caller's workspace for products split along K (null: no split): fp32
+  // partial tiles, summed by a second kernel; the planner keeps within ws_bytes
   float* ws;
+  size_t ws_bytes;
 };
 
-constexpr size_t kGemvWsPartialBytes = 64u << 20;
+// workspace size that admits every product's fastest plan
+constexpr size_t kWorkspaceBytes = 64u << 20;
 
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 

@@ -11,7 +11,8 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librq.so")
+# RQ_LIBRARY selects another build of the same library (the sanitized one)
+_LIB_PATH = os.environ.get("RQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "librq.so")
 
 RQ_OK = 0
 RQ_ERR_NULL = -1
@@ -39,7 +40,7 @@ EXPORTS = (
     "rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16", "rq_gemv_w8g32",
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
-    "rq_gemm_w4", "rq_quantize_aw",
+    "rq_gemm_w4", "rq_quantize_aw", "rq_workspace_bytes",
 )
 
 
@@ -65,7 +66,7 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError("librq.so is not built (run gemm_rwkv_amd.build or __graft_entry__.build())")
         L = ctypes.CDLL(_LIB_PATH)
-        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         qp = ctypes.POINTER(_QW)
         sig = {
             "rq_abi_version": ([], i32),
@@ -73,18 +74,19 @@ def lib():
             "rq_qweight_bytes": ([i32, i32, i64, i64] + [ctypes.POINTER(ctypes.c_size_t)] * 4, i32),
             "rq_quantize_rtn": ([vp, qp, vp], i32),
             "rq_quantize_aw": ([vp, vp, qp, vp], i32),
-            "rq_gemm_small_m": ([vp, i64, i64, qp, vp, i64, vp], i32),
-            "rq_gemm_w4": ([vp, i64, i64, qp, vp, i64, vp], i32),
-            "rq_fused_rkv": ([vp, vp, vp, i64, i64, qp, qp, qp, vp, vp, vp, i64, vp], i32),
+            "rq_gemm_small_m": ([vp, i64, i64, qp, vp, i64, vp, sz, vp], i32),
+            "rq_gemm_w4": ([vp, i64, i64, qp, vp, i64, vp, sz, vp], i32),
+            "rq_fused_rkv": ([vp, vp, vp, i64, i64, qp, qp, qp, vp, vp, vp, i64, vp, sz, vp], i32),
             "rq_quantize_act": ([vp, i64, i64, i64, i32, vp, vp, vp], i32),
-            "rq_gemm_fp8": ([vp, vp, i64, qp, vp, i64, vp], i32),
-            "rq_gemm_int8": ([vp, vp, i64, qp, vp, i64, vp], i32),
-            "rq_gemm_int8_acc": ([vp, i64, qp, vp, vp], i32),
+            "rq_gemm_fp8": ([vp, vp, i64, qp, vp, i64, vp, sz, vp], i32),
+            "rq_gemm_int8": ([vp, vp, i64, qp, vp, i64, vp, sz, vp], i32),
+            "rq_gemm_int8_acc": ([vp, i64, qp, vp, vp, sz, vp], i32),
+            "rq_workspace_bytes": ([], sz),
             "rq_host_convert": ([i32, vp, vp, i64], i32),
         }
         for name in ("rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16",
                      "rq_gemv_w8g32", "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16"):
-            sig[name] = ([vp, qp, vp, vp], i32)
+            sig[name] = ([vp, qp, vp, vp, sz, vp], i32)
         for name, (args, res) in sig.items():
             f = getattr(L, name)
             f.argtypes = args
@@ -108,6 +110,40 @@ def _ptr(t):
     if isinstance(t, int):
         return t
     return t.data_ptr()
+
+
+_default_ws = {}
+
+
+def default_workspace(device=None):
+    """The binding's default workspace on a device: a uint8 tensor of
+    rq_workspace_bytes(), allocated on first use and kept.  It is shared by
+    every call that passes no workspace of its own, so such calls must not
+    run concurrently.  Allocating it while a graph is being captured is
+    refused: call this once before capturing."""
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index or 0)
+    t = _default_ws.get(dev.index)
+    if t is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("rq: allocate the default workspace before graph capture "
+                               "(call gemm_rwkv_amd.rq.default_workspace() first)")
+        t = torch.empty(lib().rq_workspace_bytes(), dtype=torch.uint8, device=dev)
+        _default_ws[dev.index] = t
+    return t
+
+
+def _ws(ws):
+    """(pointer, bytes) of a workspace argument: None = the default
+    workspace, False = none, or a uint8 device tensor."""
+    if ws is False:
+        return None, 0
+    if ws is None:
+        if not torch.cuda.is_available():
+            return None, 0
+        ws = default_workspace()
+    if isinstance(ws, tuple):
+        return ws
+    return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def _stream(stream):
@@ -203,9 +239,9 @@ def quantize_aw(w, act_sq, fmt, group=0, stream=None):
 
 
 def _gemv(name):
-    def f(x, w, y, stream=None):
+    def f(x, w, y, stream=None, ws=None):
         d = w.desc()
-        st = getattr(lib(), name)(_ptr(x), ctypes.byref(d), _ptr(y), _stream(stream))
+        st = getattr(lib(), name)(_ptr(x), ctypes.byref(d), _ptr(y), *_ws(ws), _stream(stream))
         _check(st, name)
         return y
     f.__name__ = name
@@ -229,24 +265,24 @@ GEMV_ENTRY = {
 }
 
 
-def rq_gemm_small_m(x, m, ldx, w, y, ldy, stream=None):
+def rq_gemm_small_m(x, m, ldx, w, y, ldy, stream=None, ws=None):
     d = w.desc()
-    st = lib().rq_gemm_small_m(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, _stream(stream))
+    st = lib().rq_gemm_small_m(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_small_m")
     return y
 
 
-def rq_gemm_w4(x, m, ldx, w, y, ldy, stream=None):
+def rq_gemm_w4(x, m, ldx, w, y, ldy, stream=None, ws=None):
     d = w.desc()
-    st = lib().rq_gemm_w4(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, _stream(stream))
+    st = lib().rq_gemm_w4(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_w4")
     return y
 
 
-def rq_fused_rkv(xr, xk, xv, m, ldx, wr, wk, wv, yr, yk, yv, ldy, stream=None):
+def rq_fused_rkv(xr, xk, xv, m, ldx, wr, wk, wv, yr, yk, yv, ldy, stream=None, ws=None):
     ds = [wr.desc(), wk.desc(), wv.desc()]
     st = lib().rq_fused_rkv(_ptr(xr), _ptr(xk), _ptr(xv), m, ldx, *[ctypes.byref(d) for d in ds],
-                            _ptr(yr), _ptr(yk), _ptr(yv), ldy, _stream(stream))
+                            _ptr(yr), _ptr(yk), _ptr(yv), ldy, *_ws(ws), _stream(stream))
     _check(st, "rq_fused_rkv")
     return yr, yk, yv
 
@@ -257,25 +293,29 @@ def rq_quantize_act(x, m, k, ldx, fmt, xq, sx, stream=None):
     return xq, sx
 
 
-def rq_gemm_fp8(xq, sx, m, w, y, ldy, stream=None):
+def rq_gemm_fp8(xq, sx, m, w, y, ldy, stream=None, ws=None):
     d = w.desc()
-    st = lib().rq_gemm_fp8(_ptr(xq), _ptr(sx), m, ctypes.byref(d), _ptr(y), ldy, _stream(stream))
+    st = lib().rq_gemm_fp8(_ptr(xq), _ptr(sx), m, ctypes.byref(d), _ptr(y), ldy, *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_fp8")
     return y
 
 
-def rq_gemm_int8(xq, sx, m, w, y, ldy, stream=None):
+def rq_gemm_int8(xq, sx, m, w, y, ldy, stream=None, ws=None):
     d = w.desc()
-    st = lib().rq_gemm_int8(_ptr(xq), _ptr(sx), m, ctypes.byref(d), _ptr(y), ldy, _stream(stream))
+    st = lib().rq_gemm_int8(_ptr(xq), _ptr(sx), m, ctypes.byref(d), _ptr(y), ldy, *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_int8")
     return y
 
 
-def rq_gemm_int8_acc(xq, m, w, acc, stream=None):
+def rq_gemm_int8_acc(xq, m, w, acc, stream=None, ws=None):
     d = w.desc()
-    st = lib().rq_gemm_int8_acc(_ptr(xq), m, ctypes.byref(d), _ptr(acc), _stream(stream))
+    st = lib().rq_gemm_int8_acc(_ptr(xq), m, ctypes.byref(d), _ptr(acc), *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_int8_acc")
     return acc
+
+
+def rq_workspace_bytes():
+    return int(lib().rq_workspace_bytes())
 
 
 def rq_host_convert(kind, values):

@@ -19,15 +19,19 @@
  *     after returning.
  *   - Workspace: the products (rq_gemv_*, rq_gemm_small_m, rq_fused_rkv,
  *     rq_gemm_w4, rq_gemm_fp8, rq_gemm_int8, rq_gemm_int8_acc) may cut K
- *     across workgroups and add the partial sums in a second kernel.  Those
- *     partials live in a 64 MiB device buffer that the library allocates on
- *     the first such call on each (device, stream) pair and keeps until the
- *     process ends, so calls on different streams never share one.  While a
- *     stream is being captured into a graph nothing is allocated: a stream
- *     that has no workspace yet runs unsplit launch shapes (warm up on the
- *     capture stream to capture the split shapes).  The weight-streaming
- *     products give the same results either way; the dense GEMMs agree
- *     within the fp32 summation tolerance.
+ *     across workgroups and add the partial sums in a second kernel.  The
+ *     partial sums live in a device buffer the CALLER owns and passes as
+ *     (workspace, workspace_bytes): 16-byte aligned, disjoint from the call's
+ *     inputs and outputs (RQ_ERR_ALIGN, RQ_ERR_ALIAS).  rq_workspace_bytes()
+ *     is the size that admits every product's fastest launch shape; with a
+ *     smaller buffer, or workspace == NULL (workspace_bytes is then ignored),
+ *     the planner keeps to the shapes that fit, down to no K split at all.
+ *     The launch shape is a function of the arguments alone (shapes, formats,
+ *     whether a workspace is given and its size), never of earlier calls.  No
+ *     product call allocates device memory.  The workspace holds nothing
+ *     between calls, but calls that may run at the same time (on different
+ *     streams, or graph replays on different streams) need distinct
+ *     workspaces.
  *   - fp16 values are IEEE binary16 bit patterns (uint16_t).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it; product calls return without synchronizing.
@@ -41,15 +45,13 @@
  *   - Shapes: n >= 0 and m >= 0 (zero = nothing to do, RQ_OK, but pointers must
  *     still be valid), k >= 1, n and k below 2^31, and the per-format rules of
  *     rq_qweight.
- *   - Determinism: the same inputs on the same device give bit-identical
- *     outputs (fixed reduction order, no floating-point atomics).  Different
- *     entry points over the same weights (a fused call and three single
- *     calls, or a stream with and without a workspace) may split K
- *     differently and differ within the fp32 summation tolerance.
- *   - Thread safety: apart from the per-stream workspaces (guarded by a
- *     lock) the library keeps no state; calls on different streams may run
- *     concurrently.  A captured graph uses its capture stream's workspace,
- *     so two replays of graphs captured on one stream must not overlap.
+ *   - Determinism: the same inputs and workspace size on the same device
+ *     give bit-identical outputs (fixed reduction order, no floating-point
+ *     atomics).  Different entry points over the same weights (a fused call
+ *     and three single calls), or different workspace sizes, may split K
+ *     differently and then differ within the fp32 summation tolerance.
+ *   - Thread safety: the library keeps no state between calls; calls on
+ *     different streams may run concurrently given distinct workspaces.
  */
 #ifndef RQ_H
 #define RQ_H
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 1
+#define RQ_ABI_VERSION 2
 
 enum rq_status {
   RQ_OK = 0,
@@ -169,6 +171,10 @@ int rq_abi_version(void);
 /* Static text for a status code (never NULL). */
 const char *rq_status_str(int status);
 
+/* Size in bytes of the workspace that admits every product's fastest launch
+ * shape (see Workspace above).  Host-only. */
+size_t rq_workspace_bytes(void);
+
 /* Byte sizes of the four buffers of a (format, group, n, k) weight.  Any of
  * the output pointers may be NULL.  Host-only; launches nothing.
  * Errors: RQ_ERR_FORMAT, RQ_ERR_SHAPE. */
@@ -176,7 +182,9 @@ int rq_qweight_bytes(int format, int group, int64_t n, int64_t k, size_t *codes_
                      size_t *scales_bytes, size_t *mins_bytes, size_t *sub_bytes);
 
 /* Round-to-nearest quantization of fp32 weights w[n][k] (device, contiguous)
- * into the format, group, n and k named by *out, whose buffers the caller has
+ * into the format, group, n and k named by *out (the group-wise codes plus
+ * scales of the model card's "Format & loading" -- a .qweight code tensor and
+ * a .scale tensor -- and the formats listed above with their pages), whose buffers the caller has
  * allocated with rq_qweight_bytes sizes.  Every quotient is an IEEE fp64
  * division followed by one rounding to the target grid, so the codes and
  * scales are exactly those of the format's definition.  Synchronizes `stream`
@@ -204,18 +212,29 @@ int rq_quantize_rtn(const float *w, const rq_qweight *out, void *stream);
 int rq_quantize_aw(const float *w, const float *act_sq, const rq_qweight *out, void *stream);
 
 /* M = 1 products y[n] = sum_k x[k] * W_hat[n][k], fp32 accumulation, fp16
- * output (RNE).  x: fp16 [k]; y: fp16 [n].  Each entry point accepts exactly
+ * output (RNE): the int4 GEMV of the model card's summary (decode reads the
+ * packed codes and scales directly, no dequantized copy: RWKV-7 Quantization
+ * Toolkit, Key Design), and its int8 tier (model card, accuracy warning:
+ * w8g64).  x: fp16 [k]; y: fp16 [n].  Each entry point accepts exactly
  * its format and group (RQ_ERR_FORMAT otherwise):
  *   w4gG: RQ_W4_SYM, group G;  w8gG: RQ_W8_SYM, group G;
  *   w4sb256: RQ_W4_ASYM_SB256;  f16: RQ_F16. */
-int rq_gemv_w4g16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
-int rq_gemv_w4g32(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
-int rq_gemv_w4g64(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
-int rq_gemv_w8g16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
-int rq_gemv_w8g32(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
-int rq_gemv_w8g64(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
-int rq_gemv_w4sb256(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
-int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *stream);
+int rq_gemv_w4g16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                  size_t workspace_bytes, void *stream);
+int rq_gemv_w4g32(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                  size_t workspace_bytes, void *stream);
+int rq_gemv_w4g64(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                  size_t workspace_bytes, void *stream);
+int rq_gemv_w8g16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                  size_t workspace_bytes, void *stream);
+int rq_gemv_w8g32(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                  size_t workspace_bytes, void *stream);
+int rq_gemv_w8g64(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                  size_t workspace_bytes, void *stream);
+int rq_gemv_w4sb256(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                    size_t workspace_bytes, void *stream);
+int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 /* Small-M products for decode batches 1 <= m <= 32 (model card, summary:
  * batch sizes up to 32).  x: fp16 [m][ldx], ldx >= k, ldx % 8 == 0;
@@ -229,12 +248,12 @@ int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *strea
  * a slice too large: with chunks of C = 128 k (RQ_W6_SYM, RQ_W5_SYM) or 32 k
  * (RQ_BF16) and c = ceil(k / 16 / C) chunks per slice, (m + 1) * (c * C + 8)
  * above 40960 (k above 18432 at m = 32, 36864 at m = 16) or c above 128
- * (256 for RQ_BF16 at m <= 2).  Cutting K needs the stream's workspace (see
+ * (256 for RQ_BF16 at m <= 2).  Cutting K needs a workspace of enough bytes (see
  * Workspace); without one, (m + 1) * (k + 8) must stay within 40960, or
  * 76800 for 128 or more row tiles (192 to 256 row tiles also stream k up to
  * 8192 at m > 16 and 16384 at m = 4..8).  Other formats take any shape. */
 int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w,
-                    uint16_t *y, int64_t ldy, void *stream);
+                    uint16_t *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Prefill products on int4 codes for any number of rows m (the tensor-core
  * GEMM member of the int4 family in the model card's summary), on MFMA:
@@ -247,7 +266,7 @@ int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight 
  * activation rows; meant for m from about 64 up (rq_gemm_small_m covers
  * m <= 32).  Any m >= 0. */
 int rq_gemm_w4(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w, uint16_t *y,
-               int64_t ldy, void *stream);
+               int64_t ldy, void *workspace, size_t workspace_bytes, void *stream);
 
 /* The R, K and V projections in one launch (RWKV-7 Quantization Toolkit,
  * Key Design: "R/K/V projections computed in a single kernel launch").
@@ -257,7 +276,8 @@ int rq_gemm_w4(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w, u
  * overlap each other or any input. */
 int rq_fused_rkv(const uint16_t *xr, const uint16_t *xk, const uint16_t *xv, int64_t m,
                  int64_t ldx, const rq_qweight *wr, const rq_qweight *wk, const rq_qweight *wv,
-                 uint16_t *yr, uint16_t *yk, uint16_t *yv, int64_t ldy, void *stream);
+                 uint16_t *yr, uint16_t *yk, uint16_t *yv, int64_t ldy, void *workspace,
+                 size_t workspace_bytes, void *stream);
 
 /* Per-token dynamic activation quantization for the W8A8 / FP8 GEMMs (both
  * operands of the toolkit's int8 x int8 and fp8 x fp8 products are
@@ -274,17 +294,18 @@ int rq_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int fo
  * [m][k]; w: RQ_FP8_E4M3_CH with k % 128 == 0; y: fp16 [m][ldy], ldy >= n.
  * Any m >= 0. */
 int rq_gemm_fp8(const uint8_t *xq, const float *sx, int64_t m, const rq_qweight *w, uint16_t *y,
-                int64_t ldy, void *stream);
+                int64_t ldy, void *workspace, size_t workspace_bytes, void *stream);
 
 /* INT8 x INT8 GEMM on MFMA with exact int32 accumulation ("INT8 via DP4A" on
  * the toolkit page): y[m][n] = fp16(float(acc) * s_x[m] * s_w[n]).
  * w: RQ_I8_CH with k % 128 == 0 and k <= 131072 (|acc| < 2^31). */
 int rq_gemm_int8(const int8_t *xq, const float *sx, int64_t m, const rq_qweight *w, uint16_t *y,
-                 int64_t ldy, void *stream);
+                 int64_t ldy, void *workspace, size_t workspace_bytes, void *stream);
 
 /* The int32 accumulators of rq_gemm_int8 (acc: int32 [m][n], contiguous),
  * for bit-exact checking of the integer contraction. */
-int rq_gemm_int8_acc(const int8_t *xq, int64_t m, const rq_qweight *w, int32_t *acc, void *stream);
+int rq_gemm_int8_acc(const int8_t *xq, int64_t m, const rq_qweight *w, int32_t *acc,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Test aid: the library's own fp64 -> fp16 (kind 0, uint16 out), fp64 ->
  * fp32 (kind 1, uint32 out) and fp64 -> e4m3fn (kind 2, uint8 out)

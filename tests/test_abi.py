@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = rq.lib()
-    assert L.rq_abi_version() == 1
+    assert L.rq_abi_version() == 2
+    assert rq.rq_workspace_bytes() == 64 << 20
     for st in range(-8, 1):
         assert rq.status_str(st) and rq.status_str(st) != "unknown status"
     assert rq.status_str(-99) == "unknown status"
@@ -274,3 +275,26 @@ def test_two_plane_and_bf16_validation():
     assert _status(rq.rq_gemm_small_m, x, 4, 48, _w(rq.RQ_BF16, 0, 32, 48, A), y, 32) == rq.RQ_ERR_SHAPE
     assert _status(rq.rq_gemm_w4, x, 4, 256, w6, y, 32) == rq.RQ_ERR_FORMAT
     rq.rq_gemm_small_m(x, 0, 256, w6, y, 32)   # m == 0: no-op
+
+
+def test_workspace_validation():
+    """A workspace must be 16-byte aligned and disjoint from the call's inputs
+    and outputs; without one (NULL) any size is ignored."""
+    w = _w()
+    x = A + 0x200000
+    y = C
+    W = 0x7f0050000000
+    assert _status(rq.rq_gemm_small_m, x, 1, 128, w, y, 32, None, (W + 8, 1 << 20)) == rq.RQ_ERR_ALIGN
+    assert _status(rq.rq_gemm_small_m, x, 1, 128, w, y, 32, None, (y - 64, 1 << 20)) == rq.RQ_ERR_ALIAS
+    assert _status(rq.rq_gemm_small_m, x, 1, 128, w, y, 32, None, (A, 4096)) == rq.RQ_ERR_ALIAS    # codes
+    assert _status(rq.rq_gemm_small_m, x, 1, 128, w, y, 32, None, (x - 16, 4096)) == rq.RQ_ERR_ALIAS
+    assert _status(rq.rq_gemv_w4g64, x, w, y, None, (B, 64)) == rq.RQ_ERR_ALIAS                     # scales
+    assert _status(rq.rq_gemm_w4, x, 1, 128, w, y, 32, None, (y, 64)) == rq.RQ_ERR_ALIAS
+    assert _status(rq.rq_fused_rkv, x, x, x, 1, 128, w, w, w, y, y + 0x1000, y + 0x2000, 32, None,
+                   (y + 0x2000, 64)) == rq.RQ_ERR_ALIAS
+    f8 = _w(rq.RQ_FP8_E4M3_CH, 0, 32, 128)
+    assert _status(rq.rq_gemm_fp8, x, x + 0x10000, 1, f8, y, 32, None, (x, 64)) == rq.RQ_ERR_ALIAS
+    assert _status(rq.rq_gemm_int8_acc, x, 1, _w(rq.RQ_I8_CH, 0, 32, 128), y, None, (y + 16, 64)) == rq.RQ_ERR_ALIAS
+    # empty extents with a workspace return before any launch
+    rq.rq_gemm_small_m(x, 0, 128, w, y, 32, ws=(W, 1 << 20))
+    rq.rq_gemm_small_m(x, 1, 128, _w(n=0), y, 32, ws=False)

@@ -2,12 +2,12 @@
 
 Each replay runs after eager work of the program's own (the outputs are
 cleared and the same products run eagerly on the default stream) and a
-synchronization, and must reproduce the eager results bit for bit: the graph
-holds the same launch shapes as the eager calls on the capture stream, which
-got its K-split workspace in the eager warm-up (the library allocates
-nothing while a stream is capturing).  A second graph is captured on a
-stream that never ran eagerly: with no workspace the products take unsplit
-launch shapes, and their results must still meet the oracle's tolerance.
+synchronization, and must reproduce the eager results bit for bit: a launch
+shape is a function of the call's arguments alone, workspace included, so the
+graph holds the eager calls' shapes whether or not the capture stream ever ran
+a product before.  Products given no workspace take unsplit launch shapes;
+their graph must match eager calls without a workspace bit for bit, and the
+oracle within its tolerance.
 """
 
 import numpy as np
@@ -49,9 +49,9 @@ def _setup():
     return items
 
 
-def _run(items):
+def _run(items, ws=None):
     for it in items:
-        rq.rq_gemm_small_m(it["xd"], it["m"], it["k"], it["qw"], it["y"], it["n"])
+        rq.rq_gemm_small_m(it["xd"], it["m"], it["k"], it["qw"], it["y"], it["n"], ws=ws)
 
 
 def test_graph_replays_match_eager():
@@ -87,14 +87,43 @@ def test_graph_replays_match_eager():
             assert torch.equal(it["y"], e), (rep, it["fmt"], it["n"], it["k"], it["m"])
 
 
-def test_graph_on_a_stream_without_workspace():
+def test_graph_without_warmup_is_bit_identical():
+    """A graph captured on a stream that never ran a product eagerly holds the
+    same launch shapes, and gives the same bits, as eager calls with the same
+    workspace on another stream."""
+    items = _setup()
+    rq.default_workspace()
+    _run(items)                          # eager, default stream
+    torch.cuda.synchronize()
+    eager = [it["y"].clone() for it in items]
+    s = torch.cuda.Stream()              # no product has run on it
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    say("graph: capture with no warm-up on the capture stream")
+    with torch.cuda.graph(g, stream=s):
+        _run(items)
+    for rep in range(3):
+        for it in items:
+            it["y"].fill_(-1)
+        torch.cuda.synchronize()
+        say("graph: replay with no warm-up", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for it, e in zip(items, eager):
+            assert torch.equal(it["y"], e), (rep, it["fmt"], it["n"], it["k"], it["m"])
+
+
+def test_graph_without_workspace():
     items = [it for it in _setup() if it["fmt"] in (quant.W4_SYM, quant.W8_SYM, quant.W4_ASYM_SB256)]
-    s = torch.cuda.Stream()              # never ran a product eagerly: no workspace
+    _run(items, ws=False)
+    torch.cuda.synchronize()
+    eager = [it["y"].clone() for it in items]
+    s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     say("graph: capture without workspace")
     with torch.cuda.graph(g, stream=s):
-        _run(items)
+        _run(items, ws=False)
     for rep in range(3):
         for it in items:
             it["y"].fill_(-1)
@@ -102,7 +131,8 @@ def test_graph_on_a_stream_without_workspace():
         say("graph: replay without workspace", rep)
         g.replay()
         torch.cuda.synchronize()
-        for it in items:
+        for it, e in zip(items, eager):
+            assert torch.equal(it["y"], e), (rep, it["fmt"], it["n"], it["k"], it["m"])
             y_ref, b = ref.weight_only_ref(it["x"], it["fmt"], it["parts"], it["group"])
             ok, info = ref.compare(host(it["y"], np.float16, (it["m"], it["n"])).astype(np.float64), y_ref, b)
             assert ok, (rep, it["fmt"], it["n"], it["k"], it["m"], info)

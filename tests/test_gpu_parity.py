@@ -257,8 +257,8 @@ def test_split_k_and_tile_groups(fmt, group, n, k, m):
     y_ref, b = ref.weight_only_ref(x, fmt, parts, group)
     ok, info = ref.compare(y1, y_ref, b)
     assert ok, info
-    # the per-group arrival counters are back at zero: a second call, and a
-    # call on another stream (its own workspace), give the same bits
+    # a second call, and a call on another stream with the same workspace,
+    # give the same bits
     y2 = _run_small_m(qw, x, m, k, n)
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
     side = torch.cuda.Stream()
