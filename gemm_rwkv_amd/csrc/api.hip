@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <vector>
 
 #include "device_common.h"
@@ -68,9 +70,36 @@ int check_ws(const void* ws, size_t ws_bytes, const Span* io, int nio) {
 
 inline size_t ws_size(const void* ws, size_t ws_bytes) { return ws ? ws_bytes : 0; }
 
+// Scratch of rq_gemm_small_m_noalloc: the K-split partial sums live in this
+// file-scope device array instead of a workspace, one copy per GPU, kept
+// until the process ends.  Its host-side name is not a device address: the
+// address of each GPU's copy is taken once, with that GPU current, by
+// hipGetSymbolAddress, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// This device's scratch address (nullptr on failure).
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // Shared path of the gemv entry points and rq_gemm_small_m.
+// get_scratch (may be null): the workspace comes from it, once the arguments
+// have passed validation
 int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y, int64_t ldy,
-            void* ws, size_t ws_bytes, void* stream, int want_format, int want_group) {
+            void* ws, size_t ws_bytes, void* stream, int want_format, int want_group,
+            void* (*get_scratch)() = nullptr) {
   int st = rqv::check_weight(w);
   if (st != RQ_OK) return st;
   const int gf = gemv_fmt(w->format);
@@ -87,6 +116,10 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   if ((st = check_alias_out(ins[5], ins, 5)) != RQ_OK) return st;
   if ((st = check_ws(ws, ws_bytes, ins, 6)) != RQ_OK) return st;
   if (m == 0 || w->n == 0) return RQ_OK;
+  if (get_scratch) {
+    ws = get_scratch();
+    if (!ws) return RQ_ERR_HIP;
+  }
   rq::GemvBatch b;
   memset(&b, 0, sizeof(b));
   fill_matrix(b.mat[0], w, x, y);
@@ -181,6 +214,7 @@ const char* rq_status_str(int status) {
     case RQ_ERR_RANGE: return "scale overflows its storage type";
     case RQ_ERR_HIP: return "HIP runtime error";
     case RQ_ERR_ALIAS: return "output overlaps an input";
+    case RQ_ERR_SCRATCH: return "needs more than the static scratch of rq_gemm_small_m_noalloc";
   }
   return "unknown status";
 }
@@ -373,6 +407,17 @@ int rq_gemm_int8_acc(const int8_t* xq, int64_t m, const rq_qweight* w, int32_t* 
 }
 
 size_t rq_workspace_bytes(void) { return rq::kWorkspaceBytes; }
+
+int rq_gemm_small_m_noalloc(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y,
+                            int64_t ldy, void* stream) {
+  if (!w) return RQ_ERR_NULL;
+  // every launch shape of this product keeps its partial sums within the
+  // scratch: at most 16 K slices of 16-row tiles, each tile 1 KiB per
+  // 16 activation rows (so the plan equals that of a full workspace)
+  const int64_t mt = m <= 16 ? 1 : 2;
+  if (w->n > 0 && 16 * ((w->n + 15) / 16) * mt * 1024 > (int64_t)kScratchBytes) return RQ_ERR_SCRATCH;
+  return small_m(x, m, ldx, w, y, ldy, nullptr, kScratchBytes, stream, 0, 0, scratch_address);
+}
 
 int rq_host_convert(int kind, const double* in, void* out, int64_t count) {
   if (!in || !out) return RQ_ERR_NULL;

@@ -23,6 +23,7 @@ RQ_ERR_NONFINITE = -5
 RQ_ERR_RANGE = -6
 RQ_ERR_HIP = -7
 RQ_ERR_ALIAS = -8
+RQ_ERR_SCRATCH = -9
 
 RQ_W8_SYM = 1
 RQ_W4_SYM = 2
@@ -40,7 +41,7 @@ EXPORTS = (
     "rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16", "rq_gemv_w8g32",
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
-    "rq_gemm_w4", "rq_quantize_aw", "rq_workspace_bytes",
+    "rq_gemm_w4", "rq_quantize_aw", "rq_workspace_bytes", "rq_gemm_small_m_noalloc",
 )
 
 
@@ -82,6 +83,7 @@ def lib():
             "rq_gemm_int8": ([vp, vp, i64, qp, vp, i64, vp, sz, vp], i32),
             "rq_gemm_int8_acc": ([vp, i64, qp, vp, vp, sz, vp], i32),
             "rq_workspace_bytes": ([], sz),
+            "rq_gemm_small_m_noalloc": ([vp, i64, i64, qp, vp, i64, vp], i32),
             "rq_host_convert": ([i32, vp, vp, i64], i32),
         }
         for name in ("rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16",
@@ -269,6 +271,14 @@ def rq_gemm_small_m(x, m, ldx, w, y, ldy, stream=None, ws=None):
     d = w.desc()
     st = lib().rq_gemm_small_m(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_small_m")
+    return y
+
+
+def rq_gemm_small_m_noalloc(x, m, ldx, w, y, ldy, stream=None):
+    """rq_gemm_small_m with the library's static scratch (allocates nothing)."""
+    d = w.desc()
+    st = lib().rq_gemm_small_m_noalloc(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, _stream(stream))
+    _check(st, "rq_gemm_small_m_noalloc")
     return y
 
 

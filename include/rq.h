@@ -74,7 +74,8 @@ enum rq_status {
   RQ_ERR_NONFINITE = -5, /* NaN or Inf in quantizer input                      */
   RQ_ERR_RANGE = -6,     /* a scale overflows its storage type                 */
   RQ_ERR_HIP = -7,       /* a HIP runtime call failed                          */
-  RQ_ERR_ALIAS = -8      /* an output overlaps an input                        */
+  RQ_ERR_ALIAS = -8,     /* an output overlaps an input                        */
+  RQ_ERR_SCRATCH = -9    /* too large for rq_gemm_small_m_noalloc's scratch    */
 };
 
 /*
@@ -254,6 +255,20 @@ int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *works
  * 8192 at m > 16 and 16384 at m = 4..8).  Other formats take any shape. */
 int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w,
                     uint16_t *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream);
+
+/* rq_gemm_small_m for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, formats and results as
+ * rq_gemm_small_m given a workspace of rq_workspace_bytes() (the same launch
+ * shape, so the same bits).  Its K-split partial sums use a static device
+ * array of 8 MiB per GPU, owned by the library and held until the process
+ * ends; a call allocates nothing.  Limit: 16 * ceil(n / 16) * t * 1024 bytes
+ * must fit in 8 MiB, t = 1 for m <= 16 and 2 above (n <= 4096 at any m,
+ * n <= 8192 at m <= 16); larger calls return RQ_ERR_SCRATCH.  Every call on
+ * a GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (different streams, or graph replays running concurrently) race. */
+int rq_gemm_small_m_noalloc(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w,
+                            uint16_t *y, int64_t ldy, void *stream);
 
 /* Prefill products on int4 codes for any number of rows m (the tensor-core
  * GEMM member of the int4 family in the model card's summary), on MFMA:

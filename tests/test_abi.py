@@ -42,7 +42,7 @@ def test_version_and_status_strings():
     L = rq.lib()
     assert L.rq_abi_version() == 2
     assert rq.rq_workspace_bytes() == 64 << 20
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert rq.status_str(st) and rq.status_str(st) != "unknown status"
     assert rq.status_str(-99) == "unknown status"
 
@@ -298,3 +298,16 @@ def test_workspace_validation():
     # empty extents with a workspace return before any launch
     rq.rq_gemm_small_m(x, 0, 128, w, y, 32, ws=(W, 1 << 20))
     rq.rq_gemm_small_m(x, 1, 128, _w(n=0), y, 32, ws=False)
+
+
+def test_noalloc_limits():
+    """rq_gemm_small_m_noalloc refuses products whose partial sums could
+    exceed its 8 MiB scratch, before any device call."""
+    x = A + 0x200000
+    assert _status(rq.rq_gemm_small_m_noalloc, x, 17, 128, _w(n=4112), C, 4112) == rq.RQ_ERR_SCRATCH
+    assert _status(rq.rq_gemm_small_m_noalloc, x, 1, 128, _w(n=8208), C, 8208) == rq.RQ_ERR_SCRATCH
+    assert _status(rq.rq_gemm_small_m_noalloc, x, 1, 128, _w(codes=0), C, 32) == rq.RQ_ERR_NULL
+    assert rq.lib().rq_gemm_small_m_noalloc(x, 1, 128, None, C, 32, None) == rq.RQ_ERR_NULL
+    # within the limit, validation still applies
+    assert _status(rq.rq_gemm_small_m_noalloc, x, 33, 128, _w(), C, 32) == rq.RQ_ERR_SHAPE
+    rq.rq_gemm_small_m_noalloc(x, 0, 128, _w(n=4096), C, 4096)       # empty: nothing to do
