@@ -1,16 +1,17 @@
 // Prefill products on int4 codes, any number of activation rows (the prefill
 // chunks of 64 to 1024 tokens):
 //   y[m][n] = fp16( sum_k x[m][k] * w[n][k] ),  accumulated in fp32, with
-//   w = fp16(q * s) on symmetric int4 group codes (groups of 16, 32 or 64),
-//   w = fma16(u, fp16(S_j), fp16(-M_j)) on asymmetric 256-superblocks.
+//   w = fp16(q * s) on symmetric int4 group codes (groups of 16, 32 or 64);
+//   on asymmetric 256-superblocks, per 32-group j,
+//   sum_k x w = S_j * sum_k x u - M_j * sum_k x, the two sums on MFMA (codes
+//   u are exact fp16 integers) and S_j, M_j applied in fp32.
 // This is the tensor-core GEMM member of the int4 product family ("RWKV-7 G1
 // 1.5B -- int4 GPTQ for rwkv-sglang" model card, summary), here on gfx950
 // MFMA; the weights are read as codes and dequantized in registers, never
 // written out.  Beyond fp32 summation: symmetric, q * s is rounded once to
-// fp16 (q has 3 significant bits, s 11), at most 2^-12 of each weight;
-// superblocks, S_j and M_j (exact in fp32) are each rounded to fp16 and the
-// fp16 fma rounds once more, so each weight is off by at most about
-// 2^-12 (15 S_j + 2 M_j).
+// fp16 (q has 3 significant bits, s 11), at most 2^-11 of each weight (one
+// fp16 rounding); superblocks, nothing is rounded below fp32 (S_j, M_j and the
+// products x u are exact; the MFMA sums and the two scalings round in fp32).
 //
 // A workgroup of NW waves (4 or 8) computes a BM x BN output tile; the waves
 // form a WM x (NW / WM) grid and each computes its (BM / WM) x (BN WM / NW)
@@ -46,6 +47,18 @@
 #include "kernels.h"
 
 namespace rq {
+
+// lane exchanges (v_permlane32_swap / v_permlane16_swap) for the word transpose
+__device__ __forceinline__ void swap32w(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap16w(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
 
 template <bool SB, int G, int BM, int BN, int WM, int NW>
 __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kbs, float* __restrict__ part) {
@@ -172,41 +185,79 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
     const uint8_t* xs = (const uint8_t*)lds4 + st * STAGE;
     const uint8_t* cs = xs + SX;
     const uint8_t* ss = xs + SX + SC;
-    uint4 cw[TN];
-    half8 s01[TN], s23[TN];  // the lane's scale for steps 0-1 and 2-3, broadcast
-    half8 mneg[TN];          // superblocks: -M_j, broadcast
+    if constexpr (SB) {
+      // superblocks: a 4 x 4 word transpose across the lane quarters gives
+      // lane q word q of each of the block's four 32-groups, so k step s
+      // covers group s alone; its MFMA result is scaled by S_s and corrected
+      // by -M_s times the activations' sum over the group, both in fp32
+      // (S_s = d sc_s and M_s = dmin mc_s are exact in fp32)
+      uint32_t wv[TN][4];
+      float sc[TN][4], mn[TN][4];
 #pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const int row = wn * (BN / WN) + 16 * b + r16;
-      cw[b] = *(const uint4*)(cs + row * 64 + ((q ^ ((row >> 2) & 3)) << 4));
-      if constexpr (SB) {
-        // group j = (block % 2) * 4 + q of the superblock: S_j = d sc_j and
-        // M_j = dmin mc_j (exact in fp32), each rounded once to fp16
+      for (int b = 0; b < TN; ++b) {
+        const int row = wn * (BN / WN) + 16 * b + r16;
+        const uint4 c4 = *(const uint4*)(cs + row * 64 + ((q ^ ((row >> 2) & 3)) << 4));
+        uint32_t w0 = c4.x, w1 = c4.y, w2 = c4.z, w3 = c4.w;
+        swap32w(w0, w2);
+        swap32w(w1, w3);
+        swap16w(w0, w1);
+        swap16w(w2, w3);
+        wv[b][0] = w0;
+        wv[b][1] = w1;
+        wv[b][2] = w2;
+        wv[b][3] = w3;
         const float d = f16_bits_to_f32(*(const uint16_t*)(ss + row * 4));
         const float dm = f16_bits_to_f32(*(const uint16_t*)(ss + BN * 4 + row * 4));
         const uint4 sub = *(const uint4*)(ss + BN * 8 + row * 16);
         const uint64_t lo48 = (uint64_t)sub.x | ((uint64_t)(sub.y & 0xffffu) << 32);
         const uint64_t hi48 = (uint64_t)(sub.y >> 16) | ((uint64_t)sub.z << 16);
-        const int g = ((kb0 + j) & 1) * 4 + q;
-        const _Float16 sh = (_Float16)(d * (float)((uint32_t)(lo48 >> (6 * g)) & 63u));
-        const _Float16 mh = (_Float16)(-(dm * (float)((uint32_t)(hi48 >> (6 * g)) & 63u)));
-        s01[b] = half8{sh, sh, sh, sh, sh, sh, sh, sh};
-        s23[b] = s01[b];
-        mneg[b] = half8{mh, mh, mh, mh, mh, mh, mh, mh};
-      } else {
-        // group of k = 32 q + 8 s within the block: g64 -> q / 2, g32 -> q, g16 -> 2 q + s / 2
-        _Float16 lo, hi;
-        if constexpr (G == 16) {
-          const half2v v = *(const half2v*)(ss + row * 16 + q * 4);
-          lo = v[0];
-          hi = v[1];
-        } else {
-          lo = *(const _Float16*)(ss + row * 4 * D + (G == 64 ? (q >> 1) : q) * 2);
-          hi = lo;
+        const int g0 = ((kb0 + j) & 1) * 4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          sc[b][s] = d * (float)((uint32_t)(lo48 >> (6 * (g0 + s))) & 63u);
+          mn[b][s] = dm * (float)((uint32_t)(hi48 >> (6 * (g0 + s))) & 63u);
         }
-        s01[b] = half8{lo, lo, lo, lo, lo, lo, lo, lo};
-        s23[b] = half8{hi, hi, hi, hi, hi, hi, hi, hi};
       }
+      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+      const float4v z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        half8 bf[TN];
+#pragma unroll
+        for (int b = 0; b < TN; ++b) bf[b] = dec4n<false>(wv[b][s]);
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+          const int row = wm * (BM / WM) + 16 * a + r16;
+          const half8 af = *(const half8*)(xs + row * 256 + (((4 * s + q) ^ (row & 15)) << 4));
+          const float4v xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, ones, z, 0, 0, 0);
+#pragma unroll
+          for (int b = 0; b < TN; ++b) {
+            const float4v r = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b], z, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[a][b][i] += sc[b][s] * r[i] - mn[b][s] * xsum[i];
+          }
+        }
+      }
+      return;
+    }
+    uint4 cw[TN];
+    half8 s01[TN], s23[TN];  // the lane's scale for steps 0-1 and 2-3, broadcast
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      const int row = wn * (BN / WN) + 16 * b + r16;
+      cw[b] = *(const uint4*)(cs + row * 64 + ((q ^ ((row >> 2) & 3)) << 4));
+      // group of k = 32 q + 8 s within the block: g64 -> q / 2, g32 -> q, g16 -> 2 q + s / 2
+      _Float16 lo, hi;
+      if constexpr (G == 16) {
+        const half2v v = *(const half2v*)(ss + row * 16 + q * 4);
+        lo = v[0];
+        hi = v[1];
+      } else {
+        lo = *(const _Float16*)(ss + row * 4 * D + (G == 64 ? (q >> 1) : q) * 2);
+        hi = lo;
+      }
+      s01[b] = half8{lo, lo, lo, lo, lo, lo, lo, lo};
+      s23[b] = half8{hi, hi, hi, hi, hi, hi, hi, hi};
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -214,10 +265,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         const uint32_t w = s == 0 ? cw[b].x : (s == 1 ? cw[b].y : (s == 2 ? cw[b].z : cw[b].w));
-        if constexpr (SB)
-          bf[b] = dec4n<false>(w) * s01[b] + mneg[b];
-        else
-          bf[b] = dec4n<true>(w) * (s < 2 ? s01[b] : s23[b]);
+        bf[b] = dec4n<true>(w) * (s < 2 ? s01[b] : s23[b]);
       }
 #pragma unroll
       for (int a = 0; a < TM; ++a) {

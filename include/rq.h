@@ -272,10 +272,11 @@ int rq_gemm_small_m_noalloc(const uint16_t *x, int64_t m, int64_t ldx, const rq_
 
 /* Prefill products on int4 codes for any number of rows m (the tensor-core
  * GEMM member of the int4 family in the model card's summary), on MFMA:
- * y[m][n] = fp16(sum_k x[m][k] * w[n][k]) with fp32 accumulation and the
- * weight dequantized to fp16 in registers: w = fp16(q * s) for RQ_W4_SYM
- * (group 16, 32 or 64; k % 128 == 0), at most 2^-12 of the weight off;
- * w = fma16(u, fp16(S_j), fp16(-M_j)) for RQ_W4_ASYM_SB256.  Other formats:
+ * y[m][n] = fp16(sum_k x[m][k] * w[n][k]) with fp32 accumulation.  RQ_W4_SYM
+ * (group 16, 32 or 64; k % 128 == 0): the weight is dequantized to fp16 in
+ * registers, w = fp16(q * s), at most 2^-11 of the weight off (one rounding);
+ * RQ_W4_ASYM_SB256: per 32-group, S_j * sum(x u) - M_j * sum(x) with both sums
+ * on MFMA and S_j, M_j applied in fp32, nothing rounded below fp32.  Other formats:
  * RQ_ERR_FORMAT.  x: fp16 [m][ldx], ldx >= k, ldx % 8 == 0; y: fp16
  * [m][ldy], ldy >= n.  The weights are read once per tile row of 64 or 128
  * activation rows; meant for m from about 64 up (rq_gemm_small_m covers

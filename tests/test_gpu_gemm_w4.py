@@ -129,3 +129,28 @@ def test_gemm_w4_deterministic_and_empty():
     rq.rq_gemm_w4(dev_f16(x), 0, k, qw, y.ptr(), n)
     torch.cuda.synchronize()
     assert bool((y.buf == SENTINEL).all())
+
+
+def _sb256_adversarial(n, k, m, seed):
+    """Superblock weights with large offsets and near-cancelling values:
+    w ~ U(-2, 0.1)/sqrt(k) (each group's minimum sets M_j ~ 2/sqrt(k) while
+    S_j ~ M_j / 14), and zero weights on the 8 massive activation channels, so
+    their dequantized weights S_j q - M_j are near zero while x there is ~300."""
+    from gemm_rwkv_amd import synth
+    g = np.random.default_rng(seed)
+    w = (g.uniform(-2.0, 0.1, (n, k)) / np.sqrt(k)).astype(np.float32)
+    w[:, synth.massive_channels(k)] = 0.0
+    x = synth.act_massive(m, k, salt=seed)
+    return w, x
+
+
+@pytest.mark.parametrize("n,k,m", [(2560, 16384, 64), (2560, 16384, 16), (1000, 10240, 130)])
+def test_sb256_adversarial(n, k, m):
+    w, x = _sb256_adversarial(n, k, m, seed=n + m)
+    parts = quant.quantize(w, quant.W4_ASYM_SB256, 32)
+    qw = qweight_from_oracle(quant.W4_ASYM_SB256, 32, parts, n, k)
+    y = _run(qw, x, m, k, n)
+    y_ref, b = ref.weight_only_ref(x, quant.W4_ASYM_SB256, parts, 32)
+    ok, info = ref.compare(y, y_ref, b)
+    print("sb256 adversarial", n, k, m, info, flush=True)
+    assert ok, info
