@@ -270,11 +270,22 @@ def test_decode_layer_4096(layer_4096, m):
                       quant.W4_SYM, parts, 64, synth.MAT_NAMES[mat])
 
 
-@pytest.mark.parametrize("m", [1, 32])
-def test_head_4096x65536(m):
+@pytest.fixture(scope="module")
+def head_4096():
     n, k = 65536, 4096
     w = synth.weight(4, 61, synth.MAT_HEAD, n, k)
     qw = _gpu_weights(w, quant.F16, 0)
+    rows = _rows(n, 600)
+    parts = {"codes": w[rows].astype(np.float16)}
+    assert np.array_equal(host(qw.codes, np.uint16)[: n * k].reshape(n, k)[rows], parts["codes"].view(np.uint16))
+    yield qw, rows, parts
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
+def test_head_4096x65536(head_4096, m):
+    n, k = 65536, 4096
+    qw, rows, parts = head_4096
     x = synth.act_normal(m, k, 4, salt=2)
     y = torch.empty(m * n * 2, dtype=torch.uint8, device="cuda")
     say("head m", m)
@@ -283,10 +294,74 @@ def test_head_4096x65536(m):
     else:
         rq.rq_gemm_small_m(dev_f16(x), m, k, qw, y, n)
     torch.cuda.synchronize()
-    rows = _rows(n, 600)
-    parts = {"codes": w[rows].astype(np.float16)}
-    assert np.array_equal(host(qw.codes, np.uint16)[: n * k].reshape(n, k)[rows], parts["codes"].view(np.uint16))
     _compare_rows(host(y, np.float16).reshape(m, n), rows, x, quant.F16, parts, 0, "head")
+
+
+# --------------------------------------------------------------------------
+# a reduced 13.3B decode step in one graph: two width-4096 layers and the
+# head, launched as the benchmark's sweep launches them (fused R/K/V, O, cmix
+# key, cmix value per layer, then the head), captured once per M, replayed,
+# and checked on sampled rows of every output
+# --------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def step_4096(layer_4096, head_4096):
+    c, mats = layer_4096
+    second = {}
+    for mat, n, k in synth.layer_shapes(c):
+        w = synth.weight(4, 59, mat, n, k)
+        second[mat] = (w, _gpu_weights(w, quant.W4_SYM, 64))
+    yield c, [mats, second], head_4096
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
+def test_step_graph_4096(step_4096, m):
+    c, layers, (qh, hrows, hparts) = step_4096
+    x = synth.act_normal(m, c, 4, salt=3)
+    x4 = synth.act_normal(m, 4 * c, 4, salt=4)
+    xd, x4d = dev_f16(x), dev_f16(x4)
+    shapes = synth.layer_shapes(c)
+    ys = [{mat: torch.zeros(m * n, dtype=torch.int16, device="cuda") for mat, n, _ in shapes} for _ in layers]
+    yh = torch.zeros(m * 65536, dtype=torch.int16, device="cuda")
+
+    def step():
+        for li, mats in enumerate(layers):
+            q = {mat: mats[mat][1] for mat in mats}
+            y = ys[li]
+            rq.rq_fused_rkv(xd, xd, xd, m, c, q[synth.MAT_R], q[synth.MAT_K], q[synth.MAT_V],
+                            y[synth.MAT_R], y[synth.MAT_K], y[synth.MAT_V], c)
+            rq.rq_gemm_small_m(xd, m, c, q[synth.MAT_O], y[synth.MAT_O], c)
+            rq.rq_gemm_small_m(xd, m, c, q[synth.MAT_KEY], y[synth.MAT_KEY], 4 * c)
+            rq.rq_gemm_small_m(x4d, m, 4 * c, q[synth.MAT_VALUE], y[synth.MAT_VALUE], c)
+        rq.rq_gemm_small_m(xd, m, c, qh, yh, 65536)
+
+    rq.default_workspace()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("step graph 4096 capture m", m)
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for y in ys:
+            for t in y.values():
+                t.fill_(-1)
+        yh.fill_(-1)
+        torch.cuda.synchronize()
+        say("step graph 4096 replay m", m, rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for li, mats in enumerate(layers):
+            for mat, n, k in shapes:
+                rows = _rows(n, 900 + 10 * li + mat + m)
+                parts = _check_rows_sym(mats[mat][1], mats[mat][0], rows, quant.W4_SYM, 64)
+                _compare_rows(host(ys[li][mat], np.float16).reshape(m, n), rows, x4 if k == 4 * c else x,
+                              quant.W4_SYM, parts, 64, (li, synth.MAT_NAMES[mat], rep))
+        _compare_rows(host(yh, np.float16).reshape(m, 65536), hrows, x, quant.F16, hparts, 0, ("head", rep))
+    del g
 
 
 @pytest.mark.parametrize("fmt,group,n,k,mat", [(quant.W4_SYM, 64, 4096, 4096, synth.MAT_O),

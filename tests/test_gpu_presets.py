@@ -1,7 +1,7 @@
 """One 2.9B-shape layer (width 2560) and the head under each rwkv-quant preset
 (gemm_rwkv_amd.presets): weights quantized on the GPU in the preset's format
 per tensor, then the decode launches bench.py's preset sweep times (fused
-R/K/V, O, cmix key, cmix value, head) at M = 4.  Sampled rows of every
+R/K/V, O, cmix key, cmix value, head) at the sweep's M = 1, 4 and 16.  Sampled rows of every
 quantized tensor are checked byte for byte against the oracle, and their
 outputs against the oracle's product."""
 
@@ -16,7 +16,7 @@ from oracle import quant, ref
 
 pytestmark = pytest.mark.gpu
 
-C, VOCAB, M = 2560, 65536, 4
+C, VOCAB = 2560, 65536
 SHAPES = {"r": (C, C), "k": (C, C), "v": (C, C), "o": (C, C), "cmix_key": (4 * C, C),
           "cmix_value": (C, 4 * C), "head": (VOCAB, C)}
 MAT = {"r": synth.MAT_R, "k": synth.MAT_K, "v": synth.MAT_V, "o": synth.MAT_O, "cmix_key": synth.MAT_KEY,
@@ -36,16 +36,21 @@ def _check(qw, w, fmt, group, rows, x, y):
     assert ok, info
 
 
+@pytest.fixture(scope="module")
+def weights_2560():
+    return {t: synth.weight(2, 0, MAT[t], *SHAPES[t]) for t in presets.TENSORS}
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
 @pytest.mark.parametrize("preset,bf16_o0", [("REDUCTION", False), ("COMPRESSION", False),
                                             ("COMPRESSION", True)])
-def test_preset_layer_and_head(preset, bf16_o0):
+def test_preset_layer_and_head(weights_2560, preset, bf16_o0, M):
     x = synth.act_massive(M, C, cfg=2, salt=1)
     x4 = synth.act_massive(M, 4 * C, cfg=2, salt=2)
     xd, x4d = dev_f16(x), dev_f16(x4)
-    ws, qws, ys = {}, {}, {}
+    ws, qws, ys = weights_2560, {}, {}
     for t in presets.TENSORS:
         n, k = SHAPES[t]
-        ws[t] = synth.weight(2, 0, MAT[t], n, k)
         fmt, group = presets.scheme(preset, t, 0, bf16_o0)
         say("preset", preset, bf16_o0, t, fmt, group, n, k)
         qws[t] = rq.quantize(dev_f32(ws[t]), fmt, group)
