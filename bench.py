@@ -72,19 +72,21 @@ def capture(fn):
     return g
 
 
-def time_graph(g, reps, warmup=2):
-    """Mean ms per replay, HIP events on the current stream (where the graph runs)."""
+def time_graph(g, reps, warmup=2, launches=1):
+    """Median ms per replay over at least `reps` replays and at least 200
+    dispatches (`launches` per replay); HIP events on the current stream,
+    where the graph runs, around each replay."""
+    reps = max(reps, -(-200 // max(launches, 1)))
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
 
 
 class Decode:
@@ -252,10 +254,118 @@ class Sweep:
         out = {}
         for m in (1, 2, 4, 8, 16, 32):
             g = capture(lambda m=m: self.step(m))
-            ms = time_graph(g, steps, warmup)
+            ms = time_graph(g, steps, warmup, launches=4 * self.LAYERS + 1)
             out[str(m)] = {"ms": round(ms, 4), "GB_s": round(self.weight_bytes / (ms * 1e-3) / 1e9, 1)}
             del g
         return out
+
+
+class Ceiling:
+    """The measured read ceiling: rq_stream_read (16-byte non-temporal loads
+    over every compute unit) over a 4 GiB buffer, and over slices of it the
+    size of one product's weights, launched back to back in a graph over
+    distinct slices (as the products' classes rotate weight copies)."""
+
+    BYTES = 4 << 30
+
+    def __init__(self, dev):
+        self.buf = torch.empty(self.BYTES, dtype=torch.uint8, device=dev)
+        self.buf.fill_(1)
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        g = capture(lambda: rq.rq_stream_read(self.buf, self.BYTES, self.sink))
+        self.ms = time_graph(g, 20, launches=1)
+        self.gbs = self.BYTES / (self.ms * 1e-3) / 1e9
+
+    def per_launch_us(self, nbytes, launches=61):
+        """Median per-launch time of a plain read of nbytes (16-byte multiple)."""
+        nb = nbytes // 256 * 256
+        slots = max(1, self.BYTES // nb)
+        views = [self.buf[(i % slots) * nb:(i % slots) * nb + nb] for i in range(launches)]
+        g = capture(lambda: [rq.rq_stream_read(v, nb, self.sink) for v in views])
+        return time_graph(g, 5, launches=launches) * 1e3 / launches
+
+
+def class_row(us, wbytes, ceiling, read_us=None):
+    gbs = wbytes / us / 1e3
+    out = {"us": round(us, 3), "weight_bytes": int(wbytes), "GB_s": round(gbs, 1),
+           "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "ceiling_frac": round(gbs / ceiling.gbs, 4)}
+    if read_us is not None:
+        out["plain_read_us"] = round(read_us, 3)
+        out["vs_plain_read"] = round(us / read_us, 3)
+    return out
+
+
+def sweep_classes(sw, ceiling, m=1):
+    """Per-launch time of each launch class of the 13.3B step at M = m, each
+    in a graph over the 61 layers' weights (the head alone: 537 MB, beyond the
+    256 MB last-level cache), beside a plain read of the same bytes; and the
+    sum over the step's 245 launches of those per-launch times."""
+    c = sw.C
+    x = f16_dev(synth.act_normal(m, c, 4), "cuda")
+    x4 = f16_dev(synth.act_normal(m, 4 * c, 4, salt=1), "cuda")
+    y = {nm: torch.empty(m * n, dtype=torch.int16, device="cuda")
+         for nm, n in (("r", c), ("k", c), ("v", c), ("o", c), ("key", 4 * c), ("val", c), ("head", sw.VOCAB))}
+    L = sw.layers
+    kinds = [
+        ("fused R/K/V 3x4096x4096", lambda s: rq.rq_fused_rkv(x, x, x, m, c, s[synth.MAT_R], s[synth.MAT_K],
+                                                              s[synth.MAT_V], y["r"], y["k"], y["v"], c),
+         sum(L[0][t].nbytes() for t in (synth.MAT_R, synth.MAT_K, synth.MAT_V))),
+        ("O 4096x4096", lambda s: rq.rq_gemm_small_m(x, m, c, s[synth.MAT_O], y["o"], c), L[0][synth.MAT_O].nbytes()),
+        ("cmix key 16384x4096", lambda s: rq.rq_gemm_small_m(x, m, c, s[synth.MAT_KEY], y["key"], 4 * c),
+         L[0][synth.MAT_KEY].nbytes()),
+        ("cmix value 4096x16384", lambda s: rq.rq_gemm_small_m(x4, m, 4 * c, s[synth.MAT_VALUE], y["val"], c),
+         L[0][synth.MAT_VALUE].nbytes()),
+    ]
+    out = {}
+    step_ms = 0.0
+    for name, fn, wb in kinds:
+        g = capture(lambda fn=fn: [fn(s) for s in L])
+        us = time_graph(g, 5, launches=len(L)) * 1e3 / len(L)
+        del g
+        out[name] = class_row(us, wb, ceiling, ceiling.per_launch_us(wb))
+        step_ms += len(L) * us * 1e-3
+    g = capture(lambda: rq.rq_gemm_small_m(x, m, c, sw.head, y["head"], sw.VOCAB))
+    us = time_graph(g, 5, launches=1) * 1e3
+    del g
+    out["head 65536x4096"] = class_row(us, sw.head.nbytes(), ceiling, ceiling.per_launch_us(sw.head.nbytes(), 8))
+    step_ms += us * 1e-3
+    return out, step_ms
+
+
+def w8_rows(gen, dev, ceiling, copies=5):
+    """The int8 tier (w8g64) of the 13.3B shapes at M = 1: each class over
+    `copies` layers of distinct weights (1 GB), per-launch time beside a plain
+    read of the same bytes."""
+    c, m = 4096, 1
+    layers = []
+    for _ in range(copies):
+        s = {}
+        for mat, n, k in synth.layer_shapes(c):
+            wf = torch.randn(n, k, generator=gen, device=dev, dtype=torch.float32) * (1.0 / k ** 0.5)
+            s[mat] = rq.quantize(wf, rq.RQ_W8_SYM, 64)
+            del wf
+        layers.append(s)
+    torch.cuda.empty_cache()
+    x = f16_dev(synth.act_normal(m, c, 4), dev)
+    x4 = f16_dev(synth.act_normal(m, 4 * c, 4, salt=1), dev)
+    y = torch.empty(4 * c * 3, dtype=torch.int16, device=dev)
+    yv = [y[i * c:(i + 1) * c] for i in range(3)]
+    out = {}
+    for name, fn, mats in (
+            ("fused R/K/V 3x4096x4096", lambda s: rq.rq_fused_rkv(x, x, x, m, c, s[synth.MAT_R], s[synth.MAT_K],
+                                                                  s[synth.MAT_V], yv[0], yv[1], yv[2], c),
+             (synth.MAT_R, synth.MAT_K, synth.MAT_V)),
+            ("O 4096x4096", lambda s: rq.rq_gemv_w8g64(x, s[synth.MAT_O], y), (synth.MAT_O,)),
+            ("cmix key 16384x4096", lambda s: rq.rq_gemv_w8g64(x, s[synth.MAT_KEY], y), (synth.MAT_KEY,)),
+            ("cmix value 4096x16384", lambda s: rq.rq_gemv_w8g64(x4, s[synth.MAT_VALUE], y), (synth.MAT_VALUE,))):
+        g = capture(lambda fn=fn: [fn(s) for s in layers])
+        us = time_graph(g, 20, launches=len(layers)) * 1e3 / len(layers)
+        del g
+        wb = sum(layers[0][t].nbytes() for t in mats)
+        out[name] = class_row(us, wb, ceiling, ceiling.per_launch_us(wb, 20))
+    del layers
+    torch.cuda.empty_cache()
+    return out
 
 
 def _w4_gemm_rows(gen, dev, c, fmt, group, ms, label, graph_us):
@@ -359,7 +469,7 @@ class PresetSweep:
             per_m = {}
             for m in (1, 4, 16):
                 g = capture(lambda m=m: self.step(name, b16, m))
-                ms = time_graph(g, steps, warmup)
+                ms = time_graph(g, steps, warmup, launches=129)
                 per_m[str(m)] = {"ms": round(ms, 4), "GB_s": round(wb / (ms * 1e-3) / 1e9, 1)}
                 del g
             out[label] = {"weight_bytes": wb, "per_m": per_m}
@@ -376,7 +486,7 @@ def measure_rows(gen, dev, reps=20):
 
     def graph_us(fn, n):
         g = capture(fn)
-        return time_graph(g, reps) * 1e3 / n
+        return time_graph(g, reps, launches=n) * 1e3 / n
 
     # quantizers: fp32 bytes read per second
     for name, fmt, group, (n, k) in (("rtn w4g64 8192x2048", rq.RQ_W4_SYM, 64, (8192, 2048)),
@@ -514,12 +624,12 @@ def measure_classes(dec, pre, reps):
     for m in MS:
         for name, fn, wbytes, per_step in dec.classes(m):
             g = class_graph(fn, dec.sets)
-            ms = time_graph(g, reps) / len(dec.sets)
+            ms = time_graph(g, reps, launches=len(dec.sets)) / len(dec.sets)
             rows.append({"name": name, "ms": ms, "weight_bytes": wbytes, "per_step": per_step, "flops": 0.0,
                          "m": m, "graph": g, "launches": len(dec.sets)})
     for name, fn, wbytes, per_step, flops in pre.classes():
         g = class_graph(fn, pre.sets)
-        ms = time_graph(g, reps) / len(pre.sets)
+        ms = time_graph(g, reps, launches=len(pre.sets)) / len(pre.sets)
         rows.append({"name": name, "ms": ms, "weight_bytes": wbytes, "per_step": per_step, "flops": flops,
                      "m": pre.m, "graph": g, "launches": len(pre.sets)})
     return rows
@@ -717,15 +827,21 @@ def sources_hash(name):
     return h.hexdigest()
 
 
-def cpu_baseline(c, budget_s=20.0):
-    """The oracle (RTN quantize, dequantize, fp64 product) on host cores over a
-    bounded sample of the decode step: whole width-c layers at M = 1, 8, 32."""
-    from oracle import quant, ref
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count()
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_pass(c, budget_s):
+    """Whole width-c layers through the oracle at M = 1, 8, 32 until budget_s
+    is spent: (packed weight bytes of the passes, seconds, layers)."""
+    from oracle import quant, ref
     xs = {m: synth.act_channel_1202(m, c) for m in MS}
     x4 = {m: synth.act_normal(m, 4 * c, 1) for m in MS}
     t0 = time.perf_counter()
@@ -742,11 +858,33 @@ def cpu_baseline(c, budget_s=20.0):
         layers += 1
         if time.perf_counter() - t0 > budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d layer(s) of the width-%d int4 g64 set (6 matrices) through the oracle's RTN "
-                      "quantizer, dequantization and fp64 product at M=1,8,32: %.1f s; value = packed "
-                      "weight bytes of the decode passes / time" % (layers, c, dt)}
+    return nbytes, time.perf_counter() - t0, layers
+
+
+def cpu_baseline(c, budget_s=12.0):
+    """The oracle (RTN quantize, dequantize, fp64 product) on host cores over a
+    bounded sample of the decode step: whole width-c layers at M = 1, 8, 32,
+    once with the BLAS threads numpy has and once on one thread."""
+    threads = os.cpu_count()
+    limits = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        limits = threadpool_limits
+    except Exception:  # noqa: BLE001
+        pass
+    nb, dt, layers = _oracle_pass(c, budget_s)
+    out = {"value": round(nb / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": "%d layer(s) of the width-%d int4 g64 set (6 matrices) through the oracle's RTN "
+                     "quantizer, dequantization and fp64 product at M=1,8,32: %.1f s; value = packed "
+                     "weight bytes of the decode passes / time" % (layers, c, dt),
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+    if limits is not None:
+        with limits(limits=1):
+            nb1, dt1, layers1 = _oracle_pass(c, budget_s)
+        out["single_thread"] = {"value": round(nb1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "sample": "%d layer(s), %.1f s, BLAS limited to one thread" % (layers1, dt1)}
+    return out
 
 
 def main():
@@ -819,6 +957,7 @@ def main():
         r["alg_bytes"] = alg_bytes(r, C1, C3, M3)
     dom = max(rows, key=lambda r: r["ms"] * r["per_step"])
     traffic = stored_traffic(dom["name"])
+    ceiling = Ceiling(dev)
     if args.phases:
         for name, t in zip(["decode M=%d" % m for m in MS] + ["prefill fp8 M=%d" % M3], per):
             print("%-22s %8.3f ms" % (name, t), file=sys.stderr)
@@ -842,16 +981,30 @@ def main():
         "fp8_gemm_m256": {"tflops": round(fp8_tflops, 1), "frac_of_peak": round(fp8_tflops / FP8_PEAK_TFLOPS, 4),
                           "pass_ms": round(float(per[-1]), 4)},
         "roofline": roofline(dom, traffic),
+        "hbm_ceiling": {"GB_s": round(ceiling.gbs, 1), "bytes": Ceiling.BYTES, "ms": round(ceiling.ms, 4),
+                        "peak_frac": round(ceiling.gbs / HBM_PEAK_GBS, 4),
+                        "kernel": "rq_stream_read: 16-byte non-temporal loads, 8 per thread per step, "
+                                  "grid-stride over all compute units"},
     }
+    out["config"]["ceiling_frac"] = round(value / ceiling.gbs, 4)
+    if out["roofline"]["unit"] == "GB/s":
+        out["roofline"]["ceiling_frac"] = round(out["roofline"]["achieved"] / ceiling.gbs, 4)
     if not args.no_sweep:
         del graphs, rows
         torch.cuda.empty_cache()
         sw = Sweep(gen, dev)
         res = sw.run(max(3, args.steps // 2), 2)
+        cls, sum_ms = sweep_classes(sw, ceiling)
         out["sweep_13b"] = {"workload": "61 x (fused R/K/V, O, cmix key, cmix value) int4 g64 at width 4096 "
                                         "+ fp16 head 65536x4096, one graph of 245 launches per M",
                             "weight_bytes": sw.weight_bytes, "per_m": res,
-                            "m1_hbm_peak_frac": round(res["1"]["GB_s"] / HBM_PEAK_GBS, 4)}
+                            "m1_hbm_peak_frac": round(res["1"]["GB_s"] / HBM_PEAK_GBS, 4),
+                            "m1_ceiling_frac": round(res["1"]["GB_s"] / ceiling.gbs, 4),
+                            "m1_classes": cls,
+                            "m1_sum_of_class_launches_ms": round(sum_ms, 4)}
+        if args.phases:
+            for name, r in cls.items():
+                print("sweep M=1 %-26s %s" % (name, r), file=sys.stderr)
         if args.phases:
             for m, r in res.items():
                 print("sweep 13.3B M=%-2s %8.3f ms  %7.1f GB/s" % (m, r["ms"], r["GB_s"]), file=sys.stderr)
@@ -871,6 +1024,7 @@ def main():
     if not args.no_rows:
         torch.cuda.empty_cache()
         out["rows"] = measure_rows(gen, dev)
+        out["rows"]["w8g64 4096 layer M=1"] = w8_rows(gen, dev, ceiling)
         if args.phases:
             for name, r in out["rows"].items():
                 print("%-34s %s" % (name, r), file=sys.stderr)

@@ -408,6 +408,13 @@ int rq_gemm_int8_acc(const int8_t* xq, int64_t m, const rq_qweight* w, int32_t* 
 
 size_t rq_workspace_bytes(void) { return rq::kWorkspaceBytes; }
 
+int rq_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return RQ_ERR_NULL;
+  if (!rqv::aligned16(buf) || ((uintptr_t)sink & 3u)) return RQ_ERR_ALIGN;
+  if (bytes % 16 != 0) return RQ_ERR_SHAPE;
+  return hip_status(rq::launch_stream_read(buf, bytes, sink, S(stream)));
+}
+
 int rq_gemm_small_m_noalloc(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint16_t* y,
                             int64_t ldy, void* stream) {
   if (!w) return RQ_ERR_NULL;

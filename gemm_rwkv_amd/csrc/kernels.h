@@ -76,4 +76,7 @@ hipError_t launch_gemm_w8a8(const void* xq, const float* sx, int m, const void* 
                             int n, int k, bool fp8, uint16_t* y, int ldy, int32_t* acc_out, void* ws,
                             size_t ws_bytes, hipStream_t st);
 
+// ---- measurement aid (measure.hip) ------------------------------------------
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+
 }  // namespace rq

@@ -41,7 +41,7 @@ EXPORTS = (
     "rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16", "rq_gemv_w8g32",
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
-    "rq_gemm_w4", "rq_quantize_aw", "rq_workspace_bytes", "rq_gemm_small_m_noalloc",
+    "rq_gemm_w4", "rq_quantize_aw", "rq_workspace_bytes", "rq_gemm_small_m_noalloc", "rq_stream_read",
 )
 
 
@@ -84,6 +84,7 @@ def lib():
             "rq_gemm_int8_acc": ([vp, i64, qp, vp, vp, sz, vp], i32),
             "rq_workspace_bytes": ([], sz),
             "rq_gemm_small_m_noalloc": ([vp, i64, i64, qp, vp, i64, vp], i32),
+            "rq_stream_read": ([vp, sz, vp, vp], i32),
             "rq_host_convert": ([i32, vp, vp, i64], i32),
         }
         for name in ("rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16",
@@ -322,6 +323,11 @@ def rq_gemm_int8_acc(xq, m, w, acc, stream=None, ws=None):
     st = lib().rq_gemm_int8_acc(_ptr(xq), m, ctypes.byref(d), _ptr(acc), *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_int8_acc")
     return acc
+
+
+def rq_stream_read(buf, nbytes, sink, stream=None):
+    """Read-only stream over nbytes of the device buffer buf (measurement aid)."""
+    _check(lib().rq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "rq_stream_read")
 
 
 def rq_workspace_bytes():

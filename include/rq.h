@@ -323,6 +323,15 @@ int rq_gemm_int8(const int8_t *xq, const float *sx, int64_t m, const rq_qweight 
 int rq_gemm_int8_acc(const int8_t *xq, int64_t m, const rq_qweight *w, int32_t *acc,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Measurement aid: reads `bytes` of device memory at buf (16-byte aligned,
+ * bytes % 16 == 0) with 16-byte non-temporal loads spread over every compute
+ * unit and stores nothing but, at most, one word to *sink (device, 4-byte
+ * aligned).  A read-only stream: what the memory system delivers to a kernel
+ * that does nothing else, the ceiling the weight-streaming products are
+ * measured against beside the 8 TB/s peak.  Errors: RQ_ERR_NULL,
+ * RQ_ERR_ALIGN, RQ_ERR_SHAPE. */
+int rq_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Test aid: the library's own fp64 -> fp16 (kind 0, uint16 out), fp64 ->
  * fp32 (kind 1, uint32 out) and fp64 -> e4m3fn (kind 2, uint8 out)
  * round-to-nearest-even conversions, run on the host over `count` values of

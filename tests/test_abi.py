@@ -311,3 +311,11 @@ def test_noalloc_limits():
     # within the limit, validation still applies
     assert _status(rq.rq_gemm_small_m_noalloc, x, 33, 128, _w(), C, 32) == rq.RQ_ERR_SHAPE
     rq.rq_gemm_small_m_noalloc(x, 0, 128, _w(n=4096), C, 4096)       # empty: nothing to do
+
+
+def test_stream_read_validation():
+    assert rq.lib().rq_stream_read(None, 16, A, None) == rq.RQ_ERR_NULL
+    assert rq.lib().rq_stream_read(A, 16, None, None) == rq.RQ_ERR_NULL
+    assert rq.lib().rq_stream_read(A + 8, 16, B, None) == rq.RQ_ERR_ALIGN
+    assert rq.lib().rq_stream_read(A, 16, B + 2, None) == rq.RQ_ERR_ALIGN
+    assert rq.lib().rq_stream_read(A, 20, B, None) == rq.RQ_ERR_SHAPE
