@@ -130,7 +130,7 @@ def default_workspace(device=None):
         if torch.cuda.is_current_stream_capturing():
             raise RuntimeError("rq: allocate the default workspace before graph capture "
                                "(call gemm_rwkv_amd.rq.default_workspace() first)")
-        t = torch.empty(lib().rq_workspace_bytes(), dtype=torch.uint8, device=dev)
+        t = torch.zeros(lib().rq_workspace_bytes(), dtype=torch.uint8, device=dev)
         _default_ws[dev.index] = t
     return t
 

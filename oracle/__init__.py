@@ -14,6 +14,8 @@ What it computes, in fp64 unless a stored format says otherwise:
   activations.
 * ``ref``     -- dequantization, the fp64 product ``y = x_hat . w_hat^T``, its
   magnitude bound ``B = |x_hat| . |w_hat|^T`` and the pass/fail comparator.
+* ``proxy``   -- RWKVQuant's weights-only coarse-to-fine proxy (P_c, P_f) and
+  its SQ/VQ routing, with the readings its header lists.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against facts that do not
 come from the oracle itself (brute force, closed forms, exact round trips,
@@ -23,4 +25,4 @@ int4 symmetric range (codes -7..7, scale absmax/7) and the asymmetric
 superblock's two-level scale rule and sub-code packing.
 """
 
-from . import codecs, quant, ref  # noqa: F401
+from . import codecs, proxy, quant, ref  # noqa: F401
