@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librq.so")
 
-SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm_mfma.hip", "gemm_w4.hip", "measure.hip", "validate.cpp"]
+SOURCES = ["api.hip", "quant.hip", "gemv.hip", "gemm_mfma.hip", "gemm_w4.hip", "measure.hip", "validate.cpp",
+           "proxy.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -63,7 +64,7 @@ SANITIZED = os.path.join(BUILD, "sanitized", "librq.so")
 # host-side sanitizers only (device code is built as usual)
 SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
-HOST_SOURCES = ["api.hip", "validate.cpp"]
+HOST_SOURCES = ["api.hip", "validate.cpp", "proxy.cpp"]
 
 
 def build_sanitized(verbose=True):

@@ -215,6 +215,7 @@ const char* rq_status_str(int status) {
     case RQ_ERR_HIP: return "HIP runtime error";
     case RQ_ERR_ALIAS: return "output overlaps an input";
     case RQ_ERR_SCRATCH: return "needs more than the static scratch of rq_gemm_small_m_noalloc";
+    case RQ_ERR_DEGENERATE: return "every weight is equal: no gap to normalise";
   }
   return "unknown status";
 }

@@ -24,6 +24,8 @@ RQ_ERR_RANGE = -6
 RQ_ERR_HIP = -7
 RQ_ERR_ALIAS = -8
 RQ_ERR_SCRATCH = -9
+RQ_ERR_DEGENERATE = -10
+RQ_PROXY_MAX_K = 16
 
 RQ_W8_SYM = 1
 RQ_W4_SYM = 2
@@ -42,6 +44,7 @@ EXPORTS = (
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
     "rq_gemm_w4", "rq_quantize_aw", "rq_workspace_bytes", "rq_gemm_small_m_noalloc", "rq_stream_read",
+    "rq_proxy",
 )
 
 
@@ -85,6 +88,7 @@ def lib():
             "rq_workspace_bytes": ([], sz),
             "rq_gemm_small_m_noalloc": ([vp, i64, i64, qp, vp, i64, vp], i32),
             "rq_stream_read": ([vp, sz, vp, vp], i32),
+            "rq_proxy": ([vp, i64, i32, vp, vp, vp, vp], i32),
             "rq_host_convert": ([i32, vp, vp, i64], i32),
         }
         for name in ("rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16",
@@ -328,6 +332,34 @@ def rq_gemm_int8_acc(xq, m, w, acc, stream=None, ws=None):
 def rq_stream_read(buf, nbytes, sink, stream=None):
     """Read-only stream over nbytes of the device buffer buf (measurement aid)."""
     _check(lib().rq_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "rq_stream_read")
+
+
+def rq_proxy(w, K=4, v=None):
+    """RWKVQuant's coarse-to-fine proxy of one weight tensor on the host:
+    (P_c, P_f, [M_2..M_K]).  w: anything numpy can view as float32 (a CPU or
+    GPU tensor is copied to host memory first); v: K - 1 weights for
+    k = 2..K, None for 1/k!."""
+    import numpy as np
+    if isinstance(w, torch.Tensor):
+        w = w.detach().to("cpu", torch.float32).numpy()
+    a = np.ascontiguousarray(np.asarray(w, dtype=np.float32).ravel())
+    vv = None
+    if v is not None:
+        vv = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+        if vv.size != K - 1:
+            raise ValueError("v needs K - 1 weights (k = 2..K)")
+    pc, pf = ctypes.c_double(), ctypes.c_double()
+    mk = np.zeros(max(K - 1, 1), dtype=np.float64)
+    _check(lib().rq_proxy(a.ctypes.data, a.size, int(K), None if vv is None else vv.ctypes.data,
+                          ctypes.addressof(pc), ctypes.addressof(pf), mk.ctypes.data), "rq_proxy")
+    return pc.value, pf.value, mk[:K - 1]
+
+
+def proxy_route(pc, pf, tau_c=1.54, tau_f=30.0):
+    """The pages' routing: scalar quantization ("SQ") only when P_c < tau_c
+    and P_f < tau_f, else vector quantization ("VQ"); defaults are the
+    thresholds reported for RWKV-7."""
+    return "SQ" if (pc < tau_c and pf < tau_f) else "VQ"
 
 
 def rq_workspace_bytes():

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 2
+#define RQ_ABI_VERSION 3
 
 enum rq_status {
   RQ_OK = 0,
@@ -75,7 +75,8 @@ enum rq_status {
   RQ_ERR_RANGE = -6,     /* a scale overflows its storage type                 */
   RQ_ERR_HIP = -7,       /* a HIP runtime call failed                          */
   RQ_ERR_ALIAS = -8,     /* an output overlaps an input                        */
-  RQ_ERR_SCRATCH = -9    /* too large for rq_gemm_small_m_noalloc's scratch    */
+  RQ_ERR_SCRATCH = -9,   /* too large for rq_gemm_small_m_noalloc's scratch    */
+  RQ_ERR_DEGENERATE = -10 /* rq_proxy: every weight equal (no gap to normalise) */
 };
 
 /*
@@ -331,6 +332,26 @@ int rq_gemm_int8_acc(const int8_t *xq, int64_t m, const rq_qweight *w, int32_t *
  * measured against beside the 8 TB/s peak.  Errors: RQ_ERR_NULL,
  * RQ_ERR_ALIGN, RQ_ERR_SHAPE. */
 int rq_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/* RWKVQuant's weights-only coarse-to-fine proxy of one weight tensor (RWKVQuant:
+ * Quantizing the RWKV Family with Proxy Guided Hybrid of Scalar and Vector
+ * Quantization -- Abstract on the index page; machine-review page,
+ * pith_extraction.key_machinery): the `count` fp32 weights at w (HOST memory,
+ * any order; the tensor is flattened) are sorted, their n = count - 1 adjacent
+ * gaps divided by the mean gap (g), and
+ *   *pc = P_c = H(uniform gaps) - H(gaps) = log n - H(g / sum g)   (nats)
+ *   *pf = P_f = sum_{k=2..K} v[k-2] * |M_k|,  M_k = mean((g - mean g)^k)
+ * with v = NULL meaning v_k = 1/k!.  moments (may be NULL) receives M_2..M_K
+ * (K - 1 doubles).  The pages route a layer to scalar quantization only when
+ * P_c < tau_c and P_f < tau_f (tau_c = 1.54, tau_f = 30 reported for RWKV-7);
+ * they leave the gap normalisation, the entropy's base and binning, K and v_k
+ * open, and the values here follow the readings stated above.  Runs on the
+ * calling thread, O(count log count) for the sort, allocates a host copy of
+ * the weights.  Errors: RQ_ERR_NULL (w, pc or pf), RQ_ERR_SHAPE (count < 3,
+ * K < 2 or K > RQ_PROXY_MAX_K), RQ_ERR_NONFINITE, RQ_ERR_DEGENERATE. */
+#define RQ_PROXY_MAX_K 16
+int rq_proxy(const float *w, int64_t count, int K, const double *v, double *pc, double *pf,
+             double *moments);
 
 /* Test aid: the library's own fp64 -> fp16 (kind 0, uint16 out), fp64 ->
  * fp32 (kind 1, uint32 out) and fp64 -> e4m3fn (kind 2, uint8 out)

@@ -40,9 +40,9 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = rq.lib()
-    assert L.rq_abi_version() == 2
+    assert L.rq_abi_version() == 3
     assert rq.rq_workspace_bytes() == 64 << 20
-    for st in range(-9, 1):
+    for st in range(-10, 1):
         assert rq.status_str(st) and rq.status_str(st) != "unknown status"
     assert rq.status_str(-99) == "unknown status"
 

@@ -98,6 +98,12 @@ def test_uniform_samples_tend_to_exponential_spacings():
     assert mk[2] == pytest.approx(9.0, abs=0.6)
     assert pc == pytest.approx(1.0 - EULER_GAMMA, abs=0.01)
     assert pf == pytest.approx(1 / 2 + 2 / 6 + 9 / 24, abs=0.04)
+    # so near-uniform weights route to scalar quantization under the RWKV-7
+    # thresholds, and Gaussian ones (long tails: large gaps far from the mean
+    # gap) to vector quantization
+    assert proxy.route(pc, pf) == "SQ"
+    z = np.random.default_rng(12).standard_normal(1 << 18)
+    assert proxy.route(*proxy.proxy(z)[:2]) == "VQ"
 
 
 def test_hand_example_with_repeated_weights():
