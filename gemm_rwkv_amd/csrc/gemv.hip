@@ -25,8 +25,11 @@
 //     activation fragment is permuted to match with v_perm_b32, which is free
 //     to choose because a dot product does not depend on the order of its
 //     terms.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
+
 
 namespace rq {
 
@@ -1022,6 +1025,373 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
   if (m < p.m && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
 }
 
+// ---------------------------------------------------------------------------
+// phased activations: a workgroup = RT row tiles x a slice of K, the slice's
+// activations, codes and scales streamed through LDS in phases
+// ---------------------------------------------------------------------------
+// For batches that fill two activation tiles, staging a workgroup's whole
+// activation slice before any math (the streaming kernel above) either caps
+// the slice at what LDS holds, so that K is split into many slices whose
+// fp32 partial tiles a second kernel adds, or (one row tile per workgroup)
+// makes every workgroup read all of x.  Here the slice is cut into phases of
+// P = 4 chunks (512 k), each moved into one of three LDS buffers by LDS DMA
+// reads, two phases ahead: the 16 MT activation rows (1 KB each; rows >= M
+// read zeros through the buffer resource's range check), the RT x 16 code
+// rows (256 bytes each) and their scales.  The reads of a phase are dealt
+// evenly over every wave of the workgroup (one wave issuing them all was
+// limited by its issue rate), and the math reads only LDS.  At phase q every
+// wave waits for its own reads of phase q (those of q + 1 may stay in
+// flight); one barrier then makes the buffer visible and tells that every
+// wave is done with phase q - 1, whose buffer receives phase q + 2.  All RT
+// row tiles read the same activation rows, so x crosses L2 once per RT
+// tiles, and the whole K of most matrices fits one slice.
+//
+// Each of the eight waves owns one eighth of every phase's (chunk, group)
+// pairs for all RT row tiles: it reads an activation fragment from LDS once
+// and multiplies it into every tile, so LDS delivers each phase's activations
+// once per workgroup rather than once per tile.  A lane reads from LDS
+// exactly the code words the streaming kernel's lane exchange would hand it
+// (the 8 k at the fragment's offset), so no exchange is needed.  The eight
+// partial sums of each output are added through LDS in wave order at the
+// end.  Activation rows are padded to 1040 bytes and the 16-byte segments of
+// code row r are stored at slot (segment ^ (r % 16)), so the sixteen rows of
+// an operand read fall in distinct banks.  Decode and scaling are those of
+// the streaming kernel (symmetric int4).
+struct Plan6 {
+  int split;      // K slices (partial tiles summed by gemv5_reduce_kernel)
+  int cps;        // chunks per slice, a multiple of 4
+  int groups[3];  // tile groups (of RT tiles) per matrix
+};
+
+template <int G, int MT, int RT>
+struct G6 {
+  static constexpr int P = 4;                    // chunks per phase
+  static constexpr int NB = 3;                   // LDS buffers
+  static constexpr int NW = 8;                   // waves
+  static constexpr int GPC = 128 / G;            // scale groups per chunk
+  static constexpr int PPW = P * GPC / NW;       // (chunk, group) pairs of a wave per phase
+  static constexpr int RS = P * 256 + 16;        // LDS bytes per activation row
+  static constexpr int XR = 16 * MT;             // activation rows (one DMA each)
+  static constexpr int CD = RT * P;              // code DMAs (4 rows x 256 bytes each)
+  static constexpr int ND = XR + CD + 64 / G;    // DMA reads per phase (one or two scale spans)
+  static constexpr int DPW = (ND + NW - 1) / NW; // per wave, at most
+  static constexpr int XB = XR * RS;
+  static constexpr int CB = RT * 16 * P * 64;
+  static constexpr int SB = 2 * 64 * 16;         // scale spans: [2][64 rows][16 bytes]
+  static constexpr int BUF = XB + CB + SB;
+  static constexpr size_t LDS = (size_t)NB * BUF;
+  static_assert(PPW >= 1 && P * GPC == PPW * NW, "the pairs of a phase");
+  static_assert(RT * 16 <= 64, "one scale DMA covers the code rows");
+  static_assert(NB * BUF >= (size_t)NW * RT * MT * 1024, "the reduction fits the buffers");
+  static_assert(2 * DPW <= 63, "two phases of DMA reads within the wait counter");
+  static_assert(DPW <= 15, "the wait below covers up to fifteen");
+};
+
+// s_waitcnt vmcnt(n) for a uniform n in 0..15 (larger n waits as for 15)
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+  }
+}
+
+template <int G, int MT, int RT>
+__global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Plan6 sp) {
+  typedef F2<GF_W4, G> F;
+  typedef G6<G, MT, RT> C;
+  constexpr int P = C::P, NB = C::NB, RS = C::RS, BUF = C::BUF, DPW = C::DPW;
+  extern __shared__ uint4 lds4[];
+
+  const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
+  const int s = blockIdx.x / gtot;
+  const int gall = blockIdx.x - s * gtot;
+  const int g0 = sp.groups[0], g1 = sp.groups[1];
+  const bool in1 = gall >= g0, in2 = gall >= g0 + g1;
+  const int grp = gall - (in2 ? g0 + g1 : (in1 ? g0 : 0));
+  GemvMatrix A;
+  A.codes = in2 ? p.mat[2].codes : (in1 ? p.mat[1].codes : p.mat[0].codes);
+  A.scales = in2 ? p.mat[2].scales : (in1 ? p.mat[1].scales : p.mat[0].scales);
+  A.x = in2 ? p.mat[2].x : (in1 ? p.mat[1].x : p.mat[0].x);
+  A.y = in2 ? p.mat[2].y : (in1 ? p.mat[1].y : p.mat[0].y);
+  A.n = in2 ? p.mat[2].n : (in1 ? p.mat[1].n : p.mat[0].n);
+  A.tiles = in2 ? p.mat[2].tiles : (in1 ? p.mat[1].tiles : p.mat[0].tiles);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int k = p.k;
+  const int M = p.m;
+  const int nchunks = k / 128;
+  const int cbeg = s * sp.cps;
+  const int cend = min(nchunks, cbeg + sp.cps);
+  const int nph = (cend - cbeg) / P;
+  constexpr uint32_t kOOB = 0x7ffff000u;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
+  const uint32_t rowbytes = (uint32_t)nchunks * 64u;
+  const uint32_t srow = (uint32_t)(k / G) * 2u;
+
+  // this wave's DMA reads of a phase: d = wave DPW + i over the list
+  // [activation rows 0 .. XR - 1][code DMAs 0 .. CD - 1][scale spans]; a code
+  // DMA e covers group rows 4e .. 4e + 3 (lane l -> row 4e + l / 16, LDS slot
+  // l % 16 holding segment (l % 16) ^ (row % 16)); scale span u: lane l ->
+  // row l, 16 bytes at u 16 of its phase span.  The lane's byte offset at the
+  // slice's first phase (kOOB past the data: the read returns zeros) stays in
+  // a register; a phase adds its offset through the scalar offset operand.
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A.x, (short)0, (int)(((uint32_t)(M - 1) * (uint32_t)p.ldx + (uint32_t)k) * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A.codes, (short)0, (int)((uint32_t)A.n * rowbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A.scales, (short)0, (int)(((uint32_t)A.n * srow + 3u) & ~3u), 0x00020000);
+  const int d0 = wave * DPW;
+  const int nmine = max(0, min(DPW, C::ND - d0));
+  uint32_t vo[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int d = d0 + i;
+    if (d < C::XR) {
+      vo[i] = d < M ? (uint32_t)d * (uint32_t)p.ldx * 2u + (uint32_t)cbeg * 256u + (uint32_t)lane * 16u : kOOB;
+    } else if (d < C::XR + C::CD) {
+      const int row = 4 * (d - C::XR) + (lane >> 4);
+      const int nn = grp * RT * 16 + row;
+      const int seg = (lane & 15) ^ (row & 15);
+      vo[i] = nn < A.n ? (uint32_t)nn * rowbytes + (uint32_t)cbeg * 64u + (uint32_t)seg * 16u : kOOB;
+    } else {
+      const int u = d - C::XR - C::CD;
+      const int nn = grp * RT * 16 + lane;
+      vo[i] = (lane < RT * 16 && nn < A.n) ? (uint32_t)nn * srow + (uint32_t)cbeg * (F::GPC * 2u) + (uint32_t)u * 16u
+                                           : kOOB;
+    }
+  }
+  auto dma = [&](int q, int b) {
+    const uint32_t bb = lds_base + (uint32_t)(b * BUF);
+    const uint32_t qx = (uint32_t)q * (P * 256u), qc = (uint32_t)q * (P * 64u), qs = (uint32_t)q * (P * F::GPC * 2u);
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int d = d0 + i;
+      if (d < C::XR) {
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                     :: "v"(vo[i]), "s"(rx), "s"(qx), "s"(bb + (uint32_t)(d * RS)) : "memory", "m0");
+      } else if (d < C::XR + C::CD) {
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                     :: "v"(vo[i]), "s"(rc), "s"(qc), "s"(bb + (uint32_t)(C::XB + (d - C::XR) * 1024))
+                     : "memory", "m0");
+      } else if (d < C::ND) {
+        asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                     :: "v"(vo[i]), "s"(rsc), "s"(qs),
+                        "s"(bb + (uint32_t)(C::XB + C::CB + (d - C::XR - C::CD) * 1024))
+                     : "memory", "m0");
+      }
+    }
+  };
+
+  const int j = lane & 15;
+  const int kq = lane >> 4;
+  bool tv[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) tv[r] = grp * RT + r < A.tiles;
+
+  float4v acc[RT][MT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[r][t] = float4v{0.f, 0.f, 0.f, 0.f};
+  const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t* lds8 = (const uint8_t*)lds4;
+
+  auto compute = [&](int b) {
+    const uint8_t* bufp = lds8 + b * BUF;
+    const uint8_t* xb = bufp + j * RS + x_base<GF_W4, G>(kq) * 2;
+#pragma unroll
+    for (int e = 0; e < C::PPW; ++e) {
+      const int pi = wave * C::PPW + e;
+      const int ci = pi / C::GPC, g = pi - ci * C::GPC;  // chunk within the phase, group
+      // the lane's code bytes for k step pp: at ci 64 + (k offset of its
+      // fragment) / 2 within the row's phase span
+      const int b0 = ci * 64 + (x_base<GF_W4, G>(kq) + x_const<GF_W4, G>(g, 0)) / 2;
+      half8 af[F::MPG][MT];
+#pragma unroll
+      for (int pp = 0; pp < F::MPG; ++pp) {
+        const int xo = (ci * 128 + x_const<GF_W4, G>(g, pp)) * 2;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) af[pp][t] = *(const half8*)(xb + t * 16 * RS + xo);
+      }
+      const int hh = ci * C::GPC + g;  // scale half-word of the phase span
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int row = r * 16 + j;
+        const uint8_t* cr = bufp + C::XB + row * 256 + (b0 & 15);
+        uint32_t wv[2];
+        if constexpr (F::MPG == 2) {
+          const uint2 u = *(const uint2*)(cr + (((b0 >> 4) ^ j) << 4));
+          wv[0] = u.x;
+          wv[1] = u.y;
+        } else {
+          wv[0] = *(const uint32_t*)(cr + (((b0 >> 4) ^ j) << 4));
+          wv[1] = 0u;
+        }
+        const uint32_t word = *(const uint32_t*)(bufp + C::XB + C::CB + (hh >> 3) * (64 * 16) + row * 16 +
+                                                 ((hh & 7) >> 1) * 4);
+        const float v = f16_bits_to_f32((uint16_t)((hh & 1) ? (word >> 16) : (word & 0xffffu)));
+        const float scl = tv[r] ? v : 0.f;
+        float4v grp4[MT];
+#pragma unroll
+        for (int pp = 0; pp < F::MPG; ++pp) {
+          const half8 bq = dec4n<true>(wv[pp]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            grp4[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[pp][t], bq, pp == 0 ? zero4 : grp4[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[r][t][q] += scl * grp4[t][q];
+      }
+    }
+  };
+
+  dma(0, 0);
+  if (nph > 1) dma(1, 1);
+  for (int q = 0; q < nph; ++q) {
+    // this wave's reads of phase q have landed once only those of phase q + 1
+    // (if issued) are in flight
+    wait_vm(q + 1 < nph ? nmine : 0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (q + 2 < nph) dma(q + 2, (q + 2) % NB);
+    compute(q % NB);
+  }
+
+  // the eight waves' partial sums of each output, added in wave order
+  constexpr int E = MT * 4 * 64;  // outputs of one row tile (rows m < 16 MT)
+  const int ent = RT * E;
+  float* part = sp.split > 1 ? p.ws + ((size_t)gall * sp.split + s) * ent : nullptr;
+  float (*red)[RT][MT][4][64] = (float (*)[RT][MT][4][64])lds4;
+  __syncthreads();  // every wave is done with the buffers
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[wave][r][t][q][lane] = acc[r][t][q];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ent; idx += blockDim.x) {
+    const int rr = idx / E, e = idx - rr * E;
+    const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
+    float v = red[0][rr][t][q][l];
+#pragma unroll
+    for (int w2 = 1; w2 < C::NW; ++w2) v += red[w2][rr][t][q][l];
+    if (part) {
+      part[idx] = v;
+    } else {
+      const int m = t * 16 + 4 * (l >> 4) + q;
+      const int nn = (grp * RT + rr) * 16 + (l & 15);
+      if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
+    }
+  }
+}
+
+// Launch shape of gemv6_kernel, or false to leave the product to the
+// streaming kernel: four row tiles per workgroup (x then crosses L2 twice
+// per code byte at M = 32, within what a compute unit reads from L2 while its
+// codes stream from HBM) and K slices of whole phases until there is a
+// workgroup per compute unit.
+struct Shape6 {
+  int rt;
+  Plan6 plan;
+};
+constexpr int kG6Rt = 4;
+
+static bool plan6(const GemvBatch& b, int group, Shape6& sh) {
+  const int nchunks = b.k / 128;
+  if (b.m <= 16 || nchunks == 0 || nchunks % 4 != 0) return false;
+  // an activation slice that fits one workgroup's LDS whole: the streaming
+  // kernel stages it once, unsplit
+  if ((size_t)(b.m + 1) * (size_t)(b.k + 8) * 2u <= (size_t)kXBudgetUnsplit) return false;
+  constexpr size_t kLim = (size_t)1 << 31;
+  for (int i = 0; i < b.nmat; ++i) {
+    const size_t n = (size_t)b.mat[i].n;
+    if (n * (size_t)nchunks * 64u >= kLim || n * (size_t)(b.k / group) * 2u >= kLim) return false;
+  }
+  if ((size_t)b.m * (size_t)b.ldx * 2u >= kLim) return false;
+  int tiles = 0;
+  for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
+  // one activation tile's streamed plan of the streaming kernel (192 to 256
+  // row tiles, at most 64 chunks) does better without a K split
+  if (tiles >= 192 && tiles <= 256 && nchunks <= 64) return false;
+  constexpr int rt = kG6Rt;
+  auto groups = [&](int r) {
+    int g = 0;
+    for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
+    return g;
+  };
+  const int nph = nchunks / 4;
+  int split = 1;
+  while (groups(rt) * split < 192 && split < 16 && nph >= 4 * split) split *= 2;
+  const int cps = (nph + split - 1) / split * 4;
+  split = (nchunks + cps - 1) / cps;
+  const int mt = b.m <= 16 ? 1 : 2;
+  if (groups(rt) * split < 192) return false;
+  if (split > 1 && (!b.ws || (size_t)groups(rt) * split * rt * mt * 1024 > b.ws_bytes)) return false;
+  sh.rt = rt;
+  sh.plan.split = split;
+  sh.plan.cps = cps;
+  for (int i = 0; i < 3; ++i) sh.plan.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
+  return true;
+}
+
+template <int G>
+static bool launch6(const GemvBatch& b, hipStream_t st, hipError_t& err) {
+  Shape6 sh;
+  if (!plan6(b, G, sh)) return false;
+  const int mt = b.m <= 16 ? 1 : 2;
+  const int gtot = sh.plan.groups[0] + sh.plan.groups[1] + sh.plan.groups[2];
+  err = hipSuccess;
+  if (gtot == 0) return true;
+  const dim3 grid((unsigned)(gtot * sh.plan.split));
+#define RQ_L6(MT, RT)                                                                                \
+  do {                                                                                               \
+    typedef G6<G, MT, RT> C6;                                                                        \
+    static_assert(C6::LDS <= (size_t)160 * 1024, "LDS of a compute unit");                           \
+    static const bool attr_set = hipFuncSetAttribute((const void*)gemv6_kernel<G, MT, RT>,             \
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,      \
+                                                     (int)C6::LDS) == hipSuccess;                    \
+    (void)attr_set;                                                                                  \
+    hipLaunchKernelGGL((gemv6_kernel<G, MT, RT>), grid, dim3(C6::NW * 64), C6::LDS, st, b, sh.plan);   \
+  } while (0)
+  if (mt == 2) RQ_L6(2, kG6Rt); else RQ_L6(1, kG6Rt);
+#undef RQ_L6
+  err = hipGetLastError();
+  if (err == hipSuccess && sh.plan.split > 1) {
+    Split5 sp5;
+    sp5.split = sh.plan.split;
+    sp5.cps = sh.plan.cps;
+    sp5.wpt = 1;
+    sp5.rt = sh.rt;
+    for (int i = 0; i < 3; ++i) sp5.groups[i] = sh.plan.groups[i];
+    const int outs = gtot * sh.rt * mt * 256;
+    const dim3 rgrid((unsigned)((outs + 255) / 256));
+    if (mt == 2)
+      hipLaunchKernelGGL(gemv5_reduce_kernel<2>, rgrid, dim3(256), 0, st, b, sp5);
+    else
+      hipLaunchKernelGGL(gemv5_reduce_kernel<1>, rgrid, dim3(256), 0, st, b, sp5);
+    err = hipGetLastError();
+  }
+  return true;
+}
+
 // Chunks per wave for a slice of `cps` chunks: a wave keeps CPW code loads in
 // flight and a workgroup is best at four to eight waves per row tile, so the
 // count grows with the slice (16 only for one activation tile and formats
@@ -1334,6 +1704,10 @@ static hipError_t launch_nw(const GemvBatch& b, hipStream_t st) {
 template <int FMT, int G>
 static hipError_t launch_mt(const GemvBatch& b, hipStream_t st) {
   constexpr bool v2ok = !(FMT == GF_W4 && G == 16);
+  if constexpr (FMT == GF_W4 && (G == 64 || G == 32)) {
+    hipError_t err;
+    if (b.k % 512 == 0 && launch6<G>(b, st, err)) return err;
+  }
   if constexpr (v2ok) {
     if (b.k % F2<FMT, G>::CK == 0) {
       hipError_t err;
