@@ -1034,17 +1034,18 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
 // the slice at what LDS holds, so that K is split into many slices whose
 // fp32 partial tiles a second kernel adds, or (one row tile per workgroup)
 // makes every workgroup read all of x.  Here the slice is cut into phases of
-// P = 4 chunks (512 k), each moved into one of three LDS buffers by LDS DMA
-// reads, two phases ahead: the 16 MT activation rows (1 KB each; rows >= M
-// read zeros through the buffer resource's range check), the RT x 16 code
-// rows (256 bytes each) and their scales.  The reads of a phase are dealt
-// evenly over every wave of the workgroup (one wave issuing them all was
-// limited by its issue rate), and the math reads only LDS.  At phase q every
-// wave waits for its own reads of phase q (those of q + 1 may stay in
-// flight); one barrier then makes the buffer visible and tells that every
-// wave is done with phase q - 1, whose buffer receives phase q + 2.  All RT
-// row tiles read the same activation rows, so x crosses L2 once per RT
-// tiles, and the whole K of most matrices fits one slice.
+// P = 4 chunks (512 k), each moved into one of NB LDS buffers (three for two
+// activation tiles, four for one) by LDS DMA reads, NB - 1 phases ahead: the
+// 16 MT activation rows (1 KB each; rows >= M read zeros through the buffer
+// resource's range check), the RT x 16 code rows (256 bytes each) and their
+// scales.  The reads of a phase are dealt evenly over every wave of the
+// workgroup (one wave issuing them all was limited by its issue rate), and
+// the math reads only LDS.  At phase q every wave waits for its own reads of
+// phase q (those of later phases may stay in flight); one barrier then makes
+// the buffer visible and tells that every wave is done with phase q - 1,
+// whose buffer receives phase q + NB - 1.  All RT row tiles read the same
+// activation rows, so x crosses L2 once per RT tiles, and the whole K of
+// most matrices fits one slice.
 //
 // Each of the eight waves owns one eighth of every phase's (chunk, group)
 // pairs for all RT row tiles: it reads an activation fragment from LDS once
@@ -1066,7 +1067,7 @@ struct Plan6 {
 template <int G, int MT, int RT>
 struct G6 {
   static constexpr int P = 4;                    // chunks per phase
-  static constexpr int NB = 3;                   // LDS buffers
+  static constexpr int NB = MT == 1 ? 4 : 3;     // LDS buffers (phases in flight + 1)
   static constexpr int NW = 8;                   // waves
   static constexpr int GPC = 128 / G;            // scale groups per chunk
   static constexpr int PPW = P * GPC / NW;       // (chunk, group) pairs of a wave per phase
@@ -1083,8 +1084,8 @@ struct G6 {
   static_assert(PPW >= 1 && P * GPC == PPW * NW, "the pairs of a phase");
   static_assert(RT * 16 <= 64, "one scale DMA covers the code rows");
   static_assert(NB * BUF >= (size_t)NW * RT * MT * 1024, "the reduction fits the buffers");
-  static_assert(2 * DPW <= 63, "two phases of DMA reads within the wait counter");
-  static_assert(DPW <= 15, "the wait below covers up to fifteen");
+  static_assert((NB - 1) * DPW <= 63, "the phases in flight within the wait counter");
+  static_assert((NB - 2) * DPW <= 15, "the wait below covers up to fifteen");
 };
 
 // s_waitcnt vmcnt(n) for a uniform n in 0..15 (larger n waits as for 15)
@@ -1263,14 +1264,15 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
     }
   };
 
-  dma(0, 0);
-  if (nph > 1) dma(1, 1);
+#pragma unroll
+  for (int q = 0; q < NB - 1; ++q)
+    if (q < nph) dma(q, q);
   for (int q = 0; q < nph; ++q) {
-    // this wave's reads of phase q have landed once only those of phase q + 1
-    // (if issued) are in flight
-    wait_vm(q + 1 < nph ? nmine : 0);
+    // this wave's reads of phase q have landed once only those of the later
+    // phases already issued (up to NB - 2) are in flight
+    wait_vm(nmine * min(NB - 2, nph - 1 - q));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (q + 2 < nph) dma(q + 2, (q + 2) % NB);
+    if (q + NB - 1 < nph) dma(q + NB - 1, (q + NB - 1) % NB);
     compute(q % NB);
   }
 
