@@ -679,9 +679,18 @@ def alg_bytes(row, c1, c3, m3):
     return row["weight_bytes"] + 2 * m * c1 * 2
 
 
-def kernel_only(dec, pre, name, steps, dev):
+def _wide(name):
+    """A decode class of the width-4096 layer (the 13.3B shapes)."""
+    return "gemv" in name and ("4096x" in name or "x4096" in name)
+
+
+def kernel_only(dec, pre, name, steps, dev, gen=None):
     """Counter run: one calibration copy of CALIB_BYTES, then the class graph
-    replayed `steps` times; every dispatch after the last copy belongs to it."""
+    replayed `steps` times; every dispatch after the last copy belongs to it.
+    Classes of the width-4096 layer (e.g. "gemv w4g64 cmix key 16384x4096
+    M=1") run over rotated copies of that layer instead."""
+    if name and _wide(name):
+        dec = Decode(4096, gen, dev)
     classes = [(n, fn, dec.sets) for m in MS for n, fn, _, _ in dec.classes(m)]
     classes += [(n, fn, pre.sets) for n, fn, _, _, _ in pre.classes()]
     if not name:
@@ -734,15 +743,23 @@ def traffic_from(fetch_csv, write_csv):
     return res
 
 
-def trace_summary(path):
+def trace_summary(path, after_copy=False):
     """Library kernels of a rocprofv3 kernel trace grouped by name and launch
-    shape (workgroups x threads): dispatches, mean and median duration."""
+    shape (workgroups x threads): dispatches, mean and median duration.  With
+    after_copy, only the dispatches after the last device copy (the
+    calibration copy of a --kernel-only run)."""
     import csv
     groups = {}
     with open(path) as f:
-        for r in csv.DictReader(f):
+        rows = list(csv.DictReader(f))
+    t0 = 0
+    if after_copy:
+        ends = [int(r["End_Timestamp"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        t0 = max(ends) if ends else 0
+    for r in rows:
+        if True:
             name = r["Kernel_Name"]
-            if "rq::" not in name:
+            if "rq::" not in name or int(r["Start_Timestamp"]) < t0:
                 continue
             short = name.split("(")[0].replace("void ", "")
             wg = int(r["Workgroup_Size_X"])
@@ -760,7 +777,8 @@ def copies_for(name):
     if "fp8" in name:
         per_set = sum(n * k + 4 * n for _, n, k in synth.layer_shapes(C3))
     else:
-        per_set = sum(sum(rq.rq_qweight_bytes(rq.RQ_W4_SYM, 64, n, k)[:2]) for _, n, k in synth.layer_shapes(C1))
+        c = 4096 if _wide(name) else C1
+        per_set = sum(sum(rq.rq_qweight_bytes(rq.RQ_W4_SYM, 64, n, k)[:2]) for _, n, k in synth.layer_shapes(c))
     return -(-ROTATE_BYTES // per_set)
 
 
@@ -912,7 +930,7 @@ def main():
         print_traffic(args.traffic_from, args.kernel_only, args.steps)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary)
+        trace_summary(args.trace_summary, after_copy=args.kernel_only is not None)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -928,7 +946,7 @@ def main():
         print("weights ready", file=sys.stderr, flush=True)
 
     if args.kernel_only is not None:
-        kernel_only(dec, pre, args.kernel_only, args.steps, dev)
+        kernel_only(dec, pre, args.kernel_only, args.steps, dev, gen)
         return
 
     graphs = [capture(lambda m=m: dec.passes(m)) for m in MS] + [capture(pre.passes)]
