@@ -10,8 +10,9 @@
 // MFMA; the weights are read as codes and dequantized in registers, never
 // written out.  Beyond fp32 summation: symmetric, q * s is rounded once to
 // fp16 (q has 3 significant bits, s 11), at most 2^-11 of each weight (one
-// fp16 rounding); superblocks, nothing is rounded below fp32 (S_j, M_j and the
-// products x u are exact; the MFMA sums and the two scalings round in fp32).
+// fp16 rounding); superblocks, nothing is rounded below fp32 (the B operands
+// sc_j u and mc_j are exact fp16 integers, the products exact; the MFMA sums
+// over a 128-k block and its scalings by d and dmin round in fp32).
 //
 // A workgroup of NW waves (4 or 8) computes a BM x BN output tile; the waves
 // form a WM x (NW / WM) grid and each computes its (BM / WM) x (BN WM / NW)
@@ -188,11 +189,14 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
     if constexpr (SB) {
       // superblocks: a 4 x 4 word transpose across the lane quarters gives
       // lane q word q of each of the block's four 32-groups, so k step s
-      // covers group s alone; its MFMA result is scaled by S_s and corrected
-      // by -M_s times the activations' sum over the group, both in fp32
-      // (S_s = d sc_s and M_s = dmin mc_s are exact in fp32)
+      // covers group s alone.  With S_s = d sc_s and M_s = dmin mc_s, the
+      // block's sum is d sum_s sum_k x (sc_s u) - dmin sum_s sum_k x mc_s: the
+      // B operands sc_s u (at most 63 * 15) and mc_s are exact fp16 integers,
+      // so two MFMA chains per tile accumulate the block exactly up to fp32
+      // summation, and d and dmin are applied once per block in fp32
       uint32_t wv[TN][4];
-      float sc[TN][4], mn[TN][4];
+      uint32_t scc[TN][4], mcc[TN][4];  // the 6-bit codes, as fp16 bits (exact)
+      float dd[TN], dmm[TN];
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         const int row = wn * (BN / WN) + 16 * b + r16;
@@ -206,38 +210,60 @@ __global__ void __launch_bounds__(64 * NW) gemm_w4_kernel(const W4Gemm p, int kb
         wv[b][1] = w1;
         wv[b][2] = w2;
         wv[b][3] = w3;
-        const float d = f16_bits_to_f32(*(const uint16_t*)(ss + row * 4));
-        const float dm = f16_bits_to_f32(*(const uint16_t*)(ss + BN * 4 + row * 4));
+        dd[b] = f16_bits_to_f32(*(const uint16_t*)(ss + row * 4));
+        dmm[b] = f16_bits_to_f32(*(const uint16_t*)(ss + BN * 4 + row * 4));
         const uint4 sub = *(const uint4*)(ss + BN * 8 + row * 16);
         const uint64_t lo48 = (uint64_t)sub.x | ((uint64_t)(sub.y & 0xffffu) << 32);
         const uint64_t hi48 = (uint64_t)(sub.y >> 16) | ((uint64_t)sub.z << 16);
         const int g0 = ((kb0 + j) & 1) * 4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          sc[b][s] = d * (float)((uint32_t)(lo48 >> (6 * (g0 + s))) & 63u);
-          mn[b][s] = dm * (float)((uint32_t)(hi48 >> (6 * (g0 + s))) & 63u);
+          // an integer c < 64 is fp16 (1024 + c) - 1024: the bias trick of dec4n
+          const uint32_t c1 = (uint32_t)(lo48 >> (6 * (g0 + s))) & 63u;
+          const uint32_t c2 = (uint32_t)(hi48 >> (6 * (g0 + s))) & 63u;
+          scc[b][s] = hsub2(0x64006400u | c1 | (c1 << 16), 0x64006400u);
+          mcc[b][s] = hsub2(0x64006400u | c2 | (c2 << 16), 0x64006400u);
         }
       }
-      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-      const float4v z = {0.f, 0.f, 0.f, 0.f};
+      float4v r[TM][TN], rm[TM][TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          r[a][b] = float4v{0.f, 0.f, 0.f, 0.f};
+          rm[a][b] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        half8 bf[TN];
+        half8 bf[TN], bm[TN];
 #pragma unroll
-        for (int b = 0; b < TN; ++b) bf[b] = dec4n<false>(wv[b][s]);
+        for (int b = 0; b < TN; ++b) {
+          // sc_s u: packed fp16 products of integers below 2^11, exact
+          const uint4 u = __builtin_bit_cast(uint4, dec4n<false>(wv[b][s]));
+          const half2v c = __builtin_bit_cast(half2v, scc[b][s]);
+          bf[b] = __builtin_bit_cast(half8, make_uint4(__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u.x) * c),
+                                                       __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u.y) * c),
+                                                       __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u.z) * c),
+                                                       __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, u.w) * c)));
+          bm[b] = __builtin_bit_cast(half8, make_uint4(mcc[b][s], mcc[b][s], mcc[b][s], mcc[b][s]));
+        }
 #pragma unroll
         for (int a = 0; a < TM; ++a) {
           const int row = wm * (BM / WM) + 16 * a + r16;
           const half8 af = *(const half8*)(xs + row * 256 + (((4 * s + q) ^ (row & 15)) << 4));
-          const float4v xsum = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, ones, z, 0, 0, 0);
 #pragma unroll
           for (int b = 0; b < TN; ++b) {
-            const float4v r = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b], z, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[a][b][i] += sc[b][s] * r[i] - mn[b][s] * xsum[i];
+            r[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b], r[a][b], 0, 0, 0);
+            rm[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bm[b], rm[a][b], 0, 0, 0);
           }
         }
       }
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[a][b][i] += dd[b] * r[a][b][i] - dmm[b] * rm[a][b][i];
       return;
     }
     uint4 cw[TN];
