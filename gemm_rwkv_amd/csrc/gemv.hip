@@ -516,11 +516,25 @@ __device__ __forceinline__ void split_bf16(const half8& a, bf16x8& hi, bf16x8& l
 // distinct banks.  A workgroup then covers all of K for its 16 rows without a
 // second, reducing launch, at any K; the cost is that each workgroup reads all
 // of x.
-template <int FMT, int G, int MT, int CPW, int MR, bool ST = false>
+//
+// H > 1 (M = 1, int4 groups; "k ranges"): a tile is R = 16 / H rows, and
+// MFMA column c = h R + r holds row r over the h-th of H equal, contiguous
+// ranges of K, while A row h holds x over that same range (rows >= H read the
+// zero row).  Output (h, h R + r) is then row r's dot product over range h,
+// the other outputs are discarded, and the H of them are added at the end.
+// The MFMA work per byte is unchanged (at M = 1 fifteen A rows are zero
+// either way), but a matrix has H times as many tiles: one of 2048 rows fills
+// 256 workgroups, one per compute unit, instead of 128.  Each range of x sits
+// 16 bytes further along in LDS than a contiguous copy would put it, so the
+// H lanes reading different ranges hit different banks.
+template <int FMT, int G, int MT, int CPW, int MR, bool ST = false, int H = 1>
 __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
   typedef CodeSlot<FMT, G> S;
   static_assert(!ST || F::CK == 128, "streamed activations: 128-k chunks");
+  static_assert(H == 1 || (MT == 1 && MR == 1 && !ST && FMT == GF_W4 && H <= 4), "k ranges: M = 1, int4");
+  constexpr int R = 16 / H;                                 // rows per tile
+  constexpr int QN = MT == 1 ? (H > MR ? H : MR) : 4;       // outputs per lane that are kept
   static_assert(FMT != GF_SB || CPW % 2 == 0, "SB256: a wave's chunks pair into superblocks");
   extern __shared__ uint4 lds4[];
   uint16_t* xl = (uint16_t*)lds4;
@@ -551,15 +565,17 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   const int j = lane & 15;
   const int kq = lane >> 4;
   const int tile = grp * sp.rt + r;
-  const bool tvalid = tile < A.tiles;
-  const int n = tile * 16 + j;
-  const bool nvalid = n < A.n;
   const int k = p.k;
   const int M = p.m;
   const int nchunks = k / F::CK;
+  const int kch = nchunks / H;         // chunks of one k range (H > 1: one slice)
+  const int hr = H > 1 ? j / R : 0;    // this lane's k range
+  const bool tvalid = H > 1 ? tile * R < A.n : tile < A.tiles;
+  const int n = tile * R + (H > 1 ? j - hr * R : j);
+  const bool nvalid = n < A.n;
   const int cbeg = s * sp.cps;
-  const int cend = min(nchunks, cbeg + sp.cps);
-  const int ldl = sp.cps * F::CK + 8;  // LDS row stride (halves)
+  const int cend = H > 1 ? kch : min(nchunks, cbeg + sp.cps);
+  const int ldl = sp.cps * F::CK + 8 + (H > 1 ? 8 * H : 0);  // LDS row stride (halves)
   constexpr uint32_t kOOB = 0x7ffff000u;  // scalar offset past any buffer: loads read zero
 
   // buffer resources (num_records in bytes).  Rows >= n read row 0: their
@@ -567,7 +583,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   const uint32_t rowbytes = (uint32_t)nchunks * 64u;
   const __amdgpu_buffer_rsrc_t rc =
       __builtin_amdgcn_make_buffer_rsrc((void*)A.codes, (short)0, (int)((uint32_t)A.n * rowbytes), 0x00020000);
-  const uint32_t coff = (nvalid ? (uint32_t)n * rowbytes : 0u) + (uint32_t)kq * 16u;
+  const uint32_t coff = (nvalid ? (uint32_t)n * rowbytes : 0u) + (uint32_t)kq * 16u + (uint32_t)(hr * kch) * 64u;
   __amdgpu_buffer_rsrc_t rs = rc, rm = rc, rb = rc;
   uint32_t soff = 0, sboff = 0, subb = 0;
   // int8 group 64 stores 2 bytes of scales per chunk, so after a row with an
@@ -594,7 +610,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     const uint32_t srow = (uint32_t)(k / F::GK) * 2u;
     rs = __builtin_amdgcn_make_buffer_rsrc((void*)A.scales, (short)0, (int)(((uint32_t)A.n * srow + 3u) & ~3u),
                                            0x00020000);
-    soff = nvalid ? (uint32_t)n * srow : 0u;
+    soff = (nvalid ? (uint32_t)n * srow : 0u) + (uint32_t)(hr * kch) * (F::GPC * 2u);
     if constexpr (kHalfRow) {
       sh16 = (soff & 2u) << 3;
       soff &= ~3u;
@@ -622,14 +638,18 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   //    each chunk's compute waits only for its own code load.
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
   auto copy_x = [&]() {
-    const int blocks = (cend - cbeg) * (F::CK / 8);
+    const int blocks = (H > 1 ? nchunks : cend - cbeg) * (F::CK / 8);
     const int per_row = (blocks + 63) >> 6;
     if constexpr (MR == 1) {  // one activation row (M = 1): wave w copies blocks w, w + NW, ...
       const uint8_t* xs = (const uint8_t*)(A.x + (size_t)cbeg * F::CK) + lane * 16;
+      // k ranges: range h (kch / 4 blocks of 1 KB) lands 16 h bytes further
+      const int bpr = H > 1 ? kch / 4 : 1;
       for (int col = wave; col < per_row; col += NW)
         if (col * 64 + lane < blocks)
           asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                       :: "v"(xs + col * 1024), "s"(lds_base + (uint32_t)col * 1024u) : "memory", "m0");
+                       :: "v"(xs + col * 1024),
+                          "s"(lds_base + (uint32_t)col * 1024u + (H > 1 ? (uint32_t)(col / bpr) * 16u : 0u))
+                       : "memory", "m0");
       for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
       return;
     }
@@ -792,7 +812,10 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = t * 16 + j;
-    xrow[t] = (m < M ? m : M) * ldl + x_base<FMT, G>(kq);
+    if constexpr (H > 1)  // A row j < H: range j of x; the others the zero row
+      xrow[t] = (j < H ? j * (kch * F::CK + 8) : ldl) + x_base<FMT, G>(kq);
+    else
+      xrow[t] = (m < M ? m : M) * ldl + x_base<FMT, G>(kq);
   }
   float4v acc[MT];
 #pragma unroll
@@ -943,7 +966,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int q = 0; q < (MT == 1 ? MR : 4); ++q) {
+          for (int q = 0; q < QN; ++q) {
             acc[t][q] += scl[g] * grp[t][q];
             if constexpr (FMT == GF_SB) acc[t][q] -= mnv[g] * xs[t][q];
           }
@@ -966,6 +989,22 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
 #pragma unroll
     for (int q = 0; q < 4; ++q) red[wave][t][q][lane] = acc[t][q];
   __syncthreads();
+  if constexpr (H > 1) {
+    // row r of tile rr: output (h, h R + r) summed over the k ranges h, each
+    // over the tile's waves in wave order
+    for (int idx = threadIdx.x; idx < sp.rt * R; idx += blockDim.x) {
+      const int rr = idx / R, rw = idx - rr * R;
+      float v = 0.f;
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const int l = (h >> 2) * 16 + h * R + rw;
+        for (int w2 = 0; w2 < sp.wpt; ++w2) v += red[rr * sp.wpt + w2][0][h & 3][l];
+      }
+      const int nn = (grp * sp.rt + rr) * R + rw;
+      if (nn < A.n) A.y[nn] = f32_to_f16_bits(v);
+    }
+    return;
+  }
   constexpr int E = MT * 4 * 64;  // outputs of one row tile (rows m < 16 MT)
   const int ent = sp.rt * E;
   float* part = sp.split > 1 ? p.ws + ((size_t)gall * sp.split + s) * ent : nullptr;
@@ -1458,12 +1497,13 @@ static int pick_cpw(int cps, bool allow16, int m) {
 // unit; then as many row tiles per workgroup (up to 4, sharing the x slice)
 // as still keep that many workgroups.
 template <int FMT, int G>
-static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out) {
+static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out, int& ranges_out) {
   typedef F2<FMT, G> F;
   const int nchunks = b.k / F::CK;
   const int mt = b.m <= 16 ? 1 : 2;
   bool found = false;
   stream_out = false;
+  ranges_out = 1;
   // the kernel addresses every buffer through a buffer resource with a 32-bit
   // size and 32-bit offsets: each must stay below 2 GiB
   constexpr size_t kLim = (size_t)1 << 31;
@@ -1475,6 +1515,30 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     if (F::HW > 0 && n * (size_t)(b.k / 8) * 2u >= kLim) return false;
   }
   if ((size_t)b.m * (size_t)b.ldx * 2u >= kLim) return false;
+  // M = 1, int4 groups, fewer than 256 row tiles and at least 32 chunks: two
+  // k ranges per 8-row tile, twice the workgroups without a split (the
+  // kernel's H = 2).  Measured: cmix value 2048x8192 6.37 -> 5.63 us; O
+  // 2048x2048 (16 chunks) 3.66 -> 3.85 us, and matrices of 256 row tiles or
+  // more 4-10% slower, so those keep one range
+  if constexpr (FMT == GF_W4) {
+    int tiles = 0;
+    for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
+    const size_t xb = (size_t)2 * (nchunks * F::CK + 8 + 16) * 2;
+    const int kch = nchunks / 2;
+    const int cpw = pick_cpw(kch, true, 1);
+    const int wpt = (kch + cpw - 1) / cpw;
+    if (b.m == 1 && tiles < 256 && nchunks >= 32 && nchunks % 8 == 0 && xb <= (size_t)kXBudgetUnsplit &&
+        wpt <= 16) {
+      sp.split = 1;
+      sp.cps = nchunks;
+      sp.wpt = wpt;
+      sp.rt = 1;
+      for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? (b.mat[i].n + 7) / 8 : 0;
+      cpw_out = cpw;
+      ranges_out = 2;
+      return true;
+    }
+  }
   // formats whose decode costs more per byte than int4 groups (SB256, 5-/6-bit
   // codes, int8 group 16), on fewer than 256 row tiles with a long K at
   // M <= 4: four K slices of waves of four chunks, for four times the
@@ -1654,10 +1718,12 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   Split5 sp;
   int cpw = 4;
   bool stream = false;
-  if (!plan5<FMT, G>(b, sp, cpw, stream)) return false;
+  int ranges = 1;
+  if (!plan5<FMT, G>(b, sp, cpw, stream, ranges)) return false;
   const int mt = b.m <= 16 ? 1 : 2;
   const int nw = sp.rt * sp.wpt;
-  const size_t xb = stream ? (size_t)nw * 2 * (16 * mt * 128 * 2) : (size_t)(b.m + 1) * (sp.cps * F::CK + 8) * 2;
+  const size_t xb = stream ? (size_t)nw * 2 * (16 * mt * 128 * 2)
+                           : (size_t)(b.m + 1) * (sp.cps * F::CK + 8 + (ranges > 1 ? 8 * ranges : 0)) * 2;
   const size_t red = (size_t)nw * mt * 4 * 64 * 4;
   const size_t lds = xb > red ? xb : red;
   const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
@@ -1694,6 +1760,23 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
     }
   }
 #undef RQ_L5S
+#define RQ_L5H(CPW)                                                                               \
+  do {                                                                                            \
+    static const bool attr_set =                                                                  \
+        hipFuncSetAttribute((const void*)gemv5_kernel<FMT, G, 1, CPW, 1, false, 2>,               \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kXBudgetUnsplit + 1024) == \
+        hipSuccess;                                                                               \
+    (void)attr_set;                                                                               \
+    hipLaunchKernelGGL((gemv5_kernel<FMT, G, 1, CPW, 1, false, 2>), grid, block, lds, st, b, sp); \
+  } while (0)
+  if constexpr (FMT == GF_W4) {
+    if (ranges == 2) {
+      if (cpw == 4) RQ_L5H(4); else if (cpw == 8) RQ_L5H(8); else RQ_L5H(16);
+      err = hipGetLastError();
+      return true;
+    }
+  }
+#undef RQ_L5H
   if (mt == 2) {
     if (cpw == 2) RQ_L5(2, 2, 4); else if (cpw == 4) RQ_L5(2, 4, 4); else RQ_L5(2, 8, 4);
   } else if constexpr (FMT == GF_SB || F::HW > 0) {
