@@ -416,6 +416,12 @@ constexpr int x_const(int g, int p) {
 // per compute unit) rather than pay for a second, reducing kernel
 constexpr int kXBudget = 80 * 1024;
 constexpr int kXBudgetUnsplit = 150 * 1024;
+// largest M that the two-range plan takes (two k ranges of up to 8 rows fill
+// the 16 A rows)
+#ifndef RQ_RANGES_MAX_M
+#define RQ_RANGES_MAX_M 8
+#endif
+constexpr int kRangesMaxM = RQ_RANGES_MAX_M;
 
 // ---------------------------------------------------------------------------
 // the streaming kernel: a workgroup = RT row tiles x one slice of K
@@ -517,24 +523,27 @@ __device__ __forceinline__ void split_bf16(const half8& a, bf16x8& hi, bf16x8& l
 // second, reducing launch, at any K; the cost is that each workgroup reads all
 // of x.
 //
-// H > 1 (M = 1, int4 groups; "k ranges"): a tile is R = 16 / H rows, and
-// MFMA column c = h R + r holds row r over the h-th of H equal, contiguous
-// ranges of K, while A row h holds x over that same range (rows >= H read the
-// zero row).  Output (h, h R + r) is then row r's dot product over range h,
-// the other outputs are discarded, and the H of them are added at the end.
-// The MFMA work per byte is unchanged (at M = 1 fifteen A rows are zero
-// either way), but a matrix has H times as many tiles: one of 2048 rows fills
-// 256 workgroups, one per compute unit, instead of 128.  Each range of x sits
-// 16 bytes further along in LDS than a contiguous copy would put it, so the
-// H lanes reading different ranges hit different banks.
+// H = 2 (M <= 8, int4 groups; "k ranges"): a tile is R = 8 rows, and MFMA
+// column c = h R + r holds row r over the h-th of two equal, contiguous
+// halves of K, while A row a = h M + m holds activation row m over that same
+// half (rows a >= 2 M read the zero row).  Output (h M + m, h R + r) is then
+// row r's dot product with x_m over half h, the other outputs are discarded,
+// and the two halves are added at the end.  The MFMA work per byte is
+// unchanged (at M <= 8 at least half of the A rows are padding either way),
+// but a matrix has twice as many tiles: one of 2048 rows fills 256
+// workgroups, one per compute unit, without a K split.  In LDS each
+// activation row takes cps * 128 + 16 halves and its second half sits 16
+// bytes further along than a contiguous copy would put it, so the sixteen
+// (m, h) pairs an operand read touches start 32 m + 16 h bytes into a bank
+// row: all distinct.
 template <int FMT, int G, int MT, int CPW, int MR, bool ST = false, int H = 1>
 __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
   typedef CodeSlot<FMT, G> S;
   static_assert(!ST || F::CK == 128, "streamed activations: 128-k chunks");
-  static_assert(H == 1 || (MT == 1 && MR == 1 && !ST && FMT == GF_W4 && H <= 4), "k ranges: M = 1, int4");
+  static_assert(H == 1 || (MT == 1 && !ST && FMT == GF_W4 && H == 2), "k ranges: M <= 8, int4");
   constexpr int R = 16 / H;                                 // rows per tile
-  constexpr int QN = MT == 1 ? (H > MR ? H : MR) : 4;       // outputs per lane that are kept
+  constexpr int QN = MT == 1 ? (H * MR < 4 ? H * MR : 4) : 4;  // outputs per lane that are kept
   static_assert(FMT != GF_SB || CPW % 2 == 0, "SB256: a wave's chunks pair into superblocks");
   extern __shared__ uint4 lds4[];
   uint16_t* xl = (uint16_t*)lds4;
@@ -575,7 +584,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   const bool nvalid = n < A.n;
   const int cbeg = s * sp.cps;
   const int cend = H > 1 ? kch : min(nchunks, cbeg + sp.cps);
-  const int ldl = sp.cps * F::CK + 8 + (H > 1 ? 8 * H : 0);  // LDS row stride (halves)
+  const int ldl = sp.cps * F::CK + (H > 1 ? 16 : 8);  // LDS row stride (halves)
   constexpr uint32_t kOOB = 0x7ffff000u;  // scalar offset past any buffer: loads read zero
 
   // buffer resources (num_records in bytes).  Rows >= n read row 0: their
@@ -640,16 +649,38 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   auto copy_x = [&]() {
     const int blocks = (H > 1 ? nchunks : cend - cbeg) * (F::CK / 8);
     const int per_row = (blocks + 63) >> 6;
+    if constexpr (H > 1) {
+      // k ranges (one slice, whole 1 KB blocks): copies (m, col) dealt
+      // round-robin to the waves; the second half's blocks (col >= kch / 4)
+      // land 16 bytes further
+      const int bpr = kch / 4;
+      const uint32_t lrow = (uint32_t)ldl * 2u, grow = (uint32_t)p.ldx * 2u;
+      const uint8_t* xs = (const uint8_t*)A.x + lane * 16;
+      int m = 0, col = wave;
+      while (col >= per_row) {
+        col -= per_row;
+        ++m;
+      }
+      while (m < M) {
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :: "v"(xs + (uint32_t)m * grow + (uint32_t)col * 1024u),
+                        "s"(lds_base + (uint32_t)m * lrow + (uint32_t)col * 1024u + (col >= bpr ? 16u : 0u))
+                     : "memory", "m0");
+        col += NW;
+        while (col >= per_row) {
+          col -= per_row;
+          ++m;
+        }
+      }
+      for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + M * ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
+      return;
+    }
     if constexpr (MR == 1) {  // one activation row (M = 1): wave w copies blocks w, w + NW, ...
       const uint8_t* xs = (const uint8_t*)(A.x + (size_t)cbeg * F::CK) + lane * 16;
-      // k ranges: range h (kch / 4 blocks of 1 KB) lands 16 h bytes further
-      const int bpr = H > 1 ? kch / 4 : 1;
       for (int col = wave; col < per_row; col += NW)
         if (col * 64 + lane < blocks)
           asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                       :: "v"(xs + col * 1024),
-                          "s"(lds_base + (uint32_t)col * 1024u + (H > 1 ? (uint32_t)(col / bpr) * 16u : 0u))
-                       : "memory", "m0");
+                       :: "v"(xs + col * 1024), "s"(lds_base + (uint32_t)col * 1024u) : "memory", "m0");
       for (int b = threadIdx.x; b < blocks; b += blockDim.x) *(uint4*)(xl + ldl + b * 8) = make_uint4(0u, 0u, 0u, 0u);
       return;
     }
@@ -812,10 +843,12 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = t * 16 + j;
-    if constexpr (H > 1)  // A row j < H: range j of x; the others the zero row
-      xrow[t] = (j < H ? j * (kch * F::CK + 8) : ldl) + x_base<FMT, G>(kq);
-    else
+    if constexpr (H > 1) {  // A row j = h M + m < 2 M: row m, half h; the others the zero row
+      const int h = j / M;
+      xrow[t] = (j < H * M ? (j - h * M) * ldl + h * (kch * F::CK + 8) : M * ldl) + x_base<FMT, G>(kq);
+    } else {
       xrow[t] = (m < M ? m : M) * ldl + x_base<FMT, G>(kq);
+    }
   }
   float4v acc[MT];
 #pragma unroll
@@ -990,18 +1023,21 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     for (int q = 0; q < 4; ++q) red[wave][t][q][lane] = acc[t][q];
   __syncthreads();
   if constexpr (H > 1) {
-    // row r of tile rr: output (h, h R + r) summed over the k ranges h, each
-    // over the tile's waves in wave order
-    for (int idx = threadIdx.x; idx < sp.rt * R; idx += blockDim.x) {
-      const int rr = idx / R, rw = idx - rr * R;
+    // (m, row r of tile rr): output (h M + m, h R + r) summed over the
+    // halves h, each over the tile's waves in wave order
+    const int per_tile = M * R;
+    for (int idx = threadIdx.x; idx < sp.rt * per_tile; idx += blockDim.x) {
+      const int rr = idx / per_tile, e = idx - rr * per_tile;
+      const int m = e / R, rw = e - m * R;
       float v = 0.f;
 #pragma unroll
       for (int h = 0; h < H; ++h) {
-        const int l = (h >> 2) * 16 + h * R + rw;
-        for (int w2 = 0; w2 < sp.wpt; ++w2) v += red[rr * sp.wpt + w2][0][h & 3][l];
+        const int a = h * M + m;
+        const int l = (a >> 2) * 16 + h * R + rw;
+        for (int w2 = 0; w2 < sp.wpt; ++w2) v += red[rr * sp.wpt + w2][0][a & 3][l];
       }
       const int nn = (grp * sp.rt + rr) * R + rw;
-      if (nn < A.n) A.y[nn] = f32_to_f16_bits(v);
+      if (nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
     }
     return;
   }
@@ -1515,19 +1551,19 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     if (F::HW > 0 && n * (size_t)(b.k / 8) * 2u >= kLim) return false;
   }
   if ((size_t)b.m * (size_t)b.ldx * 2u >= kLim) return false;
-  // M = 1, int4 groups, fewer than 256 row tiles and at least 32 chunks: two
-  // k ranges per 8-row tile, twice the workgroups without a split (the
-  // kernel's H = 2).  Measured: cmix value 2048x8192 6.37 -> 5.63 us; O
-  // 2048x2048 (16 chunks) 3.66 -> 3.85 us, and matrices of 256 row tiles or
-  // more 4-10% slower, so those keep one range
+  // M <= MAXM, int4 groups, fewer than 256 row tiles and at least 32 chunks:
+  // two k ranges per 8-row tile, twice the workgroups without a split (the
+  // kernel's H = 2).  Measured at M = 1: cmix value 2048x8192 6.37 -> 5.63
+  // us; O 2048x2048 (16 chunks) 3.66 -> 3.85 us, and matrices of 256 row
+  // tiles or more 4-10% slower, so those keep one range
   if constexpr (FMT == GF_W4) {
     int tiles = 0;
     for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
-    const size_t xb = (size_t)2 * (nchunks * F::CK + 8 + 16) * 2;
+    const size_t xb = (size_t)(b.m + 1) * (nchunks * F::CK + 16) * 2;
     const int kch = nchunks / 2;
-    const int cpw = pick_cpw(kch, true, 1);
+    const int cpw = b.m <= 2 ? pick_cpw(kch, true, b.m) : (kch <= 24 ? 4 : 8);
     const int wpt = (kch + cpw - 1) / cpw;
-    if (b.m == 1 && tiles < 256 && nchunks >= 32 && nchunks % 8 == 0 && xb <= (size_t)kXBudgetUnsplit &&
+    if (b.m <= kRangesMaxM && tiles < 256 && nchunks >= 32 && nchunks % 8 == 0 && xb <= (size_t)kXBudgetUnsplit &&
         wpt <= 16) {
       sp.split = 1;
       sp.cps = nchunks;
@@ -1723,7 +1759,7 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   const int mt = b.m <= 16 ? 1 : 2;
   const int nw = sp.rt * sp.wpt;
   const size_t xb = stream ? (size_t)nw * 2 * (16 * mt * 128 * 2)
-                           : (size_t)(b.m + 1) * (sp.cps * F::CK + 8 + (ranges > 1 ? 8 * ranges : 0)) * 2;
+                           : (size_t)(b.m + 1) * (sp.cps * F::CK + (ranges > 1 ? 16 : 8)) * 2;
   const size_t red = (size_t)nw * mt * 4 * 64 * 4;
   const size_t lds = xb > red ? xb : red;
   const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
@@ -1760,18 +1796,24 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
     }
   }
 #undef RQ_L5S
-#define RQ_L5H(CPW)                                                                               \
+#define RQ_L5H(CPW, MR)                                                                           \
   do {                                                                                            \
     static const bool attr_set =                                                                  \
-        hipFuncSetAttribute((const void*)gemv5_kernel<FMT, G, 1, CPW, 1, false, 2>,               \
+        hipFuncSetAttribute((const void*)gemv5_kernel<FMT, G, 1, CPW, MR, false, 2>,              \
                             hipFuncAttributeMaxDynamicSharedMemorySize, kXBudgetUnsplit + 1024) == \
         hipSuccess;                                                                               \
     (void)attr_set;                                                                               \
-    hipLaunchKernelGGL((gemv5_kernel<FMT, G, 1, CPW, 1, false, 2>), grid, block, lds, st, b, sp); \
+    hipLaunchKernelGGL((gemv5_kernel<FMT, G, 1, CPW, MR, false, 2>), grid, block, lds, st, b, sp); \
   } while (0)
   if constexpr (FMT == GF_W4) {
     if (ranges == 2) {
-      if (cpw == 4) RQ_L5H(4); else if (cpw == 8) RQ_L5H(8); else RQ_L5H(16);
+      if (b.m == 1) {
+        if (cpw == 4) RQ_L5H(4, 1); else if (cpw == 8) RQ_L5H(8, 1); else RQ_L5H(16, 1);
+      } else if (b.m == 2) {
+        if (cpw == 4) RQ_L5H(4, 2); else if (cpw == 8) RQ_L5H(8, 2); else RQ_L5H(16, 2);
+      } else {
+        if (cpw == 4) RQ_L5H(4, 4); else RQ_L5H(8, 4);
+      }
       err = hipGetLastError();
       return true;
     }
