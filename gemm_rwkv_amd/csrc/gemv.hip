@@ -418,10 +418,7 @@ constexpr int kXBudget = 80 * 1024;
 constexpr int kXBudgetUnsplit = 150 * 1024;
 // largest M that the two-range plan takes (two k ranges of up to 8 rows fill
 // the 16 A rows)
-#ifndef RQ_RANGES_MAX_M
-#define RQ_RANGES_MAX_M 8
-#endif
-constexpr int kRangesMaxM = RQ_RANGES_MAX_M;
+constexpr int kRangesMaxM = 8;
 
 // ---------------------------------------------------------------------------
 // the streaming kernel: a workgroup = RT row tiles x one slice of K
@@ -1551,11 +1548,13 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     if (F::HW > 0 && n * (size_t)(b.k / 8) * 2u >= kLim) return false;
   }
   if ((size_t)b.m * (size_t)b.ldx * 2u >= kLim) return false;
-  // M <= MAXM, int4 groups, fewer than 256 row tiles and at least 32 chunks:
+  // M <= 8, int4 groups, fewer than 256 row tiles and at least 32 chunks:
   // two k ranges per 8-row tile, twice the workgroups without a split (the
   // kernel's H = 2).  Measured at M = 1: cmix value 2048x8192 6.37 -> 5.63
   // us; O 2048x2048 (16 chunks) 3.66 -> 3.85 us, and matrices of 256 row
-  // tiles or more 4-10% slower, so those keep one range
+  // tiles or more 4-10% slower, so those keep one range.  SB256 codes on two
+  // ranges (whole superblocks per range) were slower than their four-slice
+  // plan: 2560x10240 at M = 1 and 4, 11.4 and 12.6 -> 12.2 and 18.5 us
   if constexpr (FMT == GF_W4) {
     int tiles = 0;
     for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;

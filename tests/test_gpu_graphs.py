@@ -187,11 +187,13 @@ def test_graph_gemm_w4_and_fused_rkv():
 def test_graph_replays_planner_shapes():
     """Launch shapes added to the planner, captured and replayed: a long K
     cut four ways for SB256 on 160 row tiles (M = 1), one-tile streamed
-    activations (4-bit codes, 194 row tiles, M = 6) and a split whose last
-    slices are empty (6-bit, 41 chunks, M = 32)."""
+    activations (4-bit codes, 194 row tiles, M = 6), a split whose last
+    slices are empty (6-bit, 41 chunks, M = 32) and the two-range 8-row
+    tiles (int4, 128 and 63 row tiles of 16, M = 1 and 8)."""
     from gpu_helpers import random_parts
     cases = [(quant.W4_ASYM_SB256, 32, 2560, 10240, 1), (quant.W4_SYM, 32, 3100, 16384, 6),
-             (quant.W6_SYM, 32, 2085, 5248, 32)]
+             (quant.W6_SYM, 32, 2085, 5248, 32), (quant.W4_SYM, 64, 2048, 8192, 1),
+             (quant.W4_SYM, 32, 1000, 4096, 8)]
     items = []
     for i, (fmt, group, n, k, m) in enumerate(cases):
         g = np.random.default_rng(300 + i)

@@ -84,3 +84,39 @@ def test_ranges_fused_small(m):
         y_ref, b = ref.weight_only_ref(x, quant.W4_SYM, p, 64)
         ok, info = ref.compare(out[:, :n].astype(np.float64), y_ref, b)
         assert ok, (n, info)
+
+
+SB_SHAPES = [(2560, 10240), (1000, 4096), (9, 5120), (136, 4096), (2560, 2560)]
+
+
+@pytest.mark.parametrize("n,k", SB_SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9])
+def test_ranges_sb256(n, k, m):
+    # superblock codes at the same shapes keep their one-range plans (unsplit,
+    # or four K slices on fewer than 256 row tiles at M <= 4): the planner's
+    # boundary between the formats
+    g = np.random.default_rng(n + k + m)
+    key = ("sb", n, k)
+    if key not in _cache:
+        _cache.clear()
+        parts = random_parts(quant.W4_ASYM_SB256, 32, n, k, g)
+        _cache[key] = (parts, qweight_from_oracle(quant.W4_ASYM_SB256, 32, parts, n, k))
+    parts, qw = _cache[key]
+    ldx = k + 8 * (m % 3)
+    x = g.standard_normal((m, ldx)).astype(np.float16)
+    x[:, g.integers(0, k, 4)] *= 50.0
+    ldy = n + 4
+    y = torch.full((m * ldy,), -1, dtype=torch.int16, device="cuda")
+    say("ranges sb256", "n", n, "k", k, "m", m)
+    rq.rq_gemm_small_m(dev_f16(x), m, ldx, qw, y, ldy)
+    torch.cuda.synchronize()
+    out = host(y, np.float16, (m, ldy))
+    assert np.all(out[:, n:].view(np.int16) == -1), "wrote past n"
+    if n > 1100:
+        rows = np.concatenate([np.sort(g.choice(n - 9, 55, replace=False)), np.arange(n - 9, n)])
+        sub = rows_of(parts, rows)
+    else:
+        rows, sub = np.arange(n), parts
+    y_ref, b = ref.weight_only_ref(x[:, :k], quant.W4_ASYM_SB256, sub, 32)
+    ok, info = ref.compare(out[:, rows].astype(np.float64), y_ref, b)
+    assert ok, info
