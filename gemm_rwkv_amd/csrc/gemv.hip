@@ -512,8 +512,9 @@ __device__ __forceinline__ void split_bf16(const half8& a, bf16x8& hi, bf16x8& l
 // ST (streamed, 128-k chunks, one row tile, no split): instead of one
 // activation slice shared through LDS, every wave copies the activations of
 // its own chunks, one chunk at a time, into a private double buffer of 16 MT
-// rows x 128 k (rows >= M read zeros through the buffer resource's range
-// check), and computes chunk i while chunk i + 1 arrives.
+// rows x 128 k (rows >= M in the last copied 4-row group read zeros through
+// the buffer resource's range check; later groups are zeroed once and not
+// copied), and computes chunk i while chunk i + 1 arrives.
 // Rows are 256 bytes with the 16-byte segment s of row r stored at slot
 // s ^ (r & 15), so the sixteen rows an MFMA operand read touches fall in
 // distinct banks.  A workgroup then covers all of K for its 16 rows without a
@@ -533,6 +534,20 @@ __device__ __forceinline__ void split_bf16(const half8& a, bf16x8& hi, bf16x8& l
 // bytes further along than a contiguous copy would put it, so the sixteen
 // (m, h) pairs an operand read touches start 32 m + 16 h bytes into a bank
 // row: all distinct.
+// s_waitcnt vmcnt(n) for a wave-uniform n in 1..7 (0 above): the streamed
+// activations' wait for one chunk's copies, whose count depends on M
+__device__ __forceinline__ void wait_vm_st(int n) {
+  switch (n) {
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
 template <int FMT, int G, int MT, int CPW, int MR, bool ST = false, int H = 1>
 __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
@@ -814,10 +829,15 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc((void*)A.x, (short)0, (int)((uint32_t)M * (uint32_t)p.ldx * 2u), 0x00020000);
   const uint32_t st_r = (uint32_t)(lane >> 4), st_s = (uint32_t)(lane & 15);
+  // only the 4-row groups that hold rows < M are copied (a group past M would
+  // read zeros through the range check); the others are zeroed once in both
+  // buffers.  4096x16384 at M = 4 and 8: 15.6 and 15.8 -> 14.4 and 15.4 us
+  const int st_nq = (M + 3) >> 2 < kStCopies ? (M + 3) >> 2 : kStCopies;
   auto st_copy = [&](int i) {  // chunk c0 + i (clamped inside the slice) into buffer i & 1
     const int c = c0 + i < cend ? c0 + i : cend - 1;
 #pragma unroll
     for (int q = 0; q < kStCopies; ++q) {
+      if (q >= st_nq) break;
       const uint32_t r = 4u * q + st_r;
       const uint32_t voff = r * (uint32_t)p.ldx * 2u + (uint32_t)c * 256u + ((st_s ^ (r & 15u)) << 4);
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
@@ -825,6 +845,10 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     }
   };
   if constexpr (ST) {
+    for (int q = st_nq; q < kStCopies; ++q) {
+      *(uint4*)((uint8_t*)lds4 + wave * 2 * kStBuf + 1024 * q + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+      *(uint4*)((uint8_t*)lds4 + wave * 2 * kStBuf + kStBuf + 1024 * q + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+    }
     st_copy(0);
     if (CPW > 1) st_copy(1);
   } else if constexpr (kCodesFirst) {
@@ -868,7 +892,7 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
     }
     if constexpr (ST) {
       // chunk i has landed once only chunk i + 1's copies may be in flight
-      if (i + 1 < CPW) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kStCopies) : "memory");
+      if (i + 1 < CPW) wait_vm_st(st_nq);
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     uint32_t w[4] = {sl[i].c.x, sl[i].c.y, sl[i].c.z, sl[i].c.w};
