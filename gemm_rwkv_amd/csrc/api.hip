@@ -321,6 +321,45 @@ int rq_gemm_small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight*
   return small_m(x, m, ldx, w, y, ldy, ws, ws_bytes, stream, 0, 0);
 }
 
+int rq_plan_small_m(const rq_qweight* w, int64_t m, int64_t ldx, size_t ws_bytes, rq_plan* out) {
+  if (!out) return RQ_ERR_NULL;
+  memset(out, 0, sizeof(*out));
+  int st = rqv::check_weight(w);
+  if (st != RQ_OK) return st;
+  const int gf = gemv_fmt(w->format);
+  if (gf < 0) return RQ_ERR_FORMAT;
+  if (m < 0 || m > 32) return RQ_ERR_SHAPE;
+  // x's shape and stride checks, as rq_gemm_small_m makes them (the address
+  // stands for any aligned activation buffer)
+  if ((st = rqv::check_act((const void*)(uintptr_t)256, m, w->k, ldx)) != RQ_OK) return st;
+  if (m == 0 || w->n == 0) return RQ_OK;
+  rq::GemvBatch b;
+  memset(&b, 0, sizeof(b));
+  b.mat[0].n = (int)w->n;
+  b.mat[0].tiles = (int)((w->n + 15) / 16);
+  b.nmat = 1;
+  b.k = (int)w->k;
+  b.m = (int)m;
+  b.ldx = (int)ldx;
+  b.ldy = (int)w->n;
+  // the planner only asks whether a workspace exists and how large it is
+  b.ws = ws_bytes ? (float*)(uintptr_t)256 : nullptr;
+  b.ws_bytes = ws_bytes;
+  rq::GemvPlanInfo p;
+  if (!rq::plan_gemv(b, gf, w->group, p)) return RQ_ERR_SHAPE;
+  out->kernel = p.kernel;
+  out->split = p.split;
+  out->chunks_per_slice = p.cps;
+  out->chunks_per_wave = p.cpw;
+  out->waves_per_tile = p.wpt;
+  out->tiles_per_workgroup = p.rt;
+  out->workgroups = p.workgroups;
+  out->threads = p.threads;
+  out->lds_bytes = (int64_t)p.lds;
+  out->workspace_bytes = (int64_t)p.ws_used;
+  return RQ_OK;
+}
+
 int rq_fused_rkv(const uint16_t* xr, const uint16_t* xk, const uint16_t* xv, int64_t m, int64_t ldx,
                  const rq_qweight* wr, const rq_qweight* wk, const rq_qweight* wv, uint16_t* yr,
                  uint16_t* yk, uint16_t* yv, int64_t ldy, void* wsp, size_t ws_bytes, void* stream) {

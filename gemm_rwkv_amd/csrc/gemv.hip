@@ -1771,6 +1771,19 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
   return found;
 }
 
+// Dynamic LDS of a gemv5_kernel launch: the activation slice (or the waves'
+// streamed buffers), or the reduction of the waves' partial tiles.
+template <int FMT, int G>
+static size_t lds5(const GemvBatch& b, const Split5& sp, bool stream, int ranges) {
+  typedef F2<FMT, G> F;
+  const int mt = b.m <= 16 ? 1 : 2;
+  const int nw = sp.rt * sp.wpt;
+  const size_t xb = stream ? (size_t)nw * 2 * (16 * mt * 128 * 2)
+                           : (size_t)(b.m + 1) * (sp.cps * F::CK + (ranges > 1 ? 16 : 8)) * 2;
+  const size_t red = (size_t)nw * mt * 4 * 64 * 4;
+  return xb > red ? xb : red;
+}
+
 template <int FMT, int G>
 static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   typedef F2<FMT, G> F;
@@ -1781,10 +1794,7 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   if (!plan5<FMT, G>(b, sp, cpw, stream, ranges)) return false;
   const int mt = b.m <= 16 ? 1 : 2;
   const int nw = sp.rt * sp.wpt;
-  const size_t xb = stream ? (size_t)nw * 2 * (16 * mt * 128 * 2)
-                           : (size_t)(b.m + 1) * (sp.cps * F::CK + (ranges > 1 ? 16 : 8)) * 2;
-  const size_t red = (size_t)nw * mt * 4 * 64 * 4;
-  const size_t lds = xb > red ? xb : red;
+  const size_t lds = lds5<FMT, G>(b, sp, stream, ranges);
   const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
   err = hipSuccess;
   if (gtot == 0) return true;
@@ -1886,15 +1896,22 @@ static hipError_t launch_t(const GemvBatch& b, hipStream_t st) {
   return hipGetLastError();
 }
 
+// waves per workgroup of the first kernel: enough groups per wave to keep
+// several loads in flight
+template <int FMT, int G>
+static int nw_first(const GemvBatch& b) {
+  const int ng = b.k / Fmt<FMT, G>::GK;
+  return ng >= 8 * 16 ? 8 : (ng >= 4 * 8 ? 4 : (ng >= 2 * 4 ? 2 : 1));
+}
+
 template <int FMT, int G, int MT>
 static hipError_t launch_nw(const GemvBatch& b, hipStream_t st) {
-  const int gk = Fmt<FMT, G>::GK;
-  const int ng = b.k / gk;
-  // enough groups per wave to keep several loads in flight
-  if (ng >= 8 * 16) return launch_t<FMT, G, MT, 8>(b, st);
-  if (ng >= 4 * 8) return launch_t<FMT, G, MT, 4>(b, st);
-  if (ng >= 2 * 4) return launch_t<FMT, G, MT, 2>(b, st);
-  return launch_t<FMT, G, MT, 1>(b, st);
+  switch (nw_first<FMT, G>(b)) {
+    case 8: return launch_t<FMT, G, MT, 8>(b, st);
+    case 4: return launch_t<FMT, G, MT, 4>(b, st);
+    case 2: return launch_t<FMT, G, MT, 2>(b, st);
+    default: return launch_t<FMT, G, MT, 1>(b, st);
+  }
 }
 
 
@@ -1917,6 +1934,95 @@ static hipError_t launch_mt(const GemvBatch& b, hipStream_t st) {
     if (b.m <= 16) return launch_nw<FMT, G, 1>(b, st);
     return launch_nw<FMT, G, 2>(b, st);
   }
+}
+
+// launch_mt's choice, described instead of launched
+template <int FMT, int G>
+static bool describe_mt(const GemvBatch& b, GemvPlanInfo& o) {
+  constexpr bool v2ok = !(FMT == GF_W4 && G == 16);
+  o = GemvPlanInfo{};
+  const int mt = b.m <= 16 ? 1 : 2;
+  if constexpr (FMT == GF_W4 && (G == 64 || G == 32)) {
+    Shape6 sh;
+    if (b.k % 512 == 0 && plan6(b, G, sh)) {
+      const int gtot = sh.plan.groups[0] + sh.plan.groups[1] + sh.plan.groups[2];
+      o.kernel = 4;
+      o.split = sh.plan.split;
+      o.cps = sh.plan.cps;
+      o.rt = sh.rt;
+      o.workgroups = gtot * sh.plan.split;
+      o.threads = (mt == 2 ? G6<G, 2, kG6Rt>::NW : G6<G, 1, kG6Rt>::NW) * 64;
+      o.lds = mt == 2 ? G6<G, 2, kG6Rt>::LDS : G6<G, 1, kG6Rt>::LDS;
+      o.ws_used = sh.plan.split > 1 ? (size_t)gtot * sh.plan.split * sh.rt * mt * 1024 : 0;
+      return true;
+    }
+  }
+  if constexpr (v2ok) {
+    if (b.k % F2<FMT, G>::CK == 0) {
+      Split5 sp;
+      int cpw = 4;
+      bool stream = false;
+      int ranges = 1;
+      if (plan5<FMT, G>(b, sp, cpw, stream, ranges)) {
+        const int gtot = sp.groups[0] + sp.groups[1] + sp.groups[2];
+        o.kernel = stream ? 3 : (ranges > 1 ? 2 : 1);
+        o.split = sp.split;
+        o.cps = sp.cps;
+        o.cpw = cpw;
+        o.wpt = sp.wpt;
+        o.rt = sp.rt;
+        o.workgroups = gtot * sp.split;
+        o.threads = sp.rt * sp.wpt * 64;
+        o.lds = lds5<FMT, G>(b, sp, stream, ranges);
+        o.ws_used = sp.split > 1 ? (size_t)gtot * sp.split * sp.rt * mt * 1024 : 0;
+        return true;
+      }
+    }
+  }
+  if constexpr (FMT == GF_W5 || FMT == GF_W6 || FMT == GF_BF16) {
+    return false;
+  } else {
+    int tiles = 0;
+    for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
+    o.kernel = 5;
+    o.split = 1;
+    o.rt = 1;
+    o.workgroups = tiles;
+    o.threads = nw_first<FMT, G>(b) * 64;
+    return true;
+  }
+}
+
+bool plan_gemv(const GemvBatch& b, int fmt, int group, GemvPlanInfo& out) {
+  out = GemvPlanInfo{};
+  if (b.m == 0) return true;
+  switch (fmt) {
+    case GF_W4:
+      if (group == 64) return describe_mt<GF_W4, 64>(b, out);
+      if (group == 32) return describe_mt<GF_W4, 32>(b, out);
+      if (group == 16) return describe_mt<GF_W4, 16>(b, out);
+      break;
+    case GF_W8:
+      if (group == 64) return describe_mt<GF_W8, 64>(b, out);
+      if (group == 32) return describe_mt<GF_W8, 32>(b, out);
+      if (group == 16) return describe_mt<GF_W8, 16>(b, out);
+      break;
+    case GF_SB:
+      return describe_mt<GF_SB, 32>(b, out);
+    case GF_F16:
+      return describe_mt<GF_F16, 32>(b, out);
+    case GF_W6:
+      if (group == 64) return describe_mt<GF_W6, 64>(b, out);
+      if (group == 32) return describe_mt<GF_W6, 32>(b, out);
+      break;
+    case GF_W5:
+      if (group == 64) return describe_mt<GF_W5, 64>(b, out);
+      if (group == 32) return describe_mt<GF_W5, 32>(b, out);
+      break;
+    case GF_BF16:
+      return describe_mt<GF_BF16, 32>(b, out);
+  }
+  return false;
 }
 
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st) {

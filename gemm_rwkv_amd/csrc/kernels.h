@@ -53,6 +53,23 @@ constexpr size_t kWorkspaceBytes = 64u << 20;
 
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 
+// The launch launch_gemv would make for b, computed on the host without
+// touching the GPU (the same planners, in the same order).  false: no launch
+// shape (launch_gemv returns hipErrorInvalidConfiguration).
+struct GemvPlanInfo {
+  int kernel;      // 1 streaming, 2 streaming with two k ranges, 3 streamed activations, 4 phased, 5 first version
+  int split;       // K slices (> 1: partial tiles in the workspace and a reducing launch)
+  int cps;         // chunks per slice (streaming, phased)
+  int cpw;         // chunks per wave (streaming)
+  int wpt;         // waves per row tile (streaming)
+  int rt;          // row tiles per workgroup
+  int workgroups;  // of the main launch
+  int threads;     // per workgroup
+  size_t lds;      // dynamic LDS of the main launch, bytes
+  size_t ws_used;  // workspace bytes the partial tiles take
+};
+bool plan_gemv(const GemvBatch& b, int fmt, int group, GemvPlanInfo& out);
+
 // ---- prefill products on int4 codes, any m (gemm_w4.hip) --------------------
 struct W4Gemm {
   const uint16_t* x;       // fp16 [m][ldx]

@@ -44,8 +44,11 @@ EXPORTS = (
     "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16", "rq_gemm_small_m", "rq_fused_rkv",
     "rq_quantize_act", "rq_gemm_fp8", "rq_gemm_int8", "rq_gemm_int8_acc", "rq_host_convert",
     "rq_gemm_w4", "rq_quantize_aw", "rq_workspace_bytes", "rq_gemm_small_m_noalloc", "rq_stream_read",
-    "rq_proxy",
+    "rq_proxy", "rq_plan_small_m",
 )
+
+# rq_plan.kernel
+RQ_PLAN_NONE, RQ_PLAN_STREAMING, RQ_PLAN_TWO_RANGES, RQ_PLAN_STREAMED_X, RQ_PLAN_PHASED, RQ_PLAN_FIRST = range(6)
 
 
 class RqError(RuntimeError):
@@ -58,6 +61,13 @@ class _QW(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("group", ctypes.c_int32), ("n", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("mins", ctypes.c_void_p), ("sub", ctypes.c_void_p)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in ("kernel", "split", "chunks_per_slice", "chunks_per_wave",
+                                                    "waves_per_tile", "tiles_per_workgroup", "workgroups",
+                                                    "threads")] + \
+               [("lds_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -90,6 +100,7 @@ def lib():
             "rq_stream_read": ([vp, sz, vp, vp], i32),
             "rq_proxy": ([vp, i64, i32, vp, vp, vp, vp], i32),
             "rq_host_convert": ([i32, vp, vp, i64], i32),
+            "rq_plan_small_m": ([qp, i64, i64, sz, ctypes.POINTER(_Plan)], i32),
         }
         for name in ("rq_gemv_w4g16", "rq_gemv_w4g32", "rq_gemv_w4g64", "rq_gemv_w8g16",
                      "rq_gemv_w8g32", "rq_gemv_w8g64", "rq_gemv_w4sb256", "rq_gemv_f16"):
@@ -277,6 +288,27 @@ def rq_gemm_small_m(x, m, ldx, w, y, ldy, stream=None, ws=None):
     st = lib().rq_gemm_small_m(_ptr(x), m, ldx, ctypes.byref(d), _ptr(y), ldy, *_ws(ws), _stream(stream))
     _check(st, "rq_gemm_small_m")
     return y
+
+
+def rq_plan_small_m(w, m, ldx=None, ws_bytes=None):
+    """The launch rq_gemm_small_m would make (host only): a dict of rq_plan's
+    fields.  ws_bytes defaults to rq_workspace_bytes(); 0 means no
+    workspace.  w may be a QWeight or a (format, group, n, k) tuple."""
+    if isinstance(w, tuple):
+        fmt, group, n, k = w
+        # descriptor of 256-aligned placeholder addresses: the planner reads
+        # the shapes only
+        d = _QW(fmt, group, n, k, 256, 256, 256, 256)
+    else:
+        d = w.desc()
+    if ldx is None:
+        ldx = d.k + (8 - d.k % 8) % 8
+    if ws_bytes is None:
+        ws_bytes = lib().rq_workspace_bytes()
+    p = _Plan()
+    st = lib().rq_plan_small_m(ctypes.byref(d), m, ldx, ws_bytes, ctypes.byref(p))
+    _check(st, "rq_plan_small_m")
+    return {name: getattr(p, name) for name, _ in _Plan._fields_}
 
 
 def rq_gemm_small_m_noalloc(x, m, ldx, w, y, ldy, stream=None):

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 3
+#define RQ_ABI_VERSION 4
 
 enum rq_status {
   RQ_OK = 0,
@@ -256,6 +256,47 @@ int rq_gemv_f16(const uint16_t *x, const rq_qweight *w, uint16_t *y, void *works
  * 8192 at m > 16 and 16384 at m = 4..8).  Other formats take any shape. */
 int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight *w,
                     uint16_t *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The launch rq_gemm_small_m would make for weight w, m rows of x with row
+ * stride ldx and a workspace of workspace_bytes (0: none), described
+ * without launching (the same planner; host only, no GPU call, nothing is
+ * read through w's buffer pointers).  For callers that size workspaces, pick
+ * batch sizes or check a launch shape ahead of graph capture.
+ * kernel: RQ_PLAN_NONE when nothing would be launched (m == 0 or n == 0);
+ *   RQ_PLAN_STREAMING: one workgroup per group of tiles per K slice, the
+ *   activation slice copied once into LDS; RQ_PLAN_TWO_RANGES: the same on
+ *   8-row tiles that each cover K as two halves (int4 groups, m <= 8);
+ *   RQ_PLAN_STREAMED_X: each wave streams its own chunks of x; RQ_PLAN_PHASED:
+ *   x, codes and scales moved through LDS in phases of 512 k (int4 groups,
+ *   m > 16); RQ_PLAN_FIRST: the one-tile-per-workgroup kernel.
+ * split > 1: K is cut into split slices of chunks_per_slice chunks (128 k
+ * for 4-, 5-, 6-bit codes and SB256, 64 k for int8, 32 k for fp16/bf16), the
+ * partial tiles take workspace_bytes of the workspace and a second kernel
+ * adds them.  lds_bytes: dynamic LDS of the main launch; threads: per
+ * workgroup.  Errors as rq_gemm_small_m's validation (the buffer pointers
+ * must be valid descriptors but are not dereferenced; ldx as for x there),
+ * RQ_ERR_SHAPE when no launch shape exists, RQ_ERR_NULL for a null out. */
+enum {
+  RQ_PLAN_NONE = 0,
+  RQ_PLAN_STREAMING = 1,
+  RQ_PLAN_TWO_RANGES = 2,
+  RQ_PLAN_STREAMED_X = 3,
+  RQ_PLAN_PHASED = 4,
+  RQ_PLAN_FIRST = 5
+};
+typedef struct rq_plan {
+  int32_t kernel;              /* RQ_PLAN_* */
+  int32_t split;               /* K slices */
+  int32_t chunks_per_slice;
+  int32_t chunks_per_wave;     /* streaming kernels; 0 otherwise */
+  int32_t waves_per_tile;      /* streaming kernels; 0 otherwise */
+  int32_t tiles_per_workgroup;
+  int32_t workgroups;          /* of the main launch */
+  int32_t threads;             /* per workgroup */
+  int64_t lds_bytes;
+  int64_t workspace_bytes;
+} rq_plan;
+int rq_plan_small_m(const rq_qweight *w, int64_t m, int64_t ldx, size_t workspace_bytes, rq_plan *out);
 
 /* rq_gemm_small_m for callers that cannot allocate device memory or pass a
  * workspace: code under HIP graph capture, tight serving loops, harnesses

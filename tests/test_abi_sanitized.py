@@ -1,9 +1,10 @@
-"""The C ABI tests (tests/test_abi.py) and the host proxy's parity tests
-(tests/test_proxy_parity.py) run against a build whose host-side
-layer -- argument validation, alias and alignment checks, byte-size helpers,
-the host conversions, rq_proxy -- is compiled with AddressSanitizer and
-UndefinedBehaviorSanitizer (CPU only: no call reaches a kernel).  Any
-sanitizer report fails the run."""
+"""The C ABI tests (tests/test_abi.py), the host proxy's parity tests
+(tests/test_proxy_parity.py) and the launch planner's tests
+(tests/test_plan.py) run against a build whose host-side layer -- argument
+validation, alias and alignment checks, byte-size helpers, the host
+conversions, rq_proxy, the small-M planner -- is compiled with
+AddressSanitizer and UndefinedBehaviorSanitizer (CPU only: no call reaches a
+kernel).  Any sanitizer report fails the run."""
 
 import os
 import subprocess
@@ -31,7 +32,8 @@ def test_abi_under_address_and_undefined_sanitizers():
         "HIP_VISIBLE_DEVICES": "",
     })
     r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_abi.py"),
-                        os.path.join(ROOT, "tests", "test_proxy_parity.py"), "-q",
+                        os.path.join(ROOT, "tests", "test_proxy_parity.py"),
+                        os.path.join(ROOT, "tests", "test_plan.py"), "-q",
                         "-p", "no:cacheprovider"], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     out = r.stdout + r.stderr
     assert "AddressSanitizer" not in out and "runtime error" not in out, out[-4000:]
