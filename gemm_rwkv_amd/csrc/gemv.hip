@@ -1170,15 +1170,18 @@ struct G6 {
   static constexpr int RS = P * 256 + 16;        // LDS bytes per activation row
   static constexpr int XR = 16 * MT;             // activation rows (one DMA each)
   static constexpr int CD = RT * P;              // code DMAs (4 rows x 256 bytes each)
-  static constexpr int ND = XR + CD + 64 / G;    // DMA reads per phase (one or two scale spans)
+  static constexpr int SR = RT * 16 > 64 ? RT * 16 : 64;  // scale rows held (one DMA per 64)
+  static constexpr int SP = 64 / G;              // 16-byte parts of a row's phase span
+  static constexpr int SD = SP * (SR / 64);      // scale DMAs per phase
+  static constexpr int ND = XR + CD + SD;        // DMA reads per phase
   static constexpr int DPW = (ND + NW - 1) / NW; // per wave, at most
   static constexpr int XB = XR * RS;
   static constexpr int CB = RT * 16 * P * 64;
-  static constexpr int SB = 2 * 64 * 16;         // scale spans: [2][64 rows][16 bytes]
+  static constexpr int SB = SP * SR * 16;        // scale spans: [SP][SR rows][16 bytes]
   static constexpr int BUF = XB + CB + SB;
   static constexpr size_t LDS = (size_t)NB * BUF;
   static_assert(PPW >= 1 && P * GPC == PPW * NW, "the pairs of a phase");
-  static_assert(RT * 16 <= 64, "one scale DMA covers the code rows");
+  static_assert(SR % 64 == 0 && SR >= RT * 16, "the scale DMAs cover the code rows");
   static_assert(NB * BUF >= (size_t)NW * RT * MT * 1024, "the reduction fits the buffers");
   static_assert((NB - 1) * DPW <= 63, "the phases in flight within the wait counter");
 };
@@ -1314,10 +1317,13 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
       const int seg = (lane & 15) ^ (row & 15);
       vo[i] = nn < A.n ? (uint32_t)nn * rowbytes + (uint32_t)cbeg * 64u + (uint32_t)seg * 16u : kOOB;
     } else {
+      // scale DMA u: span part u % SP of rows 64 (u / SP) + lane
       const int u = d - C::XR - C::CD;
-      const int nn = grp * RT * 16 + lane;
-      vo[i] = (lane < RT * 16 && nn < A.n) ? (uint32_t)nn * srow + (uint32_t)cbeg * (F::GPC * 2u) + (uint32_t)u * 16u
-                                           : kOOB;
+      const int part = u % C::SP, row = (u / C::SP) * 64 + lane;
+      const int nn = grp * RT * 16 + row;
+      vo[i] = (row < RT * 16 && nn < A.n)
+                  ? (uint32_t)nn * srow + (uint32_t)cbeg * (F::GPC * 2u) + (uint32_t)part * 16u
+                  : kOOB;
     }
   }
   auto dma = [&](int q, int b) {
@@ -1334,9 +1340,10 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
                      :: "v"(vo[i]), "s"(rc), "s"(qc), "s"(bb + (uint32_t)(C::XB + (d - C::XR) * 1024))
                      : "memory", "m0");
       } else if (d < C::ND) {
+        const int u = d - C::XR - C::CD;
         asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                      :: "v"(vo[i]), "s"(rsc), "s"(qs),
-                        "s"(bb + (uint32_t)(C::XB + C::CB + (d - C::XR - C::CD) * 1024))
+                        "s"(bb + (uint32_t)(C::XB + C::CB + ((u % C::SP) * C::SR + (u / C::SP) * 64) * 16))
                      : "memory", "m0");
       }
     }
@@ -1387,7 +1394,7 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
           wv[0] = *(const uint32_t*)(cr + (((b0 >> 4) ^ j) << 4));
           wv[1] = 0u;
         }
-        const uint32_t word = *(const uint32_t*)(bufp + C::XB + C::CB + (hh >> 3) * (64 * 16) + row * 16 +
+        const uint32_t word = *(const uint32_t*)(bufp + C::XB + C::CB + (hh >> 3) * (C::SR * 16) + row * 16 +
                                                  ((hh & 7) >> 1) * 4);
         const float v = f16_bits_to_f32((uint16_t)((hh & 1) ? (word >> 16) : (word & 0xffffu)));
         const float scl = tv[r] ? v : 0.f;
