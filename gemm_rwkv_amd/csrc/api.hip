@@ -70,12 +70,42 @@ int check_ws(const void* ws, size_t ws_bytes, const Span* io, int nio) {
 
 inline size_t ws_size(const void* ws, size_t ws_bytes) { return ws ? ws_bytes : 0; }
 
+// The workspace's layout: rq::kSplitCounterBytes of arrival counters for
+// the K-split weight-streaming products (zero whenever no call is running),
+// then the partial tiles of every product.  A workspace that holds nothing
+// past the counters counts as none.
+inline bool ws_usable(const void* ws, size_t ws_bytes) { return ws && ws_bytes > rq::kSplitCounterBytes; }
+
+void set_gemv_ws(rq::GemvBatch& b, void* ws, size_t ws_bytes) {
+  if (ws_usable(ws, ws_bytes)) {
+    b.cnt = (uint32_t*)ws;
+    b.ws = (float*)((uint8_t*)ws + rq::kSplitCounterBytes);
+    b.ws_bytes = ws_bytes - rq::kSplitCounterBytes;
+  } else {
+    b.cnt = nullptr;
+    b.ws = nullptr;
+    b.ws_bytes = 0;
+  }
+}
+
+// partial tiles of the dense GEMMs: after the counters, which they leave alone
+inline void* parts_of(void* ws, size_t ws_bytes) {
+  return ws_usable(ws, ws_bytes) ? (void*)((uint8_t*)ws + rq::kSplitCounterBytes) : nullptr;
+}
+inline size_t parts_bytes(const void* ws, size_t ws_bytes) {
+  return ws_usable(ws, ws_bytes) ? ws_bytes - rq::kSplitCounterBytes : 0;
+}
+
 // Scratch of rq_gemm_small_m_noalloc: the K-split partial sums live in this
 // file-scope device array instead of a workspace, one copy per GPU, kept
 // until the process ends.  Its host-side name is not a device address: the
 // address of each GPU's copy is taken once, with that GPU current, by
-// hipGetSymbolAddress, and only that address is handed to kernels.
-constexpr size_t kScratchBytes = (size_t)8 << 20;
+// hipGetSymbolAddress, and only that address is handed to kernels.  It is
+// laid out as a workspace: the split counters (zero-initialized with the
+// array when the code object is loaded, and left at zero by every call),
+// then 8 MiB for the partial tiles.
+constexpr size_t kScratchParts = (size_t)8 << 20;
+constexpr size_t kScratchBytes = rq::kSplitCounterBytes + kScratchParts;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
@@ -128,8 +158,7 @@ int small_m(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   b.m = (int)m;
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
-  b.ws = (float*)ws;
-  b.ws_bytes = ws_size(ws, ws_bytes);
+  set_gemv_ws(b, ws, ws_size(ws, ws_bytes));
   return gemv_status(rq::launch_gemv(b, gf, w->group, S(stream)));
 }
 
@@ -162,8 +191,8 @@ int gemm_w4(const uint16_t* x, int64_t m, int64_t ldx, const rq_qweight* w, uint
   p.k = (int)w->k;
   p.ldx = (int)ldx;
   p.ldy = (int)ldy;
-  return hip_status(rq::launch_gemm_w4(p, w->format == RQ_W4_ASYM_SB256, w->group, (float*)ws,
-                                       ws_size(ws, ws_bytes), S(stream)));
+  return hip_status(rq::launch_gemm_w4(p, w->format == RQ_W4_ASYM_SB256, w->group, (float*)parts_of(ws, ws_bytes),
+                                       parts_bytes(ws, ws_bytes), S(stream)));
 }
 
 int w8a8(const void* xq, const float* sx, int64_t m, const rq_qweight* w, uint16_t* y, int64_t ldy,
@@ -193,8 +222,8 @@ int w8a8(const void* xq, const float* sx, int64_t m, const rq_qweight* w, uint16
   if ((st = check_ws(ws, ws_bytes, ins, 8)) != RQ_OK) return st;
   if (m == 0 || w->n == 0) return RQ_OK;
   return hip_status(rq::launch_gemm_w8a8(xq, sx, (int)m, w->codes, (const float*)w->scales, (int)w->n,
-                                         (int)w->k, want_format == RQ_FP8_E4M3_CH, y, (int)ldy, acc, ws,
-                                         ws_size(ws, ws_bytes), S(stream)));
+                                         (int)w->k, want_format == RQ_FP8_E4M3_CH, y, (int)ldy, acc,
+                                         parts_of(ws, ws_bytes), parts_bytes(ws, ws_bytes), S(stream)));
 }
 
 }  // namespace
@@ -343,8 +372,7 @@ int rq_plan_small_m(const rq_qweight* w, int64_t m, int64_t ldx, size_t ws_bytes
   b.ldx = (int)ldx;
   b.ldy = (int)w->n;
   // the planner only asks whether a workspace exists and how large it is
-  b.ws = ws_bytes ? (float*)(uintptr_t)256 : nullptr;
-  b.ws_bytes = ws_bytes;
+  set_gemv_ws(b, ws_bytes ? (void*)(uintptr_t)256 : nullptr, ws_bytes);
   rq::GemvPlanInfo p;
   if (!rq::plan_gemv(b, gf, w->group, p)) return RQ_ERR_SHAPE;
   out->kernel = p.kernel;
@@ -356,7 +384,7 @@ int rq_plan_small_m(const rq_qweight* w, int64_t m, int64_t ldx, size_t ws_bytes
   out->workgroups = p.workgroups;
   out->threads = p.threads;
   out->lds_bytes = (int64_t)p.lds;
-  out->workspace_bytes = (int64_t)p.ws_used;
+  out->workspace_bytes = (int64_t)(p.split > 1 ? rq::kSplitCounterBytes + p.ws_used : 0);
   return RQ_OK;
 }
 
@@ -401,8 +429,7 @@ int rq_fused_rkv(const uint16_t* xr, const uint16_t* xk, const uint16_t* xv, int
   b.m = (int)m;
   b.ldx = (int)ldx;
   b.ldy = (int)ldy;
-  b.ws = (float*)wsp;
-  b.ws_bytes = ws_size(wsp, ws_bytes);
+  set_gemv_ws(b, wsp, ws_size(wsp, ws_bytes));
   return gemv_status(rq::launch_gemv(b, gf, wr->group, S(stream)));
 }
 
@@ -462,7 +489,7 @@ int rq_gemm_small_m_noalloc(const uint16_t* x, int64_t m, int64_t ldx, const rq_
   // scratch: at most 16 K slices of 16-row tiles, each tile 1 KiB per
   // 16 activation rows (so the plan equals that of a full workspace)
   const int64_t mt = m <= 16 ? 1 : 2;
-  if (w->n > 0 && 16 * ((w->n + 15) / 16) * mt * 1024 > (int64_t)kScratchBytes) return RQ_ERR_SCRATCH;
+  if (w->n > 0 && 16 * ((w->n + 15) / 16) * mt * 1024 > (int64_t)kScratchParts) return RQ_ERR_SCRATCH;
   return small_m(x, m, ldx, w, y, ldy, nullptr, kScratchBytes, stream, 0, 0, scratch_address);
 }
 

@@ -413,7 +413,7 @@ constexpr int x_const(int g, int p) {
 
 // bytes of LDS for a workgroup's activation slice: 80 KB keeps two
 // workgroups per compute unit; an unsplit launch may take up to 150 KB (one
-// per compute unit) rather than pay for a second, reducing kernel
+// per compute unit) rather than pay for a K split's partial tiles
 constexpr int kXBudget = 80 * 1024;
 constexpr int kXBudgetUnsplit = 150 * 1024;
 // largest M that the two-range plan takes (two k ranges of up to 8 rows fill
@@ -435,9 +435,11 @@ constexpr int kRangesMaxM = 8;
 //
 // K is cut into `split` slices of cps chunks.  The waves of a tile reduce
 // through LDS in wave order; with split = 1 they store fp16, otherwise each
-// workgroup stores its fp32 partial tile group in the workspace and a second
-// kernel adds the `split` partials in slice order (deterministic, no atomics
-// or cross-workgroup fences).  Splitting feeds the compute units when there
+// workgroup stores its fp32 partial tile group in the workspace, and the
+// `split` partials are added in slice order (deterministic, no floating-point
+// atomics): by the last of the tile group's workgroups to finish, in the same
+// launch, for up to kSplitInLaunch slices (split_arrive / split_finish), by a
+// second kernel for more.  Splitting feeds the compute units when there
 // are few row tiles, and keeps the LDS slice of x small when M * K is large;
 // RT tiles per workgroup share one slice.
 struct Split5 {
@@ -548,6 +550,92 @@ __device__ __forceinline__ void wait_vm_st(int n) {
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
+// ---------------------------------------------------------------------------
+// K split added up inside the launch
+// ---------------------------------------------------------------------------
+// The `split` workgroups of a tile group (one per K slice) each store their
+// fp32 partial tile with agent-scope stores, which are coherent across the
+// XCDs' separate L2 caches, wait until those stores have completed, and then
+// count themselves in on the tile group's counter.  The workgroup that arrives
+// last reads the split partial tiles back with agent-scope loads, adds them in
+// slice order (the same order, so the same bits, whichever workgroup arrives
+// last) and stores fp16.  The increment wraps modulo split, so that last
+// arrival also returns the counter to zero for the next call.  No cache-wide
+// fence is needed (those write back or invalidate a whole XCD L2): the data
+// itself is stored and loaded coherently, the counter is updated only after
+// the stores completed, and the reads are issued only after the update returned.
+// Up to kSplitInLaunch slices the last workgroup adds them; more slices
+// leave more partial bytes to that one workgroup than a second, reducing
+// kernel spread over the whole chip costs (measured: 4096x16384 at M = 16,
+// eight slices, 16.4 us with the second kernel against 18.8 us in launch;
+// four slices, 2048x8192 at M = 16 and 4096x16384 at M = 32: 8.6 -> 7.8 and
+// 18.2 -> 17.0 us in launch).
+constexpr int kSplitInLaunch = 4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kSC1 = 16;  // cache-policy operand of the buffer builtins: sc1 (agent scope)
+// buffer resource over the tile group's partial tiles, split * ent floats
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(float* part, int split, int ent) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, split * ent * 4, 0x00020000);
+}
+// four consecutive outputs idx .. idx + 3 of slice s: stored coherently
+// (agent scope) for the in-launch sums, plainly for the second kernel, which
+// the kernel boundary orders after them
+__device__ __forceinline__ void part_store4(__amdgpu_buffer_rsrc_t r, int s, int ent, int idx, float4v v,
+                                            bool coherent) {
+  // (whole-vector bit casts only: a bit cast of one vector element reads
+  // element 0 with this compiler)
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  if (coherent)
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, (uint32_t)idx * 4u, (uint32_t)(s * ent) * 4u, kSC1);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, (uint32_t)idx * 4u, (uint32_t)(s * ent) * 4u, 0);
+}
+// true, in every thread, for the workgroup that arrives last at counter c;
+// flag: an LDS word no thread reads or writes at this point
+__device__ __forceinline__ bool split_arrive(uint32_t* c, int split, uint32_t* flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __builtin_amdgcn_atomic_inc32(c, (uint32_t)(split - 1), __ATOMIC_RELAXED, "agent");
+  __syncthreads();
+  return *flag == (uint32_t)(split - 1);
+}
+// The last workgroup's sums: the tile group's ent outputs (RT tiles x MT
+// activation tiles x 256), four consecutive ones per thread, every slice's
+// load issued before the first add
+template <int MT>
+__device__ __forceinline__ void split_finish(__amdgpu_buffer_rsrc_t r, int split, int ent, int rt, int grp, int M,
+                                             int ldy, const GemvMatrix& A) {
+  constexpr int E = MT * 4 * 64;
+  for (int i4 = threadIdx.x; i4 < ent / 4; i4 += blockDim.x) {
+    float4v vals[16];
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2)
+      if (s2 < split)
+        vals[s2] = __builtin_bit_cast(
+            float4v, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)i4 * 16u, (uint32_t)(s2 * ent) * 4u, kSC1));
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = vals[0][c];
+#pragma unroll
+    for (int s2 = 1; s2 < 16; ++s2)
+      if (s2 < split)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] += vals[s2][c];
+    const int idx = 4 * i4;
+    const int rr = idx / E, e = idx - rr * E;
+    const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
+    const int m = t * 16 + 4 * (l >> 4) + q;
+    const int nn = (grp * rt + rr) * 16 + (l & 15);
+    if (m < M) {
+      uint16_t* yr = A.y + (size_t)m * ldy;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (nn + c < A.n) yr[nn + c] = f32_to_f16_bits(v[c]);
+    }
+  }
+}
+
 template <int FMT, int G, int MT, int CPW, int MR, bool ST = false, int H = 1>
 __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
@@ -1064,25 +1152,42 @@ __global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Sp
   }
   constexpr int E = MT * 4 * 64;  // outputs of one row tile (rows m < 16 MT)
   const int ent = sp.rt * E;
-  float* part = sp.split > 1 ? p.ws + ((size_t)gall * sp.split + s) * ent : nullptr;
+  if (sp.split > 1) {
+    // four consecutive outputs per thread (same row tile, activation tile
+    // and q; lanes l .. l + 3)
+    const __amdgpu_buffer_rsrc_t rp = part_rsrc(p.ws + (size_t)gall * sp.split * ent, sp.split, ent);
+    for (int i4 = threadIdx.x; i4 < ent / 4; i4 += blockDim.x) {
+      const int idx = 4 * i4;
+      const int rr = idx / E, e = idx - rr * E;
+      const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
+      float4v v = *(const float4v*)&red[rr * sp.wpt][t][q][l];
+      for (int w2 = 1; w2 < sp.wpt; ++w2) {
+        const float4v u = *(const float4v*)&red[rr * sp.wpt + w2][t][q][l];
+        v[0] += u[0];
+        v[1] += u[1];
+        v[2] += u[2];
+        v[3] += u[3];
+      }
+      part_store4(rp, s, ent, idx, v, sp.split <= kSplitInLaunch);
+    }
+    if (sp.split <= kSplitInLaunch && split_arrive(p.cnt + gall, sp.split, (uint32_t*)lds4))
+      split_finish<MT>(rp, sp.split, ent, sp.rt, grp, M, p.ldy, A);
+    return;
+  }
   for (int idx = threadIdx.x; idx < ent; idx += blockDim.x) {
     const int rr = idx / E, e = idx - rr * E;
     const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
     float v = red[rr * sp.wpt][t][q][l];
     for (int w2 = 1; w2 < sp.wpt; ++w2) v += red[rr * sp.wpt + w2][t][q][l];
-    if (part) {
-      part[idx] = v;
-    } else {
-      const int m = t * 16 + 4 * (l >> 4) + q;
-      const int nn = (grp * sp.rt + rr) * 16 + (l & 15);
-      if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
-    }
+    const int m = t * 16 + 4 * (l >> 4) + q;
+    const int nn = (grp * sp.rt + rr) * 16 + (l & 15);
+    if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
   }
 }
 
-// Split K, second step: y = fp16(sum of the `split` partial tiles, in slice
-// order), one thread per output of a tile group.  The kernel boundary orders
-// it after every slice's stores.
+// Split K over more than kSplitInLaunch slices, second step: y = fp16(sum of
+// the `split` partial tiles, in slice order), one thread per output of a tile
+// group.  The kernel boundary orders it after every slice's stores.
 template <int MT>
 __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, const Split5 sp) {
   constexpr int E = MT * 4 * 64;
@@ -1128,7 +1233,7 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
 // For batches that fill two activation tiles, staging a workgroup's whole
 // activation slice before any math (the streaming kernel above) either caps
 // the slice at what LDS holds, so that K is split into many slices whose
-// fp32 partial tiles a second kernel adds, or (one row tile per workgroup)
+// fp32 partial tiles must all be added, or (one row tile per workgroup)
 // makes every workgroup read all of x.  Here the slice is cut into phases of
 // P = 4 chunks (512 k), each moved into one of NB LDS buffers (three for two
 // activation tiles, four for one) by LDS DMA reads, NB - 1 phases ahead: the
@@ -1155,7 +1260,7 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
 // an operand read fall in distinct banks.  Decode and scaling are those of
 // the streaming kernel (symmetric int4).
 struct Plan6 {
-  int split;      // K slices (partial tiles summed by gemv5_reduce_kernel)
+  int split;      // K slices (partial tiles added in launch up to kSplitInLaunch, else by gemv5_reduce_kernel)
   int cps;        // chunks per slice, a multiple of 4
   int groups[3];  // tile groups (of RT tiles) per matrix
 };
@@ -1429,7 +1534,6 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
   // the eight waves' partial sums of each output, added in wave order
   constexpr int E = MT * 4 * 64;  // outputs of one row tile (rows m < 16 MT)
   const int ent = RT * E;
-  float* part = sp.split > 1 ? p.ws + ((size_t)gall * sp.split + s) * ent : nullptr;
   float (*red)[RT][MT][4][64] = (float (*)[RT][MT][4][64])lds4;
   __syncthreads();  // every wave is done with the buffers
 #pragma unroll
@@ -1439,19 +1543,37 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
 #pragma unroll
       for (int q = 0; q < 4; ++q) red[wave][r][t][q][lane] = acc[r][t][q];
   __syncthreads();
+  if (sp.split > 1) {
+    // four consecutive outputs per thread (lanes l .. l + 3)
+    const __amdgpu_buffer_rsrc_t rp = part_rsrc(p.ws + (size_t)gall * sp.split * ent, sp.split, ent);
+    for (int i4 = threadIdx.x; i4 < ent / 4; i4 += blockDim.x) {
+      const int idx = 4 * i4;
+      const int rr = idx / E, e = idx - rr * E;
+      const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
+      float4v v = *(const float4v*)&red[0][rr][t][q][l];
+#pragma unroll
+      for (int w2 = 1; w2 < C::NW; ++w2) {
+        const float4v u = *(const float4v*)&red[w2][rr][t][q][l];
+        v[0] += u[0];
+        v[1] += u[1];
+        v[2] += u[2];
+        v[3] += u[3];
+      }
+      part_store4(rp, s, ent, idx, v, sp.split <= kSplitInLaunch);
+    }
+    if (sp.split <= kSplitInLaunch && split_arrive(p.cnt + gall, sp.split, (uint32_t*)lds4))
+      split_finish<MT>(rp, sp.split, ent, RT, grp, M, p.ldy, A);
+    return;
+  }
   for (int idx = threadIdx.x; idx < ent; idx += blockDim.x) {
     const int rr = idx / E, e = idx - rr * E;
     const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
     float v = red[0][rr][t][q][l];
 #pragma unroll
     for (int w2 = 1; w2 < C::NW; ++w2) v += red[w2][rr][t][q][l];
-    if (part) {
-      part[idx] = v;
-    } else {
-      const int m = t * 16 + 4 * (l >> 4) + q;
-      const int nn = (grp * RT + rr) * 16 + (l & 15);
-      if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
-    }
+    const int m = t * 16 + 4 * (l >> 4) + q;
+    const int nn = (grp * RT + rr) * 16 + (l & 15);
+    if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
   }
 }
 
@@ -1496,7 +1618,9 @@ static bool plan6(const GemvBatch& b, int group, Shape6& sh) {
   split = (nchunks + cps - 1) / cps;
   const int mt = b.m <= 16 ? 1 : 2;
   if (groups(rt) * split < 192) return false;
-  if (split > 1 && (!b.ws || (size_t)groups(rt) * split * rt * mt * 1024 > b.ws_bytes)) return false;
+  if (split > 1 && (!b.ws || (split <= kSplitInLaunch && (!b.cnt || groups(rt) > kSplitCounters)) ||
+                    (size_t)groups(rt) * split * rt * mt * 1024 > b.ws_bytes))
+    return false;
   sh.rt = rt;
   sh.plan.split = split;
   sh.plan.cps = cps;
@@ -1526,7 +1650,7 @@ static bool launch6(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   if (mt == 2) RQ_L6(2, kG6Rt); else RQ_L6(1, kG6Rt);
 #undef RQ_L6
   err = hipGetLastError();
-  if (err == hipSuccess && sh.plan.split > 1) {
+  if (err == hipSuccess && sh.plan.split > kSplitInLaunch) {
     Split5 sp5;
     sp5.split = sh.plan.split;
     sp5.cps = sh.plan.cps;
@@ -1618,7 +1742,7 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     const int used = (nchunks + cps - 1) / cps;
     const int wpt = (cps + 3) / 4;
     const size_t xb = (size_t)(b.m + 1) * (cps * F::CK + 8) * 2;
-    if (b.ws && b.m <= 4 && tiles < 256 && nchunks >= 64 && wpt <= 16 && xb <= (size_t)kXBudget &&
+    if (b.ws && b.cnt && b.m <= 4 && tiles < 256 && nchunks >= 64 && wpt <= 16 && xb <= (size_t)kXBudget &&
         (size_t)tiles * used * mt * 1024 <= b.ws_bytes) {
       sp.split = used;
       sp.cps = cps;
@@ -1758,7 +1882,9 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     while (share_x && rt < 4 && 2 * rt * wpt <= 16 &&
            (!one_round(rt) || (x_heavy(rt) && groups(2 * rt) * used >= 256)))
       rt *= 2;
-    if (used > 1 && (size_t)groups(rt) * rt * used * mt * 1024 > b.ws_bytes) break;
+    if (used > 1 && ((used <= kSplitInLaunch && (!b.cnt || groups(rt) > kSplitCounters)) ||
+                     (size_t)groups(rt) * rt * used * mt * 1024 > b.ws_bytes))
+      break;
     sp.split = used;
     sp.cps = cps;
     sp.wpt = wpt;
@@ -1766,8 +1892,9 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? (b.mat[i].tiles + rt - 1) / rt : 0;
     cpw_out = cpw;
     found = true;
-    // a split costs a second launch: worth it only to occupy more than half
-    // of the compute units, or to fit the activations
+    // a split costs the partial tiles' round trip through the workspace and
+    // the last workgroups' sums: worth it only to occupy more than half of
+    // the compute units, or to fit the activations
     if (groups(rt) * used >= (used == 1 ? 128 : 256)) break;
   }
   if (!found && have_unsplit) {
@@ -1878,7 +2005,7 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   }
 #undef RQ_L5
   err = hipGetLastError();
-  if (err == hipSuccess && sp.split > 1) {
+  if (err == hipSuccess && sp.split > kSplitInLaunch) {
     const int outs = gtot * sp.rt * mt * 256;
     const dim3 rgrid((unsigned)((outs + 255) / 256));
     if (mt == 2)

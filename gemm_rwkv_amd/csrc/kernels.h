@@ -43,13 +43,23 @@ struct GemvBatch {
   int ldx;
   int ldy;
   // caller's workspace for products split along K (null: no split): fp32
-  // partial tiles, summed by a second kernel; the planner keeps within ws_bytes
+  // partial tiles (the planner keeps within ws_bytes), and one arrival
+  // counter per tile group (zero between calls) through which, for a split
+  // of up to four slices, the workgroup that finishes a tile group last finds
+  // itself and adds the partial tiles (a second kernel adds more slices)
   float* ws;
   size_t ws_bytes;
+  uint32_t* cnt;
 };
 
 // workspace size that admits every product's fastest plan
 constexpr size_t kWorkspaceBytes = 64u << 20;
+// The workspace starts with the arrival counters of the K-split weight-
+// streaming products (one 32-bit word per tile group, zero whenever no call
+// is running: zero-filled by the caller once, and every call leaves them at
+// zero); the partial tiles of every product follow them.
+constexpr size_t kSplitCounterBytes = 64u << 10;
+constexpr int kSplitCounters = (int)(kSplitCounterBytes / 4);
 
 hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 
@@ -58,7 +68,7 @@ hipError_t launch_gemv(const GemvBatch& b, int fmt, int group, hipStream_t st);
 // shape (launch_gemv returns hipErrorInvalidConfiguration).
 struct GemvPlanInfo {
   int kernel;      // 1 streaming, 2 streaming with two k ranges, 3 streamed activations, 4 phased, 5 first version
-  int split;       // K slices (> 1: partial tiles in the workspace and a reducing launch)
+  int split;       // K slices (> 1: partial tiles in the workspace, added in launch up to 4, else by a second kernel)
   int cps;         // chunks per slice (streaming, phased)
   int cpw;         // chunks per wave (streaming)
   int wpt;         // waves per row tile (streaming)
@@ -66,7 +76,7 @@ struct GemvPlanInfo {
   int workgroups;  // of the main launch
   int threads;     // per workgroup
   size_t lds;      // dynamic LDS of the main launch, bytes
-  size_t ws_used;  // workspace bytes the partial tiles take
+  size_t ws_used;  // workspace bytes the partial tiles take (after the counters)
 };
 bool plan_gemv(const GemvBatch& b, int fmt, int group, GemvPlanInfo& out);
 

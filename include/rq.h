@@ -19,19 +19,26 @@
  *     after returning.
  *   - Workspace: the products (rq_gemv_*, rq_gemm_small_m, rq_fused_rkv,
  *     rq_gemm_w4, rq_gemm_fp8, rq_gemm_int8, rq_gemm_int8_acc) may cut K
- *     across workgroups and add the partial sums in a second kernel.  The
- *     partial sums live in a device buffer the CALLER owns and passes as
+ *     across workgroups and add the partial sums afterwards.  The partial
+ *     sums live in a device buffer the CALLER owns and passes as
  *     (workspace, workspace_bytes): 16-byte aligned, disjoint from the call's
- *     inputs and outputs (RQ_ERR_ALIGN, RQ_ERR_ALIAS).  rq_workspace_bytes()
- *     is the size that admits every product's fastest launch shape; with a
- *     smaller buffer, or workspace == NULL (workspace_bytes is then ignored),
- *     the planner keeps to the shapes that fit, down to no K split at all.
- *     The launch shape is a function of the arguments alone (shapes, formats,
- *     whether a workspace is given and its size), never of earlier calls.  No
- *     product call allocates device memory.  The workspace holds nothing
- *     between calls, but calls that may run at the same time (on different
- *     streams, or graph replays on different streams) need distinct
- *     workspaces.
+ *     inputs and outputs (RQ_ERR_ALIGN, RQ_ERR_ALIAS).  Its first 64 KiB hold
+ *     the arrival counters through which the weight-streaming products
+ *     (rq_gemv_*, rq_gemm_small_m, rq_fused_rkv) let the last workgroup of
+ *     each tile group split into up to four K slices add the partial sums,
+ *     in the same launch (more slices are added by a second kernel): the
+ *     caller ZERO-FILLS them once, before the buffer's first use (e.g. one
+ *     hipMemset of the whole buffer after allocating it), and every call
+ *     leaves them at zero when it completes.  Bytes past the first 64 KiB
+ *     hold nothing between calls.  rq_workspace_bytes() is the size that
+ *     admits every product's fastest launch shape; with a smaller buffer (64
+ *     KiB or less counts as none), or workspace == NULL (workspace_bytes is
+ *     then ignored), the planner keeps to the shapes that fit, down to no K
+ *     split at all.  The launch shape is a function of the arguments alone
+ *     (shapes, formats, whether a workspace is given and its size), never of
+ *     earlier calls.  No product call allocates device memory.  Calls that
+ *     may run at the same time (on different streams, or graph replays on
+ *     different streams) need distinct workspaces.
  *   - fp16 values are IEEE binary16 bit patterns (uint16_t).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it; product calls return without synchronizing.
@@ -63,7 +70,7 @@
 extern "C" {
 #endif
 
-#define RQ_ABI_VERSION 4
+#define RQ_ABI_VERSION 5
 
 enum rq_status {
   RQ_OK = 0,
@@ -271,8 +278,9 @@ int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight 
  *   m > 16); RQ_PLAN_FIRST: the one-tile-per-workgroup kernel.
  * split > 1: K is cut into split slices of chunks_per_slice chunks (128 k
  * for 4-, 5-, 6-bit codes and SB256, 64 k for int8, 32 k for fp16/bf16), the
- * partial tiles take workspace_bytes of the workspace and a second kernel
- * adds them.  lds_bytes: dynamic LDS of the main launch; threads: per
+ * counters and partial tiles take the first workspace_bytes of the workspace;
+ * the last workgroup of each tile group adds them in the same launch for
+ * split <= 4 (at most 16384 tile groups), a second kernel for more slices.  lds_bytes: dynamic LDS of the main launch; threads: per
  * workgroup.  Errors as rq_gemm_small_m's validation (the buffer pointers
  * must be valid descriptors but are not dereferenced; ldx as for x there),
  * RQ_ERR_SHAPE when no launch shape exists, RQ_ERR_NULL for a null out. */
@@ -303,8 +311,9 @@ int rq_plan_small_m(const rq_qweight *w, int64_t m, int64_t ldx, size_t workspac
  * that forbid hipMalloc.  Same arguments, formats and results as
  * rq_gemm_small_m given a workspace of rq_workspace_bytes() (the same launch
  * shape, so the same bits).  Its K-split partial sums use a static device
- * array of 8 MiB per GPU, owned by the library and held until the process
- * ends; a call allocates nothing.  Limit: 16 * ceil(n / 16) * t * 1024 bytes
+ * array of 8 MiB per GPU (after 64 KiB of split counters, zero when the
+ * library is loaded and left at zero by every call), owned by the library and
+ * held until the process ends; a call allocates nothing.  Limit: 16 * ceil(n / 16) * t * 1024 bytes
  * must fit in 8 MiB, t = 1 for m <= 16 and 2 above (n <= 4096 at any m,
  * n <= 8192 at m <= 16); larger calls return RQ_ERR_SCRATCH.  Every call on
  * a GPU shares that GPU's array: calls that overlap in time on one GPU

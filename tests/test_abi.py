@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = rq.lib()
-    assert L.rq_abi_version() == 4
+    assert L.rq_abi_version() == 5
     assert rq.rq_workspace_bytes() == 64 << 20
     for st in range(-10, 1):
         assert rq.status_str(st) and rq.status_str(st) != "unknown status"
