@@ -905,6 +905,57 @@ def cpu_baseline(c, budget_s=12.0):
     return out
 
 
+def vendor_gemm(gen, dev, ms=(64, 256, 1024), reps=20):
+    """Context, not the product: the library's fp8 and int8 GEMMs beside the
+    vendor library's (hipBLASLt through torch._scaled_mm with per-tensor
+    scales and fp16 output, and torch._int_mm) at the 7.2B-width prefill
+    shapes.  Each side runs back to back over rotated weight copies (over
+    1 GiB) in one captured graph per shape; activations are quantized
+    beforehand.  us per product, median over at least 200 dispatches."""
+    shapes = [("R/K/V/O", C3, C3), ("cmix key", 4 * C3, C3), ("cmix value", C3, 4 * C3)]
+    out = {}
+    for name, n, k in shapes:
+        copies = max(4, -(-ROTATE_BYTES // (n * k)))
+        ours8 = [rq.quantize(torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5), rq.RQ_FP8_E4M3_CH)
+                 for _ in range(copies)]
+        ours_i = [rq.quantize(torch.randn(n, k, generator=gen, device=dev) * (1.0 / k ** 0.5), rq.RQ_I8_CH)
+                  for _ in range(copies)]
+        # the vendor side multiplies the same code bytes, viewed as torch fp8 / int8 tensors [n][k]
+        v8 = [w.codes.view(torch.float8_e4m3fn).view(n, k) for w in ours8]
+        vi = [w.codes.view(torch.int8).view(n, k) for w in ours_i]
+        one = torch.ones((), device=dev, dtype=torch.float32)
+        for m in ms:
+            xa = f16_dev(synth.act_normal(m, k, 3), dev)
+            xq = torch.empty(m * k, dtype=torch.uint8, device=dev)
+            xqi = torch.empty(m * k, dtype=torch.uint8, device=dev)
+            sx = torch.empty(m, dtype=torch.float32, device=dev)
+            sxi = torch.empty(m, dtype=torch.float32, device=dev)
+            rq.rq_quantize_act(xa, m, k, k, rq.RQ_FP8_E4M3_CH, xq, sx)
+            rq.rq_quantize_act(xa, m, k, k, rq.RQ_I8_CH, xqi, sxi)
+            y = torch.empty(m * n, dtype=torch.int16, device=dev)
+            x8 = xq.view(torch.float8_e4m3fn).view(m, k)
+            x8i = xqi.view(torch.int8).view(m, k)
+            fl = 2.0 * m * n * k
+            row = {}
+            legs = [("fp8 library", lambda: [rq.rq_gemm_fp8(xq, sx, m, w, y, n) for w in ours8]),
+                    ("fp8 hipBLASLt", lambda: [torch._scaled_mm(x8, w.t(), scale_a=one, scale_b=one,
+                                                                out_dtype=torch.float16) for w in v8]),
+                    ("int8 library", lambda: [rq.rq_gemm_int8(xqi, sxi, m, w, y, n) for w in ours_i]),
+                    ("int8 hipBLASLt", lambda: [torch._int_mm(x8i, w.t()) for w in vi])]
+            for leg, fn in legs:
+                try:
+                    us = time_graph(capture(fn), reps, launches=copies) * 1e3 / copies
+                    row[leg] = {"us": round(us, 2), "TFLOP_s": round(fl / us / 1e6, 1)}
+                except Exception as e:  # a vendor path this torch build does not offer
+                    row[leg] = {"error": "%s: %s" % (type(e).__name__, str(e)[:160])}
+                torch.cuda.synchronize()
+            out["%s %dx%d M=%d" % (name, n, k, m)] = row
+            print("%-28s %s" % ("%s %dx%d M=%d" % (name, n, k, m), row), file=sys.stderr, flush=True)
+        del ours8, ours_i, v8, vi
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -922,6 +973,9 @@ def main():
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per kernel and launch shape: dispatches and mean duration, from a "
                          "rocprofv3 --kernel-trace CSV")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only the fp8/int8 GEMMs beside the vendor library's at the prefill shapes "
+                         "(context), one JSON line")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs of a --kernel-only run into HBM "
                          "bytes per launch (printed as the lines of a profiles/ summary)")
@@ -939,6 +993,9 @@ def main():
     torch.cuda.set_device(dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
+    if args.vendor_gemm:
+        print(json.dumps({"vendor_gemm": vendor_gemm(gen, dev)}))
+        return
 
     dec = Decode(C1, gen, dev)
     pre = Prefill(C3, M3, gen, dev)

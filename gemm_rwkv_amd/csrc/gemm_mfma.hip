@@ -338,6 +338,131 @@ __global__ void __launch_bounds__(64 * NW) gemm_w8a8_ring_kernel(const uint8_t* 
   }
 }
 
+// Large-tile variant for long prefill chunks: a 256 x 256 output tile per
+// workgroup of eight waves, wave (qm, qn) computing rows 128 qm .. + 127 and
+// columns 64 qn .. + 63 of it over all of K.  Every operand byte that reaches
+// the compute unit feeds 256 outputs instead of 128, which halves the
+// L2-to-LDS traffic per flop of the 128 x 128 ring; the price is LDS for only
+// two stages of 64 KB (one k block multiplied while the next is copied).  The
+// copy, swizzle and fragment reads are those of the ring kernel: 64 LDS DMA
+// reads of 8 rows x 128 B per k block, eight per wave; one barrier per block
+// tells that every wave's part of block j has landed and that block j - 1's
+// stage is free for block j + 1.  Taken where the 256 x 256 tiles alone fill
+// the 256 compute units (m >= 1024 with n >= 16384, for instance).
+template <bool FP8>
+__global__ void __launch_bounds__(512) gemm_w8a8_big_kernel(const uint8_t* __restrict__ xq,
+                                                            const float* __restrict__ sx, int M,
+                                                            const uint8_t* __restrict__ wq,
+                                                            const float* __restrict__ sw, int N, int K,
+                                                            uint16_t* __restrict__ y, int ldy,
+                                                            int32_t* __restrict__ acc_out) {
+  constexpr int BT = 256;                  // tile rows of x and of w
+  constexpr int SA = BT * 128;             // bytes of one operand's k block
+  constexpr int STAGE = 2 * SA;
+  constexpr int PER = 8;                   // DMA instructions per wave per block (64 / 8 waves)
+  typedef typename std::conditional<FP8, float4v, int4v>::type AccT;
+  extern __shared__ uint4 lds4[];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15;
+  const int q = lane >> 4;
+  const int m0 = blockIdx.y * BT;
+  const int n0 = blockIdx.x * BT;
+  const int nkb = K >> 7;
+  const int qm = wave >> 2, qn = wave & 3;  // 128-row half, 64-column quarter
+
+  // instruction g = wave * PER + u of a block takes rows 8 (g % 32) .. + 7
+  // of x (g < 32) or of w (g >= 32)
+  const int drow = lane >> 3, dslot = lane & 7;
+  const uint8_t* src[PER];
+  uint32_t dst[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int g = wave * PER + u;
+    const int r = 8 * (g & 31) + drow;
+    const int seg = (dslot ^ ((r >> 1) & 7)) << 4;
+    src[u] = g < 32 ? xq + (size_t)min(m0 + r, M - 1) * K + seg : wq + (size_t)min(n0 + r, N - 1) * K + seg;
+    dst[u] = (g < 32 ? 0 : SA) + (g & 31) * 1024;
+  }
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4;
+  auto dma = [&](int st, int kb) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const uint8_t* g = src[u] + (size_t)kb * 128;
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                   :: "v"(g), "s"(ring + st * STAGE + dst[u]) : "memory", "m0");
+    }
+  };
+
+  const int swz = (r16 >> 1) & 7;
+  const int o0 = r16 * 128 + (((2 * q) ^ swz) << 4);
+  const int o1 = r16 * 128 + (((2 * q + 1) ^ swz) << 4);
+  const uint8_t* abase = (const uint8_t*)lds4 + qm * 128 * 128;
+  const uint8_t* bbase = (const uint8_t*)lds4 + SA + qn * 64 * 128;
+
+  AccT acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = AccT{0, 0, 0, 0};
+
+  auto compute = [&](int st) {
+    uint4 fb[4][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      fb[b][0] = *(const uint4*)(bbase + st * STAGE + b * 2048 + o0);
+      fb[b][1] = *(const uint4*)(bbase + st * STAGE + b * 2048 + o1);
+    }
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const uint4 al = *(const uint4*)(abase + st * STAGE + a * 2048 + o0);
+      const uint4 ah = *(const uint4*)(abase + st * STAGE + a * 2048 + o1);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint4 bl = fb[b][0], bh = fb[b][1];
+        if constexpr (FP8) {
+          const int8v av = {(int)al.x, (int)al.y, (int)al.z, (int)al.w, (int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
+          const int8v bv = {(int)bl.x, (int)bl.y, (int)bl.z, (int)bl.w, (int)bh.x, (int)bh.y, (int)bh.z, (int)bh.w};
+          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[a][b], 0, 0, 0, 0, 0, 0);
+        } else {
+          const int4v a0 = {(int)al.x, (int)al.y, (int)al.z, (int)al.w};
+          const int4v b0 = {(int)bl.x, (int)bl.y, (int)bl.z, (int)bl.w};
+          const int4v a1 = {(int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
+          const int4v b1 = {(int)bh.x, (int)bh.y, (int)bh.z, (int)bh.w};
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc[a][b], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nkb > 0) dma(0, 0);
+  for (int j = 0; j < nkb; ++j) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of block j has landed
+    __syncthreads();  // every wave's part of block j is in; block j - 1's stage is free
+    if (j + 1 < nkb) dma((j + 1) & 1, j + 1);
+    compute(j & 1);
+  }
+
+  // epilogue: lane holds D[m = 4q + r][n = r16] of each 16 x 16 block
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int n = n0 + qn * 64 + b * 16 + r16;
+    if (n >= N) continue;
+    const float swn = y ? sw[n] : 0.f;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + qm * 128 + a * 16 + 4 * q + r;
+        if (m >= M) continue;
+        if (acc_out) acc_out[(size_t)m * N + n] = (int32_t)acc[a][b][r];
+        if (y) y[(size_t)m * ldy + n] = f32_to_f16_bits((float)acc[a][b][r] * sx[m] * swn);
+      }
+  }
+}
+
 // Split K, second step: the slices' tiles summed in slice order (fp32 for
 // fp8, exact int32 for int8), then scaled, one thread per output.
 template <bool FP8>
@@ -397,6 +522,19 @@ static hipError_t launch_w8a8_t(const void* xq, const float* sx, int m, const vo
                                 size_t ws_bytes, hipStream_t st) {
   // 128 x 128 tiles on a shared ring when they still make one workgroup per
   // compute unit
+  // 256 x 256 tiles where they alone fill the compute units
+  const long tiles256 = (long)((m + 255) / 256) * (long)((n + 255) / 256);
+  if (tiles256 >= 256) {
+    constexpr size_t lds = (size_t)2 * 2 * 256 * 128;
+    static const bool attr_set = hipFuncSetAttribute((const void*)gemm_w8a8_big_kernel<FP8>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)lds) == hipSuccess;
+    (void)attr_set;
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)((m + 255) / 256));
+    hipLaunchKernelGGL((gemm_w8a8_big_kernel<FP8>), grid, dim3(512), lds, st, (const uint8_t*)xq, sx, m,
+                       (const uint8_t*)wq, sw, n, k, y, ldy, acc_out);
+    return hipGetLastError();
+  }
   const long tiles128 = (long)((m + 127) / 128) * (long)((n + 127) / 128);
   if (tiles128 >= 256) {
     launch_ring<FP8>(xq, sx, m, wq, sw, n, k, y, ldy, acc_out, 1, nullptr, st);

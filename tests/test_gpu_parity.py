@@ -407,6 +407,41 @@ def test_w8a8_parity(kind, n, k, m):
         assert np.array_equal(got.astype(np.int64), ref.int_acc_ref(xq["codes"], parts["codes"]))
 
 
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+@pytest.mark.parametrize("n,k,m", [(16300, 384, 1000), (16384, 256, 1024), (16000, 128, 1100)])
+def test_w8a8_large_tiles(kind, n, k, m):
+    """256 x 256 tiles (256 or more of them fill the compute units on their
+    own): ragged m and n (1000 = 3 x 256 + 232 rows, 16300 = 63 x 256 + 172
+    columns), exact multiples, a single k block.  Sampled output columns,
+    the last ones included, against the oracle; int8 accumulators bit-exact."""
+    fmt = quant.FP8_E4M3_CH if kind == "fp8" else quant.I8_CH
+    w = _weights(n, k, n + k)
+    parts = quant.quantize(w, fmt)
+    qw = qweight_from_oracle(fmt, 0, parts, n, k)
+    x = np.random.default_rng(m + k).standard_normal((m, k)).astype(np.float16)
+    xq = quant.quantize_rows(x, kind)
+    y = Guarded(2 * m * n)
+    say("gemm large tiles", kind, "m", m, "n", n, "k", k)
+    f = rq.rq_gemm_fp8 if kind == "fp8" else rq.rq_gemm_int8
+    f(dev_bytes(xq["codes"]), dev_f32(xq["scales"]), m, qw, y.ptr(), n)
+    torch.cuda.synchronize()
+    y.check_guards()
+    out = host(y.t, np.float16).reshape(m, n)
+    g = np.random.default_rng(n)
+    cols = np.concatenate([np.sort(g.choice(n - 40, 88, replace=False)), np.arange(n - 40, n)])
+    sub = {name: arr[cols] for name, arr in parts.items()}
+    y_ref, b = ref.w8a8_ref(xq["codes"], xq["scales"], kind, fmt, sub)
+    ok, info = ref.compare(out[:, cols], y_ref, b)
+    assert ok, info
+    if kind == "int8":
+        acc = Guarded(4 * m * n)
+        rq.rq_gemm_int8_acc(dev_bytes(xq["codes"]), m, qw, acc.ptr())
+        torch.cuda.synchronize()
+        acc.check_guards()
+        got = host(acc.t, np.int32).reshape(m, n)[:, cols]
+        assert np.array_equal(got.astype(np.int64), ref.int_acc_ref(xq["codes"], parts["codes"][cols]))
+
+
 def test_fp8_integer_operands_exact():
     """Integer-valued e4m3fn operands with unit scales: the fp32 MFMA sum is
     exact whatever its order, and checks that the matrix core reads OCP e4m3fn."""
