@@ -38,6 +38,9 @@ def _plan(fmt, group, n, k, m, ws):
         return None
 
 
+COUNTERS = 64 << 10  # the workspace's leading split counters
+
+
 @pytest.mark.parametrize("fmt,group,ck", FORMATS)
 def test_plans_are_well_formed(fmt, group, ck):
     for n, k, m, ws in itertools.product(NS, KS, MS, (0, WS)):
@@ -55,7 +58,8 @@ def test_plans_are_well_formed(fmt, group, ck):
         assert 0 <= p["lds_bytes"] <= LDS_MAX, where
         assert p["workgroups"] >= 1 and p["split"] >= 1, where
         if p["split"] > 1:
-            assert ws > 0 and 0 < p["workspace_bytes"] <= ws, where
+            # the split counters (64 KiB) and then the partial tiles
+            assert ws > 0 and COUNTERS < p["workspace_bytes"] <= ws, where
         else:
             assert p["workspace_bytes"] == 0, where
         tiles16 = (n + 15) // 16
@@ -136,3 +140,19 @@ def test_plan_validation():
         rq.rq_plan_small_m((rq.RQ_FP8_E4M3_CH, 0, 2048, 2048), 1)
     assert e.value.status == rq.RQ_ERR_FORMAT
     assert rq.lib().rq_plan_small_m(None, 1, 2048, 0, None) == rq.RQ_ERR_NULL
+
+
+def test_workspace_without_room_past_the_counters_is_none():
+    """A workspace of 64 KiB or less holds only the split counters: every
+    product plans as with no workspace at all; one byte more admits a split
+    only where the partial tiles fit after the counters."""
+    for fmt, group, n, k, m in [(rq.RQ_W4_SYM, 64, 2048, 8192, 32), (rq.RQ_W4_SYM, 64, 4096, 16384, 16),
+                                (rq.RQ_W4_ASYM_SB256, 32, 2560, 10240, 1), (rq.RQ_W8_SYM, 16, 2560, 10240, 4)]:
+        none = _plan(fmt, group, n, k, m, 0)
+        full = _plan(fmt, group, n, k, m, WS)
+        assert full["split"] > 1, (fmt, n, k, m)
+        for ws in (1024, COUNTERS - 16, COUNTERS):
+            assert _plan(fmt, group, n, k, m, ws) == none, (fmt, n, k, m, ws)
+        assert _plan(fmt, group, n, k, m, full["workspace_bytes"]) == full, (fmt, n, k, m)
+        tight = _plan(fmt, group, n, k, m, full["workspace_bytes"] - 16)
+        assert tight["split"] == 1 or tight["workspace_bytes"] <= full["workspace_bytes"] - 16
