@@ -137,8 +137,10 @@ def default_workspace(device=None):
     """The binding's default workspace on a device: a uint8 tensor of
     rq_workspace_bytes(), allocated on first use and kept.  It is shared by
     every call that passes no workspace of its own, so such calls must not
-    run concurrently.  Allocating it while a graph is being captured is
-    refused: call this once before capturing."""
+    run concurrently.  It is zero-filled (its first 64 KiB are the split
+    counters, which every call leaves at zero) and synchronized before first
+    use.  Allocating it while a graph is being captured is refused: call this
+    once before capturing."""
     dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index or 0)
     t = _default_ws.get(dev.index)
     if t is None:
@@ -146,6 +148,8 @@ def default_workspace(device=None):
             raise RuntimeError("rq: allocate the default workspace before graph capture "
                                "(call gemm_rwkv_amd.rq.default_workspace() first)")
         t = torch.zeros(lib().rq_workspace_bytes(), dtype=torch.uint8, device=dev)
+        # the split counters at its head must read zero from any stream
+        torch.cuda.synchronize(dev)
         _default_ws[dev.index] = t
     return t
 

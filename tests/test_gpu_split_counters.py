@@ -80,6 +80,7 @@ def test_split_in_launch(fmt, group, n, k, m):
     torch.cuda.synchronize()
     assert torch.equal(y, first)
     own = torch.zeros(rq.rq_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()    # the zero fill ran on the current stream
     st = torch.cuda.Stream()
     y2 = torch.empty_like(y)
     with torch.cuda.stream(st):
@@ -100,6 +101,7 @@ def test_no_room_past_counters_means_no_split():
     x = g.standard_normal((m, k)).astype(np.float16)
     small = torch.zeros(COUNTER_BYTES, dtype=torch.uint8, device="cuda")
     y = torch.empty(m * n, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
     say("split: 64 KiB workspace", n, k, m)
     rq.rq_gemm_small_m(dev_f16(x), m, k, qw, y, n, ws=small)
     torch.cuda.synchronize()
