@@ -1882,9 +1882,10 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     while (share_x && rt < 4 && 2 * rt * wpt <= 16 &&
            (!one_round(rt) || (x_heavy(rt) && groups(2 * rt) * used >= 256)))
       rt *= 2;
-    if (used > 1 && ((used <= kSplitInLaunch && (!b.cnt || groups(rt) > kSplitCounters)) ||
-                     (size_t)groups(rt) * rt * used * mt * 1024 > b.ws_bytes))
-      break;
+    if (used > 1 && (size_t)groups(rt) * rt * used * mt * 1024 > b.ws_bytes) break;
+    // slices added in the launch need a counter per tile group; past that,
+    // a larger split adds them in a second kernel
+    if (used > 1 && used <= kSplitInLaunch && (!b.cnt || groups(rt) > kSplitCounters)) continue;
     sp.split = used;
     sp.cps = cps;
     sp.wpt = wpt;
