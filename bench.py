@@ -543,6 +543,16 @@ def measure_rows(gen, dev, reps=20):
         out["sb256 2560 set M=%d" % m] = {"us_per_set": round(us, 2), "GB_s": round(wb / us / 1e3, 1),
                                            "hbm_peak_frac": round(wb / us / 1e3 / HBM_PEAK_GBS, 4)}
     del sets
+    # fp8 prefill set (activation quantization included, as in the step) at
+    # the other prefill chunk sizes, M = 64 and 1024
+    for m in (64, 1024):
+        pm = Prefill(4096, m, gen, dev)
+        us = graph_us(pm.passes, pm.copies)
+        out["fp8 gemm 4096 set M=%d" % m] = {"us_per_set": round(us, 2),
+                                             "TFLOPS": round(pm.flops / us / 1e6, 1),
+                                             "frac_of_peak": round(pm.flops / us / 1e6 / FP8_PEAK_TFLOPS, 4)}
+        del pm
+        torch.cuda.empty_cache()
     # int8 GEMM, width-4096 prefill set at M = 256, 6 copies
     c, m = 4096, 256
     isets = []
@@ -973,6 +983,8 @@ def main():
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="per kernel and launch shape: dispatches and mean duration, from a "
                          "rocprofv3 --kernel-trace CSV")
+    ap.add_argument("--prefill-m", type=int, default=M3,
+                    help="with --kernel-only: the prefill classes at this M (default 256)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only the fp8/int8 GEMMs beside the vendor library's at the prefill shapes "
                          "(context), one JSON line")
@@ -998,7 +1010,7 @@ def main():
         return
 
     dec = Decode(C1, gen, dev)
-    pre = Prefill(C3, M3, gen, dev)
+    pre = Prefill(C3, args.prefill_m if args.kernel_only is not None else M3, gen, dev)
     if args.kernel_only is not None:
         print("weights ready", file=sys.stderr, flush=True)
 
