@@ -636,8 +636,14 @@ __device__ __forceinline__ void split_finish(__amdgpu_buffer_rsrc_t r, int split
   }
 }
 
+// Streamed activations with two activation tiles run at most eight waves per
+// workgroup (one row tile, at most 64 chunks in waves of 2, 4 or 8 chunks),
+// so they declare 512 threads and get the register file of two waves per
+// SIMD: declared for 1024, the compiler capped them at 128 VGPRs and spilled
+// (4096x8192 at M = 32: int4 group 32 31.7 -> 13.7 us, 6-bit 33.1 -> 17.2,
+// SB256 58.8 -> 41.9, int4 group 64 14.8 -> 13.4).
 template <int FMT, int G, int MT, int CPW, int MR, bool ST = false, int H = 1>
-__global__ void __launch_bounds__(1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
+__global__ void __launch_bounds__(ST && MT == 2 ? 512 : 1024) gemv5_kernel(const GemvBatch p, const Split5 sp) {
   typedef F2<FMT, G> F;
   typedef CodeSlot<FMT, G> S;
   static_assert(!ST || F::CK == 128, "streamed activations: 128-k chunks");
@@ -1954,6 +1960,11 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
   } while (0)
   if constexpr (F::CK == 128) {
     if (stream) {
+      // the kernel's declared bound for two activation tiles
+      if (mt == 2 && nw > 8) {
+        err = hipErrorInvalidConfiguration;
+        return true;
+      }
       if (mt == 2) {
         if (cpw == 2) RQ_L5S(2, 2); else if (cpw == 4) RQ_L5S(2, 4); else RQ_L5S(2, 8);
       } else {

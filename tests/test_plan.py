@@ -75,6 +75,9 @@ def test_plans_are_well_formed(fmt, group, ck):
             assert p["workgroups"] == -(-tiles16 // rt) * split, where
             continue
         assert p["waves_per_tile"] * rt * 64 == p["threads"], where
+        if p["kernel"] == rq.RQ_PLAN_STREAMED_X and m > 16:
+            # the kernel declares at most 512 threads for two activation tiles
+            assert p["threads"] <= 512 and rt == 1, where
         span = cps // 2 if p["kernel"] == rq.RQ_PLAN_TWO_RANGES else cps
         assert p["chunks_per_wave"] * p["waves_per_tile"] >= span, where
         assert (p["chunks_per_wave"] * (p["waves_per_tile"] - 1)) < span, where
