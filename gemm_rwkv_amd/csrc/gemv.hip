@@ -1762,11 +1762,20 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
   // an activation slice that does not fit one workgroup's LDS: stream it per
   // wave (one row tile per workgroup, waves of 2, 4 or 8 chunks) rather than
   // split K, when that makes 192 to 256 workgroups (one per CU) and the
-  // waves' buffers fit.  Measured: O 4096x4096 at M = 32 gains 2.6 us over
-  // the split plan, 4096x16384 at M = 4 and 8 0.9 and 1.2 us (at M = 12 no
-  // change, at M = 16 0.5 us slower: one activation tile streams only up to
-  // M = 8); with fewer row tiles (2048x8192, 128) the split plan is faster,
+  // waves' buffers fit.  Preferred for two activation tiles (M > 16) and
+  // codes other than SB256 (against the split plan, 4096 rows at M = 32:
+  // int4 group 64 K = 4096 7.65 vs 9.04 us, K = 8192 13.44 vs 13.77; int4
+  // group 32 K = 4096 8.11 vs 9.74; SB256 K = 8192 41.9 vs 16.8).  With one
+  // activation tile (M = 4..8) the split plan, whose slices are added in the
+  // launch, is faster (4096x16384, int4 group 64 at M = 4, 6, 8: 13.58,
+  // 13.29, 14.51 against 13.85, 14.82, 14.91 us streamed; group 32 at M = 4
+  // 14.94 against 17.22; SB256 19.2 against 53.0), so there the streamed
+  // plan serves only where no split is possible (no workspace, or none
+  // found).  With fewer row tiles (2048x8192, 128) the split plan is faster,
   // since each workgroup streams all of x through one CU.
+  bool stream_ok = false;
+  Split5 streamed;
+  int streamed_cpw = 0;
   if constexpr (F::CK == 128) {
     int tiles = 0;
     for (int i = 0; i < b.nmat; ++i) tiles += b.mat[i].tiles;
@@ -1774,14 +1783,19 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
     if (xb > (size_t)kXBudgetUnsplit && (mt == 2 || b.m <= 8) && nchunks <= 64 * (3 - mt) && tiles >= 192 &&
         tiles <= 256) {
       const int cpw = nchunks <= 16 ? 2 : (nchunks <= 32 ? 4 : 8);
-      sp.split = 1;
-      sp.cps = nchunks;
-      sp.wpt = (nchunks + cpw - 1) / cpw;
-      sp.rt = 1;
-      for (int i = 0; i < 3; ++i) sp.groups[i] = i < b.nmat ? b.mat[i].tiles : 0;
-      cpw_out = cpw;
-      stream_out = true;
-      return true;
+      streamed.split = 1;
+      streamed.cps = nchunks;
+      streamed.wpt = (nchunks + cpw - 1) / cpw;
+      streamed.rt = 1;
+      for (int i = 0; i < 3; ++i) streamed.groups[i] = i < b.nmat ? b.mat[i].tiles : 0;
+      streamed_cpw = cpw;
+      stream_ok = true;
+      if (!b.ws || (mt == 2 && FMT != GF_SB)) {
+        sp = streamed;
+        cpw_out = cpw;
+        stream_out = true;
+        return true;
+      }
     }
   }
   // row tiles share a workgroup (and its activation slice) only where that
@@ -1907,6 +1921,12 @@ static bool plan5(const GemvBatch& b, Split5& sp, int& cpw_out, bool& stream_out
   if (!found && have_unsplit) {
     sp = unsplit;
     cpw_out = unsplit_cpw;
+    return true;
+  }
+  if (!found && stream_ok) {
+    sp = streamed;
+    cpw_out = streamed_cpw;
+    stream_out = true;
     return true;
   }
   return found;

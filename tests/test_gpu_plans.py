@@ -40,15 +40,15 @@ def _weight(fmt, group, n, k):
     return _cache[key]
 
 
-def _check(fmt, group, n, k, m):
+def _check(fmt, group, n, k, m, ws=None):
     parts, qw = _weight(fmt, group, n, k)
     g = np.random.default_rng(m * 1000 + k)
     ldx = k + 8 * (m % 3)
     x = g.standard_normal((m, ldx)).astype(np.float16)
     ldy = n + 4
     y = torch.full((m * ldy,), -1, dtype=torch.int16, device="cuda")
-    say("plans", fmt, group, "n", n, "k", k, "m", m)
-    rq.rq_gemm_small_m(dev_f16(x), m, ldx, qw, y, ldy)
+    say("plans", fmt, group, "n", n, "k", k, "m", m, "ws", ws)
+    rq.rq_gemm_small_m(dev_f16(x), m, ldx, qw, y, ldy, ws=ws)
     torch.cuda.synchronize()
     out = host(y, np.float16, (m, ldy))
     assert np.all(out[:, n:].view(np.int16) == -1), "wrote past n"
@@ -83,3 +83,18 @@ def test_plans_2p9b_shapes(fmt, group, n, k, m):
     # M = 9..16 the key's 640 row tiles would need two rounds of one
     # workgroup per CU unsplit, so K is split
     _check(fmt, group, n, k, m)
+
+
+@pytest.mark.parametrize("fmt,group", [(quant.W4_ASYM_SB256, 32), (quant.W4_SYM, 32), (quant.W6_SYM, 32),
+                                       (quant.W5_SYM, 64), (quant.W4_SYM, 64)])
+@pytest.mark.parametrize("k,m", [(8192, 32), (8192, 20), (16384, 4), (16384, 8)])
+def test_streamed_without_workspace(fmt, group, k, m):
+    """Without a workspace no K split is possible, and 194 row tiles with an
+    activation slice too large for LDS take the per-wave streamed plan for
+    every format (with a workspace, one activation tile and SB256 split K
+    instead)."""
+    n = 3100
+    plan = rq.rq_plan_small_m((fmt, 32 if fmt == quant.W4_ASYM_SB256 else group, n, k), m, ldx=k + 8 * (m % 3),
+                              ws_bytes=0)
+    assert plan["kernel"] == rq.RQ_PLAN_STREAMED_X, plan
+    _check(fmt, group, n, k, m, ws=False)

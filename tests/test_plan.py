@@ -107,11 +107,17 @@ def test_documented_plans():
     # width-2048 O (16 chunks) keeps one range
     assert rq.rq_plan_small_m(W4 + (2048, 2048), 1)["kernel"] == rq.RQ_PLAN_STREAMING
     # width-4096 cmix value at M = 1: sixteen-chunk waves, one workgroup of
-    # eight waves per row tile; M = 4: each wave streams its activations
+    # eight waves per row tile; M = 4: K in four slices added in the launch,
+    # or, with no workspace, each wave streams its activations
     p = rq.rq_plan_small_m(W4 + (4096, 16384), 1)
     assert (p["kernel"], p["chunks_per_wave"], p["waves_per_tile"], p["workgroups"]) == \
         (rq.RQ_PLAN_STREAMING, 16, 8, 256)
-    assert rq.rq_plan_small_m(W4 + (4096, 16384), 4)["kernel"] == rq.RQ_PLAN_STREAMED_X
+    p = rq.rq_plan_small_m(W4 + (4096, 16384), 4)
+    assert (p["kernel"], p["split"]) == (rq.RQ_PLAN_STREAMING, 4)
+    assert rq.rq_plan_small_m(W4 + (4096, 16384), 4, ws_bytes=0)["kernel"] == rq.RQ_PLAN_STREAMED_X
+    # M > 16: O 4096x4096 streams its activations; SB256 splits instead
+    assert rq.rq_plan_small_m(W4 + (4096, 4096), 32)["kernel"] == rq.RQ_PLAN_STREAMED_X
+    assert rq.rq_plan_small_m((rq.RQ_W4_ASYM_SB256, 32, 4096, 8192), 32)["kernel"] == rq.RQ_PLAN_STREAMING
     # K is not split at M = 1 for the width-4096 matrices
     for n, k in ((4096, 4096), (16384, 4096), (4096, 16384)):
         assert rq.rq_plan_small_m(W4 + (n, k), 1)["split"] == 1
