@@ -1611,17 +1611,34 @@ static bool plan6(const GemvBatch& b, int group, Shape6& sh) {
   // one activation tile's streamed plan of the streaming kernel (192 to 256
   // row tiles, at most 64 chunks) does better without a K split
   if (tiles >= 192 && tiles <= 256 && nchunks <= 64) return false;
-  constexpr int rt = kG6Rt;
   auto groups = [&](int r) {
     int g = 0;
     for (int i = 0; i < b.nmat; ++i) g += (b.mat[i].tiles + r - 1) / r;
     return g;
   };
   const int nph = nchunks / 4;
-  int split = 1;
-  while (groups(rt) * split < 192 && split < 16 && nph >= 4 * split) split *= 2;
-  const int cps = (nph + split - 1) / split * 4;
-  split = (nchunks + cps - 1) / cps;
+  // slices of whole phases until there are 192 workgroups
+  auto slices = [&](int r, int& cps_out) {
+    int sp = 1;
+    while (groups(r) * sp < 192 && sp < 16 && nph >= 4 * sp) sp *= 2;
+    cps_out = (nph + sp - 1) / sp * 4;
+    return (nchunks + cps_out - 1) / cps_out;
+  };
+  int rt = kG6Rt, cps = 0;
+  int split = slices(rt, cps);
+  // two row tiles per workgroup where four would need more slices than the
+  // launch adds up itself and two do not (2048x8192 at M = 32: four tiles
+  // in 8 slices plus the reducing kernel 9.37 us, two in 4 slices 9.12; at
+  // M = 17 9.35 against 8.92), at the price of twice the activation reads
+  if (split > kSplitInLaunch) {
+    int cps2 = 0;
+    const int split2 = slices(2, cps2);
+    if (split2 <= kSplitInLaunch && groups(2) * split2 >= 192) {
+      rt = 2;
+      split = split2;
+      cps = cps2;
+    }
+  }
   const int mt = b.m <= 16 ? 1 : 2;
   if (groups(rt) * split < 192) return false;
   if (split > 1 && (!b.ws || (split <= kSplitInLaunch && (!b.cnt || groups(rt) > kSplitCounters)) ||
@@ -1653,7 +1670,11 @@ static bool launch6(const GemvBatch& b, hipStream_t st, hipError_t& err) {
     (void)attr_set;                                                                                  \
     hipLaunchKernelGGL((gemv6_kernel<G, MT, RT>), grid, dim3(C6::NW * 64), C6::LDS, st, b, sh.plan);   \
   } while (0)
-  if (mt == 2) RQ_L6(2, kG6Rt); else RQ_L6(1, kG6Rt);
+  if (sh.rt == 2) {
+    if (mt == 2) RQ_L6(2, 2); else RQ_L6(1, 2);
+  } else {
+    if (mt == 2) RQ_L6(2, kG6Rt); else RQ_L6(1, kG6Rt);
+  }
 #undef RQ_L6
   err = hipGetLastError();
   if (err == hipSuccess && sh.plan.split > kSplitInLaunch) {
@@ -2118,7 +2139,10 @@ static bool describe_mt(const GemvBatch& b, GemvPlanInfo& o) {
       o.rt = sh.rt;
       o.workgroups = gtot * sh.plan.split;
       o.threads = (mt == 2 ? G6<G, 2, kG6Rt>::NW : G6<G, 1, kG6Rt>::NW) * 64;
-      o.lds = mt == 2 ? G6<G, 2, kG6Rt>::LDS : G6<G, 1, kG6Rt>::LDS;
+      if (sh.rt == 2)
+        o.lds = mt == 2 ? G6<G, 2, 2>::LDS : G6<G, 1, 2>::LDS;
+      else
+        o.lds = mt == 2 ? G6<G, 2, kG6Rt>::LDS : G6<G, 1, kG6Rt>::LDS;
       o.ws_used = sh.plan.split > 1 ? (size_t)gtot * sh.plan.split * sh.rt * mt * 1024 : 0;
       return true;
     }

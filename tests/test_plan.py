@@ -102,7 +102,8 @@ def test_documented_plans():
     p = rq.rq_plan_small_m(W4 + (2048, 8192), 8)
     assert (p["kernel"], p["workgroups"]) == (rq.RQ_PLAN_TWO_RANGES, 256)
     p = rq.rq_plan_small_m(W4 + (2048, 8192), 32)
-    assert (p["kernel"], p["split"], p["tiles_per_workgroup"], p["workgroups"]) == (rq.RQ_PLAN_PHASED, 8, 4, 256)
+    # phased, two row tiles per workgroup in four slices summed in the launch
+    assert (p["kernel"], p["split"], p["tiles_per_workgroup"], p["workgroups"]) == (rq.RQ_PLAN_PHASED, 4, 2, 256)
     assert rq.rq_plan_small_m(W4 + (2048, 8192), 32, ws_bytes=0)["kernel"] == rq.RQ_PLAN_FIRST
     # width-2048 O (16 chunks) keeps one range
     assert rq.rq_plan_small_m(W4 + (2048, 2048), 1)["kernel"] == rq.RQ_PLAN_STREAMING
