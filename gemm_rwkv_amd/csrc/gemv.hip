@@ -1594,9 +1594,9 @@ struct Shape6 {
 };
 constexpr int kG6Rt = 4;
 
-static bool plan6(const GemvBatch& b, int group, Shape6& sh) {
+static bool plan6(const GemvBatch& b, int group, int min_m, Shape6& sh) {
   const int nchunks = b.k / 128;
-  if (b.m <= 16 || nchunks == 0 || nchunks % 4 != 0) return false;
+  if (b.m < min_m || nchunks == 0 || nchunks % 4 != 0) return false;
   // an activation slice that fits one workgroup's LDS whole: the streaming
   // kernel stages it once, unsplit
   if ((size_t)(b.m + 1) * (size_t)(b.k + 8) * 2u <= (size_t)kXBudgetUnsplit) return false;
@@ -1652,9 +1652,7 @@ static bool plan6(const GemvBatch& b, int group, Shape6& sh) {
 }
 
 template <int G>
-static bool launch6(const GemvBatch& b, hipStream_t st, hipError_t& err) {
-  Shape6 sh;
-  if (!plan6(b, G, sh)) return false;
+static bool launch6(const GemvBatch& b, const Shape6& sh, hipStream_t st, hipError_t& err) {
   const int mt = b.m <= 16 ? 1 : 2;
   const int gtot = sh.plan.groups[0] + sh.plan.groups[1] + sh.plan.groups[2];
   err = hipSuccess;
@@ -2073,6 +2071,26 @@ static bool launch5(const GemvBatch& b, hipStream_t st, hipError_t& err) {
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
+// The phased kernel's shape for int4 groups, or false: past 16 activation
+// rows wherever plan6 finds one; from 9 to 16 rows only where the streaming
+// kernel would cut K into more slices than its launch adds up (a second,
+// reducing kernel), or finds no plan, and the phased kernel needs no more
+// slices than that
+// (4096x16384 at M = 9, 12, 16: 15.8, 16.3, 16.3 -> 14.3, 14.6, 14.6 us;
+// where the streaming kernel's split stays in its launch it is faster:
+// 2048x8192 at M = 12, 16 7.4, 7.6 against 7.9, 8.0 us).
+template <int FMT, int G>
+static bool choose6(const GemvBatch& b, Shape6& sh) {
+  if (b.k % 512 != 0) return false;
+  if (plan6(b, G, 17, sh)) return true;
+  if (b.m < 9 || b.m > 16) return false;
+  Split5 sp;
+  int cpw = 4, ranges = 1;
+  bool stream = false;
+  if (plan5<FMT, G>(b, sp, cpw, stream, ranges) && sp.split <= kSplitInLaunch) return false;
+  return plan6(b, G, 9, sh) && sh.plan.split <= kSplitInLaunch;
+}
+
 template <int FMT, int G, int MT, int NW>
 static hipError_t launch_t(const GemvBatch& b, hipStream_t st) {
   constexpr int U = Fmt<FMT, G>::GK == 16 ? 8 : (Fmt<FMT, G>::GK == 32 ? 4 : 2);
@@ -2107,7 +2125,8 @@ static hipError_t launch_mt(const GemvBatch& b, hipStream_t st) {
   constexpr bool v2ok = !(FMT == GF_W4 && G == 16);
   if constexpr (FMT == GF_W4 && (G == 64 || G == 32)) {
     hipError_t err;
-    if (b.k % 512 == 0 && launch6<G>(b, st, err)) return err;
+    Shape6 sh;
+    if (choose6<FMT, G>(b, sh) && launch6<G>(b, sh, st, err)) return err;
   }
   if constexpr (v2ok) {
     if (b.k % F2<FMT, G>::CK == 0) {
@@ -2131,7 +2150,7 @@ static bool describe_mt(const GemvBatch& b, GemvPlanInfo& o) {
   const int mt = b.m <= 16 ? 1 : 2;
   if constexpr (FMT == GF_W4 && (G == 64 || G == 32)) {
     Shape6 sh;
-    if (b.k % 512 == 0 && plan6(b, G, sh)) {
+    if (choose6<FMT, G>(b, sh)) {
       const int gtot = sh.plan.groups[0] + sh.plan.groups[1] + sh.plan.groups[2];
       o.kernel = 4;
       o.split = sh.plan.split;

@@ -1,15 +1,16 @@
 """K-split weight-streaming products cut into up to four slices add their
 partial tiles inside the same launch: the last workgroup of each tile group,
 found through an arrival counter at the head of the workspace, sums the slices
-in slice order (eight slices go through a second, reducing kernel).
+in slice order (more slices go through a second, reducing kernel).
 
-Checked here, on shapes whose plans split K (the phased kernel at M > 16 in 8
-and 4 slices, the streaming kernel's split at M = 16, the four-slice plan of
-SB256, int8 group 16 and 6-bit codes at M <= 4, ragged tile counts): every
-call leaves the counters at zero; repeated calls, calls on a caller-owned
-zero-filled workspace and graph replays give bit-identical outputs; a
-workspace with no room past the counters means no split; and sampled rows
-agree with the oracle."""
+Checked here, on shapes whose plans split K in four: the phased kernel with
+two activation tiles (two or four row tiles per workgroup) and with one
+(M = 9..16, where the streaming kernel would need eight slices), the
+streaming kernel at M = 16, the four-slice plans of SB256, int8 group 16 and
+6-bit codes at M <= 4, ragged tile counts.  Every call leaves the counters at
+zero; repeated calls, calls on a caller-owned zero-filled workspace and graph
+replays give bit-identical outputs; a workspace with no room past the
+counters means no split; and sampled rows agree with the oracle."""
 
 import numpy as np
 import pytest
@@ -25,11 +26,13 @@ COUNTER_BYTES = 64 << 10
 
 # (format, group, n, k, m)
 SHAPES = [
-    (quant.W4_SYM, 64, 2048, 8192, 32),       # phased, K in 8 slices, four tiles per workgroup
+    (quant.W4_SYM, 64, 2048, 8192, 32),       # phased, two tiles per workgroup, K in 4 slices
     (quant.W4_SYM, 64, 2085, 8192, 17),       # phased, ragged last tile group
-    (quant.W4_SYM, 64, 4096, 16384, 16),      # streaming, K in 8 slices
+    (quant.W4_SYM, 64, 4096, 16384, 16),      # phased with one activation tile, K in 4 slices
     (quant.W4_SYM, 64, 4096, 16384, 32),      # phased, K in 4 slices
     (quant.W4_SYM, 64, 2048, 8192, 16),       # streaming, K in 4 slices, shared tiles
+    (quant.W4_SYM, 64, 4100, 16384, 12),      # phased with one activation tile, ragged last tile group
+    (quant.W4_SYM, 32, 4096, 16384, 9),
     (quant.W4_ASYM_SB256, 32, 2560, 10240, 1),  # four-slice plan of the costlier decoders
     (quant.W8_SYM, 16, 2560, 10240, 4),
     (quant.W6_SYM, 32, 1000, 10240, 3),
