@@ -28,9 +28,14 @@ namespace rq {
 // halves what L2 delivers per instruction.  Instead each wave copies its k
 // block with LDS DMA reads of 8 rows x 128 B (whole lines) into a private
 // 2-stage ring and reads the fragments back with ds_read_b128.  The 16-byte
-// segments of row r are stored at slot (segment ^ ((r / 2) % 8)), so the 16
-// rows a fragment read touches fall in distinct banks.  While block j is
-// multiplied, block j + 1 is in flight.
+// segments of row r are stored at slot (segment ^ (r % 8)), and lane
+// (row r16 = lane % 16, q = lane / 16) takes segments q and q + 4 of its row
+// (32 bytes, the same k for x and w, so every k still meets its partner):
+// then the sixteen lanes that LDS serves together read sixteen distinct
+// 16-byte bank groups.  (Segments 2q and 2q + 1 under the swizzle
+// (r / 2) % 8 cost four bank-conflict cycles per read, counted with
+// SQ_LDS_BANK_CONFLICT.)  While block j is multiplied, block j + 1 is in
+// flight.
 //
 // The DMA and its waits are issued as inline asm: the compiler cannot tell
 // which LDS bytes an LDS DMA writes, and would otherwise wait for every DMA
@@ -62,19 +67,19 @@ __global__ void __launch_bounds__(64 * KW) gemm_w8a8_kernel(const uint8_t* __res
   const int nkb = K >> 7;
 
   // LDS DMA sources: instruction i covers tile rows 8i .. 8i + 7, lane ->
-  // row 8i + lane / 8, LDS slot lane % 8 holding segment slot ^ ((row / 2) % 8)
+  // row 8i + lane / 8, LDS slot lane % 8 holding segment slot ^ (row % 8)
   const int drow = lane >> 3, dslot = lane & 7;
   const uint8_t* asrc[TM * 2];
   const uint8_t* bsrc[TN * 2];
 #pragma unroll
   for (int i = 0; i < TM * 2; ++i) {
     const int r = 8 * i + drow;
-    asrc[i] = xq + (size_t)min(m0 + r, M - 1) * K + ((dslot ^ ((r >> 1) & 7)) << 4);
+    asrc[i] = xq + (size_t)min(m0 + r, M - 1) * K + ((dslot ^ (r & 7)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < TN * 2; ++i) {
     const int r = 8 * i + drow;
-    bsrc[i] = wq + (size_t)min(n0 + r, N - 1) * K + ((dslot ^ ((r >> 1) & 7)) << 4);
+    bsrc[i] = wq + (size_t)min(n0 + r, N - 1) * K + ((dslot ^ (r & 7)) << 4);
   }
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds4 + wave * NB * STAGE;
   auto dma = [&](int st, int kb) {
@@ -93,10 +98,10 @@ __global__ void __launch_bounds__(64 * KW) gemm_w8a8_kernel(const uint8_t* __res
     }
   };
 
-  // fragment reads: row r16 of a 16-row block, segments 2q and 2q + 1
-  const int swz = (r16 >> 1) & 7;
-  const int o0 = r16 * 128 + (((2 * q) ^ swz) << 4);
-  const int o1 = r16 * 128 + (((2 * q + 1) ^ swz) << 4);
+  // fragment reads: row r16 of a 16-row block, segments q and q + 4
+  const int swz = r16 & 7;
+  const int o0 = r16 * 128 + ((q ^ swz) << 4);
+  const int o1 = r16 * 128 + (((q + 4) ^ swz) << 4);
   const uint8_t* my = (const uint8_t*)lds4 + wave * NB * STAGE;
 
   AccT acc[TM][TN];
@@ -236,7 +241,7 @@ __global__ void __launch_bounds__(64 * NW) gemm_w8a8_ring_kernel(const uint8_t* 
   for (int u = 0; u < PER; ++u) {
     const int g = wave * PER + u;
     const int r = 8 * (g & 15) + drow;
-    const int seg = (dslot ^ ((r >> 1) & 7)) << 4;
+    const int seg = (dslot ^ (r & 7)) << 4;
     src[u] = g < 16 ? xq + (size_t)min(m0 + r, M - 1) * K + seg : wq + (size_t)min(n0 + r, N - 1) * K + seg;
     dst[u] = (g < 16 ? 0 : SA) + (g & 15) * 1024;
   }
@@ -250,9 +255,9 @@ __global__ void __launch_bounds__(64 * NW) gemm_w8a8_ring_kernel(const uint8_t* 
     }
   };
 
-  const int swz = (r16 >> 1) & 7;
-  const int o0 = r16 * 128 + (((2 * q) ^ swz) << 4);
-  const int o1 = r16 * 128 + (((2 * q + 1) ^ swz) << 4);
+  const int swz = r16 & 7;
+  const int o0 = r16 * 128 + ((q ^ swz) << 4);
+  const int o1 = r16 * 128 + (((q + 4) ^ swz) << 4);
   const uint8_t* abase = (const uint8_t*)lds4 + qm * 64 * 128;
   const uint8_t* bbase = (const uint8_t*)lds4 + SA + qn * (16 * TB) * 128;
 
@@ -381,7 +386,7 @@ __global__ void __launch_bounds__(512) gemm_w8a8_big_kernel(const uint8_t* __res
   for (int u = 0; u < PER; ++u) {
     const int g = wave * PER + u;
     const int r = 8 * (g & 31) + drow;
-    const int seg = (dslot ^ ((r >> 1) & 7)) << 4;
+    const int seg = (dslot ^ (r & 7)) << 4;
     src[u] = g < 32 ? xq + (size_t)min(m0 + r, M - 1) * K + seg : wq + (size_t)min(n0 + r, N - 1) * K + seg;
     dst[u] = (g < 32 ? 0 : SA) + (g & 31) * 1024;
   }
@@ -395,9 +400,9 @@ __global__ void __launch_bounds__(512) gemm_w8a8_big_kernel(const uint8_t* __res
     }
   };
 
-  const int swz = (r16 >> 1) & 7;
-  const int o0 = r16 * 128 + (((2 * q) ^ swz) << 4);
-  const int o1 = r16 * 128 + (((2 * q + 1) ^ swz) << 4);
+  const int swz = r16 & 7;
+  const int o0 = r16 * 128 + ((q ^ swz) << 4);
+  const int o1 = r16 * 128 + (((q + 4) ^ swz) << 4);
   const uint8_t* abase = (const uint8_t*)lds4 + qm * 128 * 128;
   const uint8_t* bbase = (const uint8_t*)lds4 + SA + qn * 64 * 128;
 
