@@ -69,7 +69,9 @@ def _compare_rows(y, rows, x, fmt, parts, group, what):
 
 
 # --------------------------------------------------------------------------
-# width 2048 (1.5B) layer, int4 g64, M in {1, 8, 32}: the benchmark's decode
+# width 2048 (1.5B) layer, int4 g64, every M from 1 to 32: the benchmark's
+# decode (M = 1, 8, 32) and every plan between (two-range tiles up to M = 8,
+# streaming tiles, the phased kernel past M = 16, K splits summed in launch)
 # --------------------------------------------------------------------------
 
 
@@ -84,13 +86,13 @@ def layer_2048():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m", [1, 8, 32])
+@pytest.mark.parametrize("m", list(range(1, 33)))
 def test_decode_layer_2048(layer_2048, m):
     c, mats = layer_2048
     x = synth.act_channel_1202(m, c)
     x4 = synth.act_normal(m, 4 * c, 1)
     xd, x4d = dev_f16(x), dev_f16(x4)
-    say("decode layer 2048 m", m)
+    say("decode layer 2048 m", m, rq.rq_plan_small_m(mats[synth.MAT_VALUE][1], m, 4 * c))
     ys = {mat: torch.empty(m * n * 2, dtype=torch.uint8, device="cuda") for mat, n, _ in synth.layer_shapes(c)}
     q = {mat: mats[mat][1] for mat in mats}
     rq.rq_fused_rkv(xd, xd, xd, m, c, q[synth.MAT_R], q[synth.MAT_K], q[synth.MAT_V],
@@ -248,7 +250,7 @@ def layer_4096():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 6, 8, 9, 12, 16, 17, 24, 32])
 def test_decode_layer_4096(layer_4096, m):
     c, mats = layer_4096
     x = synth.act_normal(m, c, 4)
