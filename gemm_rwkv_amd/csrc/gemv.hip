@@ -1254,14 +1254,18 @@ __global__ void __launch_bounds__(256) gemv5_reduce_kernel(const GemvBatch p, co
 // activation rows, so x crosses L2 once per RT tiles, and the whole K of
 // most matrices fits one slice.
 //
-// Each of the eight waves owns one eighth of every phase's (chunk, group)
-// pairs for all RT row tiles: it reads an activation fragment from LDS once
-// and multiplies it into every tile, so LDS delivers each phase's activations
-// once per workgroup rather than once per tile.  A lane reads from LDS
+// Each of eight waves owns one eighth of every phase's (chunk, group) pairs
+// for two row tiles: it reads an activation fragment from LDS once and
+// multiplies it into both, so LDS delivers a phase's activations once per
+// two tiles rather than once per tile.  With four row tiles the workgroup
+// runs sixteen waves, the second eight on tiles 2 and 3: four waves per
+// SIMD hide the LDS and MFMA latencies of the short per-phase chains better
+// than two (width-4096 shapes at M = 12..32: 2-6% faster; at two tiles,
+// sixteen waves of one tile each were 1% slower).  A lane reads from LDS
 // exactly the code words the streaming kernel's lane exchange would hand it
 // (the 8 k at the fragment's offset), so no exchange is needed.  The eight
-// partial sums of each output are added through LDS in wave order at the
-// end.  Activation rows are padded to 1040 bytes and the 16-byte segments of
+// partial sums of each output (one per pair share) are added through LDS in
+// share order at the end.  Activation rows are padded to 1040 bytes and the 16-byte segments of
 // code row r are stored at slot (segment ^ (r % 16)), so the sixteen rows of
 // an operand read fall in distinct banks.  Decode and scaling are those of
 // the streaming kernel (symmetric int4).
@@ -1275,9 +1279,12 @@ template <int G, int MT, int RT>
 struct G6 {
   static constexpr int P = 4;                    // chunks per phase
   static constexpr int NB = MT == 1 ? 4 : 3;     // LDS buffers (phases in flight + 1)
-  static constexpr int NW = 8;                   // waves
+  static constexpr int NWP = 8;                  // waves sharing out a phase's (chunk, group) pairs
+  static constexpr int TS = RT >= 4 ? 2 : 1;     // row-tile shares (sixteen waves for four tiles)
+  static constexpr int NW = NWP * TS;            // waves
+  static constexpr int RTW = RT / TS;            // row tiles of a wave
   static constexpr int GPC = 128 / G;            // scale groups per chunk
-  static constexpr int PPW = P * GPC / NW;       // (chunk, group) pairs of a wave per phase
+  static constexpr int PPW = P * GPC / NWP;      // (chunk, group) pairs of a wave per phase
   static constexpr int RS = P * 256 + 16;        // LDS bytes per activation row
   static constexpr int XR = 16 * MT;             // activation rows (one DMA each)
   static constexpr int CD = RT * P;              // code DMAs (4 rows x 256 bytes each)
@@ -1291,9 +1298,10 @@ struct G6 {
   static constexpr int SB = SP * SR * 16;        // scale spans: [SP][SR rows][16 bytes]
   static constexpr int BUF = XB + CB + SB;
   static constexpr size_t LDS = (size_t)NB * BUF;
-  static_assert(PPW >= 1 && P * GPC == PPW * NW, "the pairs of a phase");
+  static_assert(PPW >= 1 && P * GPC == PPW * NWP, "the pairs of a phase");
+  static_assert(RTW >= 1 && RT == TS * RTW, "the row-tile shares");
   static_assert(SR % 64 == 0 && SR >= RT * 16, "the scale DMAs cover the code rows");
-  static_assert(NB * BUF >= (size_t)NW * RT * MT * 1024, "the reduction fits the buffers");
+  static_assert(NB * BUF >= (size_t)NWP * RT * MT * 1024, "the reduction fits the buffers");
   static_assert((NB - 1) * DPW <= 63, "the phases in flight within the wait counter");
 };
 
@@ -1368,7 +1376,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 template <int G, int MT, int RT>
-__global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Plan6 sp) {
+__global__ void __launch_bounds__(RT >= 4 ? 1024 : 512) gemv6_kernel(const GemvBatch p, const Plan6 sp) {
   typedef F2<GF_W4, G> F;
   typedef G6<G, MT, RT> C;
   constexpr int P = C::P, NB = C::NB, RS = C::RS, BUF = C::BUF, DPW = C::DPW;
@@ -1462,13 +1470,15 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
 
   const int j = lane & 15;
   const int kq = lane >> 4;
-  bool tv[RT];
+  // wave = th NWP + pw: pair share pw of every phase, row tiles th RTW ..
+  const int th = wave / C::NWP, pw = wave - th * C::NWP;
+  bool tv[C::RTW];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) tv[r] = grp * RT + r < A.tiles;
+  for (int r = 0; r < C::RTW; ++r) tv[r] = grp * RT + th * C::RTW + r < A.tiles;
 
-  float4v acc[RT][MT];
+  float4v acc[C::RTW][MT];
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+  for (int r = 0; r < C::RTW; ++r)
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[r][t] = float4v{0.f, 0.f, 0.f, 0.f};
   const float4v zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -1479,7 +1489,7 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
     const uint8_t* xb = bufp + j * RS + x_base<GF_W4, G>(kq) * 2;
 #pragma unroll
     for (int e = 0; e < C::PPW; ++e) {
-      const int pi = wave * C::PPW + e;
+      const int pi = pw * C::PPW + e;
       const int ci = pi / C::GPC, g = pi - ci * C::GPC;  // chunk within the phase, group
       // the lane's code bytes for k step pp: at ci 64 + (k offset of its
       // fragment) / 2 within the row's phase span
@@ -1493,8 +1503,8 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
       }
       const int hh = ci * C::GPC + g;  // scale half-word of the phase span
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int row = r * 16 + j;
+      for (int r = 0; r < C::RTW; ++r) {
+        const int row = (th * C::RTW + r) * 16 + j;
         const uint8_t* cr = bufp + C::XB + row * 256 + (b0 & 15);
         uint32_t wv[2];
         if constexpr (F::MPG == 2) {
@@ -1537,17 +1547,17 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
     compute(q % NB);
   }
 
-  // the eight waves' partial sums of each output, added in wave order
+  // the NWP pair shares' partial sums of each output, added in share order
   constexpr int E = MT * 4 * 64;  // outputs of one row tile (rows m < 16 MT)
   const int ent = RT * E;
   float (*red)[RT][MT][4][64] = (float (*)[RT][MT][4][64])lds4;
   __syncthreads();  // every wave is done with the buffers
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+  for (int r = 0; r < C::RTW; ++r)
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) red[wave][r][t][q][lane] = acc[r][t][q];
+      for (int q = 0; q < 4; ++q) red[pw][th * C::RTW + r][t][q][lane] = acc[r][t][q];
   __syncthreads();
   if (sp.split > 1) {
     // four consecutive outputs per thread (lanes l .. l + 3)
@@ -1558,7 +1568,7 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
       const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
       float4v v = *(const float4v*)&red[0][rr][t][q][l];
 #pragma unroll
-      for (int w2 = 1; w2 < C::NW; ++w2) {
+      for (int w2 = 1; w2 < C::NWP; ++w2) {
         const float4v u = *(const float4v*)&red[w2][rr][t][q][l];
         v[0] += u[0];
         v[1] += u[1];
@@ -1576,7 +1586,7 @@ __global__ void __launch_bounds__(512) gemv6_kernel(const GemvBatch p, const Pla
     const int t = e >> 8, q = (e >> 6) & 3, l = e & 63;
     float v = red[0][rr][t][q][l];
 #pragma unroll
-    for (int w2 = 1; w2 < C::NW; ++w2) v += red[w2][rr][t][q][l];
+    for (int w2 = 1; w2 < C::NWP; ++w2) v += red[w2][rr][t][q][l];
     const int m = t * 16 + 4 * (l >> 4) + q;
     const int nn = (grp * RT + rr) * 16 + (l & 15);
     if (m < M && nn < A.n) A.y[(size_t)m * p.ldy + nn] = f32_to_f16_bits(v);
@@ -2157,7 +2167,7 @@ static bool describe_mt(const GemvBatch& b, GemvPlanInfo& o) {
       o.cps = sh.plan.cps;
       o.rt = sh.rt;
       o.workgroups = gtot * sh.plan.split;
-      o.threads = (mt == 2 ? G6<G, 2, kG6Rt>::NW : G6<G, 1, kG6Rt>::NW) * 64;
+      o.threads = (sh.rt == 2 ? G6<G, 1, 2>::NW : G6<G, 1, kG6Rt>::NW) * 64;
       if (sh.rt == 2)
         o.lds = mt == 2 ? G6<G, 2, 2>::LDS : G6<G, 1, 2>::LDS;
       else
