@@ -4,7 +4,8 @@ found through an arrival counter at the head of the workspace, sums the slices
 in slice order (more slices go through a second, reducing kernel).
 
 Checked here, on shapes whose plans split K in four: the phased kernel with
-two activation tiles (two or four row tiles per workgroup) and with one
+two activation tiles (two or four row tiles per workgroup, the latter on
+sixteen waves, with ragged last tile groups) and with one
 (M = 9..16, where the streaming kernel would need eight slices), the
 streaming kernel at M = 16, the four-slice plans of SB256, int8 group 16 and
 6-bit codes at M <= 4, ragged tile counts.  Every call leaves the counters at
@@ -32,6 +33,9 @@ SHAPES = [
     (quant.W4_SYM, 64, 4096, 16384, 32),      # phased, K in 4 slices
     (quant.W4_SYM, 64, 2048, 8192, 16),       # streaming, K in 4 slices, shared tiles
     (quant.W4_SYM, 64, 4100, 16384, 12),      # phased with one activation tile, ragged last tile group
+    (quant.W4_SYM, 64, 4100, 16384, 32),      # phased, sixteen waves on four row tiles, ragged last group
+    (quant.W4_SYM, 64, 4100, 16384, 20),      # the same with activation rows 20..31 empty
+    (quant.W4_SYM, 32, 4100, 8192, 24),       # group 32, four row tiles, ragged
     (quant.W4_SYM, 32, 4096, 16384, 9),
     (quant.W4_ASYM_SB256, 32, 2560, 10240, 1),  # four-slice plan of the costlier decoders
     (quant.W8_SYM, 16, 2560, 10240, 4),
