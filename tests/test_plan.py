@@ -75,6 +75,8 @@ def test_plans_are_well_formed(fmt, group, ck):
             assert fmt == rq.RQ_W4_SYM and group in (32, 64) and cps % 4 == 0, where
             assert m > 16 or (m >= 9 and split <= 4), where
             assert p["workgroups"] == -(-tiles16 // rt) * split, where
+            # eight waves on two row tiles, sixteen on four
+            assert (rt, p["threads"]) in ((2, 512), (4, 1024)), where
             continue
         assert p["waves_per_tile"] * rt * 64 == p["threads"], where
         if p["kernel"] == rq.RQ_PLAN_STREAMED_X and m > 16:
@@ -106,7 +108,11 @@ def test_documented_plans():
     p = rq.rq_plan_small_m(W4 + (2048, 8192), 32)
     # phased, two row tiles per workgroup in four slices summed in the launch
     assert (p["kernel"], p["split"], p["tiles_per_workgroup"], p["workgroups"]) == (rq.RQ_PLAN_PHASED, 4, 2, 256)
+    assert p["threads"] == 512
     assert rq.rq_plan_small_m(W4 + (2048, 8192), 32, ws_bytes=0)["kernel"] == rq.RQ_PLAN_FIRST
+    # width-4096 cmix value at M = 32: phased, four row tiles on sixteen waves
+    p = rq.rq_plan_small_m(W4 + (4096, 16384), 32)
+    assert (p["kernel"], p["split"], p["tiles_per_workgroup"], p["threads"]) == (rq.RQ_PLAN_PHASED, 4, 4, 1024)
     # width-2048 O (16 chunks) keeps one range
     assert rq.rq_plan_small_m(W4 + (2048, 2048), 1)["kernel"] == rq.RQ_PLAN_STREAMING
     # width-4096 cmix value at M = 1: sixteen-chunk waves, one workgroup of
