@@ -1608,8 +1608,9 @@ static bool plan6(const GemvBatch& b, int group, int min_m, Shape6& sh) {
   const int nchunks = b.k / 128;
   if (b.m < min_m || nchunks == 0 || nchunks % 4 != 0) return false;
   // an activation slice that fits one workgroup's LDS whole: the streaming
-  // kernel stages it once, unsplit
-  if ((size_t)(b.m + 1) * (size_t)(b.k + 8) * 2u <= (size_t)kXBudgetUnsplit) return false;
+  // kernel stages it once, unsplit, unless four row tiles on sixteen waves
+  // take it (checked below)
+  const bool fits_unsplit = (size_t)(b.m + 1) * (size_t)(b.k + 8) * 2u <= (size_t)kXBudgetUnsplit;
   constexpr size_t kLim = (size_t)1 << 31;
   for (int i = 0; i < b.nmat; ++i) {
     const size_t n = (size_t)b.mat[i].n;
@@ -1651,6 +1652,12 @@ static bool plan6(const GemvBatch& b, int group, int min_m, Shape6& sh) {
   }
   const int mt = b.m <= 16 ? 1 : 2;
   if (groups(rt) * split < 192) return false;
+  // four row tiles on sixteen waves, unsplit, beat the streaming kernel's
+  // unsplit slice (K = 4096 at M = 9..17: 16384x4096 13.5-16.8 -> 11.9-13.7
+  // us, 12288x4096 12.6-15.5 -> 11.1-12.9); with K split to fill the chip
+  // (6144x2048, 8192x2048, 10240x2560) or on two tiles they do not
+  // (6144x2048 at M = 32: 7.4 -> 8.8 us)
+  if (fits_unsplit && (rt != kG6Rt || split != 1)) return false;
   if (split > 1 && (!b.ws || (split <= kSplitInLaunch && (!b.cnt || groups(rt) > kSplitCounters)) ||
                     (size_t)groups(rt) * split * rt * mt * 1024 > b.ws_bytes))
     return false;
@@ -2094,6 +2101,8 @@ static bool choose6(const GemvBatch& b, Shape6& sh) {
   if (b.k % 512 != 0) return false;
   if (plan6(b, G, 17, sh)) return true;
   if (b.m < 9 || b.m > 16) return false;
+  // four row tiles on sixteen waves, within a launch's own K split
+  if (plan6(b, G, 9, sh) && sh.rt == kG6Rt && sh.plan.split <= kSplitInLaunch) return true;
   Split5 sp;
   int cpw = 4, ranges = 1;
   bool stream = false;

@@ -275,7 +275,8 @@ int rq_gemm_small_m(const uint16_t *x, int64_t m, int64_t ldx, const rq_qweight 
  *   8-row tiles that each cover K as two halves (int4 groups, m <= 8);
  *   RQ_PLAN_STREAMED_X: each wave streams its own chunks of x; RQ_PLAN_PHASED:
  *   x, codes and scales moved through LDS in phases of 512 k (int4 groups,
- *   m > 16, or m >= 9 in place of a split into more than four slices);
+ *   m > 16, or m >= 9 in place of a split into more than four slices or
+ *   where four row tiles per workgroup need no split);
  *   RQ_PLAN_FIRST: the one-tile-per-workgroup kernel.
  * split > 1: K is cut into split slices of chunks_per_slice chunks (128 k
  * for 4-, 5-, 6-bit codes and SB256, 64 k for int8, 32 k for fp16/bf16), the

@@ -113,6 +113,14 @@ def test_documented_plans():
     # width-4096 cmix value at M = 32: phased, four row tiles on sixteen waves
     p = rq.rq_plan_small_m(W4 + (4096, 16384), 32)
     assert (p["kernel"], p["split"], p["tiles_per_workgroup"], p["threads"]) == (rq.RQ_PLAN_PHASED, 4, 4, 1024)
+    # width-4096 cmix key at M = 9..17: phased unsplit on four row tiles,
+    # though its activation slice would fit one workgroup whole; the
+    # width-2048 K = 2048 shapes, which would need a K split, stay streaming
+    for m in (9, 16, 17):
+        p = rq.rq_plan_small_m(W4 + (16384, 4096), m)
+        assert (p["kernel"], p["split"], p["tiles_per_workgroup"]) == (rq.RQ_PLAN_PHASED, 1, 4), m
+        for n in (6144, 8192):
+            assert rq.rq_plan_small_m(W4 + (n, 2048), m)["kernel"] == rq.RQ_PLAN_STREAMING, (n, m)
     # width-2048 O (16 chunks) keeps one range
     assert rq.rq_plan_small_m(W4 + (2048, 2048), 1)["kernel"] == rq.RQ_PLAN_STREAMING
     # width-4096 cmix value at M = 1: sixteen-chunk waves, one workgroup of
